@@ -1,0 +1,311 @@
+/*
+ * ra_oracle.c -- plain, slow, fp64 CPU oracle for one rank's share of ring
+ * (blockwise) attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; the only thing both sides
+ * share is the seeded input generator.
+ *
+ * What it computes, and the passages it follows (glossary page "sequence
+ * parallelism transformers"):
+ *   - "Fundamentals / Sequence Dimension Splitting": N tokens are cut into P
+ *     contiguous chunks of N/P; rank r owns tokens [r*N/P, (r+1)*N/P).
+ *   - "Ring Attention / Ring Communication": in each of P steps GPU i passes
+ *     its current block to GPU i+1 and takes one from GPU i-1, so at step s
+ *     rank r holds block (r - s) mod P  (orc_ring_block).
+ *   - "Ring Attention / Computation": for every block it holds, a rank
+ *     attends its local queries to that block's keys/values and accumulates
+ *     the result, which equals full attention (orc_block_partial,
+ *     orc_merge, orc_rank_share).
+ *   - "Ulysses Sequence Parallelism / Attention Computation": full attention
+ *     over all tokens for a subset of heads (orc_attention with P = 1).
+ *   - "Implementation Considerations / Numerical Stability": the softmax
+ *     normalisation across blocks is carried as (running max m, running sum
+ *     l, unnormalised output o) and merged by rescaling to the common max.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of this repository):
+ *   - softmax scale 1/sqrt(d) is an argument; logits s_ij = scale * <q_i, k_j>;
+ *   - causal: key at global position kv_off + j is visible to query at global
+ *     position q_off + i iff kv_off + j <= q_off + i;
+ *   - grouped-query attention: query head h reads kv head h / (Hq / Hkv);
+ *   - an empty visible set gives the merge identity (m, l, o) = (-inf, 0, 0);
+ *   - LSE is the natural-log log-sum-exp of the scaled logits.
+ *
+ * Arithmetic is fp64 with plain loops in index order; no BLAS, no SIMD
+ * intrinsics, no blocking or reordering beyond what the definition states.
+ * Threads (pthreads) only split the list of independent output rows.
+ *
+ * Layout: q is [B, nq_rows, Hq, d], k and v are [B, nkv_rows, Hkv, d], all
+ * contiguous fp64; the *_rows arguments give the batch stride in rows.  A row
+ * list is an int64 array of (b, h, i) triples; outputs are compact,
+ * o[r*d + c], lse[r], m[r], l[r] for the r-th listed row.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    const double *q, *k, *v;
+    int64_t q_rows, kv_rows;   /* rows per batch entry of the q and k/v buffers */
+    int64_t nq, nkv, hq, hkv, d;
+    int64_t q_off, kv_off;     /* global position of local query 0 / key 0 */
+    int causal;
+    double scale;
+} orc_problem;
+
+static int visible(const orc_problem *p, int64_t i, int64_t j)
+{
+    if (!p->causal) return 1;
+    return p->kv_off + j <= p->q_off + i;
+}
+
+/* Unnormalised softmax partial of query row (b, h, i) over the keys of *p:
+ *   m = max_j s_ij,  l = sum_j exp(s_ij - m),  o = sum_j exp(s_ij - m) v_j
+ * over the visible j.  s is scratch of nkv doubles. */
+static void partial_row(const orc_problem *p, int64_t b, int64_t h, int64_t i,
+                        double *s, double *m_out, double *l_out, double *o_out)
+{
+    const int64_t d = p->d;
+    const int64_t g = h / (p->hq / p->hkv);
+    const double *qi = p->q + ((b * p->q_rows + i) * p->hq + h) * d;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < p->nkv; ++j) {
+        if (!visible(p, i, j)) continue;
+        const double *kj = p->k + ((b * p->kv_rows + j) * p->hkv + g) * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+        s[j] = p->scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t c = 0; c < d; ++c) o_out[c] = 0.0;
+    if (m != -INFINITY) {
+        for (int64_t j = 0; j < p->nkv; ++j) {
+            if (!visible(p, i, j)) continue;
+            const double *vj = p->v + ((b * p->kv_rows + j) * p->hkv + g) * d;
+            double w = exp(s[j] - m);
+            l += w;
+            for (int64_t c = 0; c < d; ++c) o_out[c] += w * vj[c];
+        }
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+typedef struct {
+    const orc_problem *p;
+    const int64_t *rows;
+    int64_t r0, r1;
+    int normalise;            /* 1: full attention (O, LSE); 0: partial (m, l, o) */
+    double *o, *a, *bb;       /* normalise: a = lse; else a = m, bb = l */
+    int err;
+} orc_job;
+
+static void *run_rows(void *arg)
+{
+    orc_job *J = (orc_job *)arg;
+    const orc_problem *p = J->p;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(p->nkv > 0 ? p->nkv : 1));
+    if (!s) { J->err = 1; return NULL; }
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        int64_t b = J->rows[3 * r], h = J->rows[3 * r + 1], i = J->rows[3 * r + 2];
+        double m, l;
+        double *o = J->o + r * p->d;
+        partial_row(p, b, h, i, s, &m, &l, o);
+        if (J->normalise) {
+            for (int64_t c = 0; c < p->d; ++c) o[c] = o[c] / l;
+            J->a[r] = m + log(l);
+        } else {
+            J->a[r] = m;
+            J->bb[r] = l;
+        }
+    }
+    free(s);
+    return NULL;
+}
+
+static int check_rows(const orc_problem *p, const int64_t *rows, int64_t nrows, int64_t B)
+{
+    if (p->d <= 0 || p->hq <= 0 || p->hkv <= 0 || p->hq % p->hkv != 0) return -3;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= p->hq || i < 0 || i >= p->nq) return -5;
+    }
+    return 0;
+}
+
+static int run_threads(const orc_problem *p, const int64_t *rows, int64_t nrows, int normalise,
+                       double *o, double *a, double *bb, int nthreads)
+{
+    if (nrows <= 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nrows) nthreads = (int)nrows;
+    orc_job *jobs = (orc_job *)calloc((size_t)nthreads, sizeof(orc_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    int *joined = (int *)calloc((size_t)nthreads, sizeof(int));
+    if (!jobs || !tid || !joined) { free(jobs); free(tid); free(joined); return -8; }
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        orc_job *J = &jobs[t];
+        J->p = p; J->rows = rows; J->normalise = normalise;
+        J->o = o; J->a = a; J->bb = bb;
+        J->r0 = t * per;
+        J->r1 = (t + 1) * per < nrows ? (t + 1) * per : nrows;
+        if (J->r0 >= J->r1) continue;
+        if (pthread_create(&tid[t], NULL, run_rows, J) == 0) joined[t] = 1;
+        else run_rows(J);                 /* no thread: do the rows here */
+    }
+    int err = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (joined[t]) pthread_join(tid[t], NULL);
+        if (jobs[t].err) err = -8;
+    }
+    free(jobs); free(tid); free(joined);
+    return err;
+}
+
+/* Full softmax attention of the listed query rows over all keys of the block
+ * (the plain definition): O_i = sum_j softmax_j(s_ij) v_j, LSE_i = log sum_j e^{s_ij}. */
+int orc_attention(const double *q, const double *k, const double *v,
+                  int64_t B, int64_t q_rows, int64_t kv_rows, int64_t nq, int64_t nkv,
+                  int64_t hq, int64_t hkv, int64_t d, int64_t q_off, int64_t kv_off,
+                  int causal, double scale, const int64_t *rows, int64_t nrows,
+                  double *o, double *lse, int nthreads)
+{
+    orc_problem p = {q, k, v, q_rows, kv_rows, nq, nkv, hq, hkv, d, q_off, kv_off, causal, scale};
+    int e = check_rows(&p, rows, nrows, B);
+    if (e) return e;
+    return run_threads(&p, rows, nrows, 1, o, lse, NULL, nthreads);
+}
+
+/* Unnormalised partial (m, l, o) of the listed rows against one key/value block. */
+int orc_block_partial(const double *q, const double *k, const double *v,
+                      int64_t B, int64_t q_rows, int64_t kv_rows, int64_t nq, int64_t nkv,
+                      int64_t hq, int64_t hkv, int64_t d, int64_t q_off, int64_t kv_off,
+                      int causal, double scale, const int64_t *rows, int64_t nrows,
+                      double *m, double *l, double *o, int nthreads)
+{
+    orc_problem p = {q, k, v, q_rows, kv_rows, nq, nkv, hq, hkv, d, q_off, kv_off, causal, scale};
+    int e = check_rows(&p, rows, nrows, B);
+    if (e) return e;
+    return run_threads(&p, rows, nrows, 0, o, m, l, nthreads);
+}
+
+/* Merge two partials over disjoint key sets A and B:
+ *   sum_{j in A u B} e^{s_j - m} = e^{m_a - m} sum_A e^{s_j - m_a} + e^{m_b - m} sum_B e^{s_j - m_b}
+ * with m = max(m_a, m_b); a side with m = -inf holds no keys and weighs 0. */
+void orc_merge(int64_t nrows, int64_t d,
+               const double *ma, const double *la, const double *oa,
+               const double *mb, const double *lb, const double *ob,
+               double *m, double *l, double *o)
+{
+    for (int64_t r = 0; r < nrows; ++r) {
+        double mm = ma[r] > mb[r] ? ma[r] : mb[r];
+        double wa = ma[r] == -INFINITY ? 0.0 : exp(ma[r] - mm);
+        double wb = mb[r] == -INFINITY ? 0.0 : exp(mb[r] - mm);
+        double ll = wa * la[r] + wb * lb[r];
+        for (int64_t c = 0; c < d; ++c) o[r * d + c] = wa * oa[r * d + c] + wb * ob[r * d + c];
+        m[r] = mm;
+        l[r] = ll;
+    }
+}
+
+/* O = o / l, LSE = m + ln l. */
+void orc_finalize(int64_t nrows, int64_t d, const double *m, const double *l, const double *o,
+                  double *out, double *lse)
+{
+    for (int64_t r = 0; r < nrows; ++r) {
+        for (int64_t c = 0; c < d; ++c) out[r * d + c] = o[r * d + c] / l[r];
+        lse[r] = m[r] + log(l[r]);
+    }
+}
+
+/* Ring position: at step s rank r holds the block that started at rank (r - s) mod P. */
+int64_t orc_ring_block(int64_t P, int64_t rank, int64_t s)
+{
+    int64_t j = (rank - s) % P;
+    return j < 0 ? j + P : j;
+}
+
+/* One rank's share: the local query block (q, [B, N/P, Hq, d]) against the P
+ * key/value blocks of k, v ([B, N, Hkv, d]) visited in ring order, each
+ * block's partial folded into the running state, then normalised. */
+int orc_rank_share(const double *q, const double *k, const double *v,
+                   int64_t B, int64_t N, int64_t P, int64_t rank,
+                   int64_t hq, int64_t hkv, int64_t d, int causal, double scale,
+                   const int64_t *rows, int64_t nrows, double *out, double *lse, int nthreads)
+{
+    if (P <= 0 || N % P != 0) return -3;
+    if (rank < 0 || rank >= P) return -5;
+    const int64_t nb = N / P;
+    size_t nd = (size_t)(nrows > 0 ? nrows : 1) * (size_t)d;
+    size_t n1 = (size_t)(nrows > 0 ? nrows : 1);
+    double *m = malloc(n1 * sizeof(double)), *l = malloc(n1 * sizeof(double));
+    double *o = malloc(nd * sizeof(double));
+    double *pm = malloc(n1 * sizeof(double)), *pl = malloc(n1 * sizeof(double));
+    double *po = malloc(nd * sizeof(double));
+    int e = 0;
+    if (!m || !l || !o || !pm || !pl || !po) { e = -8; goto done; }
+    for (int64_t r = 0; r < nrows; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.0;
+        for (int64_t c = 0; c < d; ++c) o[r * d + c] = 0.0;
+    }
+    for (int64_t s = 0; s < P; ++s) {
+        int64_t j = orc_ring_block(P, rank, s);
+        e = orc_block_partial(q, k + j * nb * hkv * d, v + j * nb * hkv * d,
+                              B, nb, N, nb, nb, hq, hkv, d, rank * nb, j * nb,
+                              causal, scale, rows, nrows, pm, pl, po, nthreads);
+        if (e) goto done;
+        orc_merge(nrows, d, m, l, o, pm, pl, po, m, l, o);
+    }
+    orc_finalize(nrows, d, m, l, o, out, lse);
+done:
+    free(m); free(l); free(o); free(pm); free(pl); free(po);
+    return e;
+}
+
+/* Block class of (query positions [q_off, q_off+nq), key positions
+ * [kv_off, kv_off+nkv)): 0 = no visible pair (SKIP), 1 = every pair visible
+ * (FULL), 2 = some but not all (PARTIAL). */
+int orc_classify(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal)
+{
+    if (nq <= 0 || nkv <= 0) return 0;
+    if (!causal) return 1;
+    if (kv_off > q_off + nq - 1) return 0;          /* first key after last query */
+    if (kv_off + nkv - 1 <= q_off) return 1;        /* last key at or before first query */
+    return 2;
+}
+
+/* Number of visible (query, key) pairs, counted row by row. */
+int64_t orc_visible_pairs(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal)
+{
+    int64_t n = 0;
+    for (int64_t i = 0; i < nq; ++i) {
+        int64_t c = causal ? q_off + i - kv_off + 1 : nkv;
+        if (c < 0) c = 0;
+        if (c > nkv) c = nkv;
+        n += c;
+    }
+    return n;
+}
+
+/* Algorithmic FLOP of one rank's share, "4 * Nq * Nkv * d * H, causal-halved":
+ * each block counts 4 * d * Hq * Nq * Nkv * B weighted 1 (FULL), 1/2 (PARTIAL)
+ * or 0 (SKIP). */
+double orc_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d, int causal)
+{
+    const int64_t nb = N / P;
+    double f = 0.0;
+    for (int64_t s = 0; s < P; ++s) {
+        int64_t j = orc_ring_block(P, rank, s);
+        int cls = orc_classify(rank * nb, nb, j * nb, nb, causal);
+        double w = cls == 1 ? 1.0 : (cls == 2 ? 0.5 : 0.0);
+        f += w * 4.0 * (double)d * (double)hq * (double)nb * (double)nb * (double)B;
+    }
+    return f;
+}

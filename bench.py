@@ -1,0 +1,210 @@
+"""Benchmark of one rank's share of ring attention on one MI355X.
+
+A step is one ra_rank_share call: the local query block against all P key/value
+blocks in ring order plus the normalisation, inputs resident in HBM.  Prints
+one JSON line (rank 0, N = 1):
+
+  value        algorithmic TFLOP/s of the whole step (4 * Nq * Nkv * d * Hq per
+               block, 1/2 for the causal diagonal block, 0 for skipped blocks)
+  roofline     the fused attention kernel against the bf16 dense MFMA peak,
+               its average duration taken with HIP events around every launch
+  cpu_baseline the fp64 oracle on a bounded sample of the same share's rows,
+               timed on this host's cores, in the same unit
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "rank7_of_8_bf16_causal"
+KERNEL_SOURCES = ["sequence_transformer_attention_amd/csrc/ra_kernels.hip",
+                  "sequence_transformer_attention_amd/csrc/ra_plan.h",
+                  "sequence_transformer_attention_amd/csrc/ra_launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    counter runs, or None when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, x, O_gpu, lse_gpu, target_s: float):
+    """Oracle (fp64 C, pthreads) on a seeded sample of the share's rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = max(1, min(16, oracle.default_threads()))
+    r = w.ranks[0]
+    g = torch.Generator().manual_seed(w.seed + 77)
+
+    def sample(n):
+        b = torch.randint(w.B, (n,), generator=g)
+        h = torch.randint(w.Hq, (n,), generator=g)
+        i = torch.randint(w.nq, (n,), generator=g)
+        return torch.stack([b, h, i], 1).numpy()
+
+    def row_flops(rows):
+        # visible keys of each row over the whole share (rank r owns positions r*nq..)
+        pos = rows[:, 2] + r * w.nq
+        vis = np.minimum(pos + 1, w.N) if w.causal else np.full(len(rows), w.N)
+        return float(4.0 * w.d * vis.sum())
+
+    q64 = x["q"].to(torch.float64).numpy()
+    k64 = x["k"].to(torch.float64).numpy()
+    v64 = x["v"].to(torch.float64).numpy()
+    probe = sample(2 * threads)
+    t0 = time.perf_counter()
+    oracle.rank_share(q64, k64, v64, w.P, r, w.causal, rows=probe, nthreads=threads)
+    dt = time.perf_counter() - t0
+    n = int(max(2 * threads, min(200000, len(probe) * target_s / max(dt, 1e-3))))
+    rows = sample(n)
+    log(f"cpu baseline: oracle on {n} sampled rows with {threads} threads")
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.rank_share(q64, k64, v64, w.P, r, w.causal, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = row_flops(rows)
+    rt = torch.as_tensor(rows, dtype=torch.long, device=O_gpu.device)
+    o = O_gpu[rt[:, 0], rt[:, 2], rt[:, 1]].double().cpu().numpy()
+    lse = lse_gpu[rt[:, 0], rt[:, 1], rt[:, 2]].double().cpu().numpy()
+    parity = {"rows": n, "max_abs_dO": float(np.abs(o - o_ref).max()),
+              "max_abs_dLSE": float(np.abs(lse - l_ref).max()), "tol_O": 1e-2, "tol_LSE": 1e-3}
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} random (b, h, i) rows of the same share, each against all its visible "
+                      f"keys in ring order; {flops:.3e} FLOP in {dt:.2f} s (fp64, plain C)"}
+    return base, parity
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from sequence_transformer_attention_amd import inputs, workloads
+    from sequence_transformer_attention_amd import ringattn as ra
+
+    dev = torch.device("cuda:0")
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n * 4, "launches": 5}))
+        return 0
+
+    w = workloads.BY_NAME[args.workload]
+    r = w.ranks[0]
+    log(f"workload {w.name}: drawing inputs")
+    x = inputs.workload_inputs(w)
+    q = inputs.local_q(w, x["q"], r).contiguous()
+    xq = dict(x, q=q)
+    qd, kd, vd = (t.to(dev) for t in (q, x["k"], x["v"]))
+    odt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    O = torch.empty((w.B, w.nq, w.Hq, w.d), dtype=odt, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.nq), dtype=torch.float32, device=dev)
+    flop = ra.ra_share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal)
+
+    def step():
+        ra.ra_rank_share(qd, kd, vd, w.P, r, w.causal, O, lse)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(per) / len(per)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (mean_ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms_per_step:.3f} ms/step, kernel mean {mean_ms:.3f} ms "
+        f"(median {per[len(per) // 2]:.3f}, min {per[0]:.3f}) -> {achieved:.1f} TFLOP/s")
+
+    out = {
+        "metric": "rank-share ring-attention TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": w.N,
+                   "P": w.P, "rank": r, "causal": w.causal, "q_block": w.nq, "input": w.dist,
+                   "seed": w.seed},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": flop,
+        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
+                      "min": round(per[0], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name)},
+        "inputs_sha256": {t: inputs.sha256(xq[t])[:16] for t in "qkv"},
+    }
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(w, xq, O, lse, args.cpu_seconds)
+        out["cpu_baseline"] = base
+        out["parity_sample"] = parity
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,159 @@
+/*
+ * libringattn -- one rank's share of ring (blockwise) attention on MI355X (gfx950).
+ *
+ * The operation (glossary page "sequence parallelism transformers"):
+ *   - section "Fundamentals", item "Sequence Dimension Splitting": the N tokens
+ *     are split into P contiguous chunks of N/P; rank r owns the queries and the
+ *     key/value block at positions [r*N/P, (r+1)*N/P);
+ *   - section "Ring Attention", item "Ring Communication": in P steps each rank
+ *     passes its current block to rank r+1 and receives from rank r-1, so at
+ *     step s rank r holds block (r - s) mod P;
+ *   - section "Ring Attention", item "Computation": at every step the rank
+ *     attends its local queries to the held block and accumulates; the
+ *     accumulated result equals full softmax attention;
+ *   - section "Implementation Considerations", item "Numerical Stability": the
+ *     accumulation carries the softmax normalisation as a running maximum m and
+ *     running sum l per query row (log-sum-exp rescaling);
+ *   - section "Ulysses Sequence Parallelism", item "Attention Computation":
+ *     after the all-to-all a GPU holds all N tokens for a subset of heads and
+ *     runs full attention on them: ra_rank_share with P = 1.
+ *
+ * On one GPU all P blocks are resident in device memory and the ring is
+ * replayed as sequential steps; no inter-GPU traffic happens in this library.
+ *
+ * Conventions shared by every call
+ *   - Tensors are described by ra_tensor: a DEVICE pointer owned by the caller
+ *     (the library never allocates, frees or keeps it), an element type, a
+ *     4-d shape and 4 strides counted in elements.
+ *   - q, k, v, o_acc, o_out use the [B, S, H, d] layout (batch, sequence,
+ *     heads, head_dim; the sequence on dim 1 as the mvp-engine
+ *     sequence-parallel skill page fixes for [batch, seq, hidden]).  stride[3]
+ *     must be 1; data and stride[0..2] * element size must be multiples of
+ *     16 bytes (128-bit loads).  Any other strides are accepted, so a
+ *     [B, H, S, d] buffer can be passed as a permuted view.
+ *   - Per-row statistics m, l, lse are fp32 with shape [B, H, S, 1]
+ *     (stride[3] ignored), any strides.
+ *   - Query position i of the local block is global position q_off + i; key j
+ *     of a block is global position kv_off + j.  With causal != 0 a key is
+ *     visible iff its global position <= the query's global position.
+ *   - Grouped-query attention: Hq must be a multiple of Hkv; query head h
+ *     reads kv head h / (Hq / Hkv).
+ *   - The softmax scale is opts->scale, or 1/sqrt(d) when opts is NULL or
+ *     opts->scale <= 0.  Logits are scaled in fp32 (never folded into bf16 Q).
+ *   - Running state (o_acc, m, l): o_acc fp32 [B, Nq, Hq, d] holds the
+ *     unnormalised output sum_j e^{s_j - m} v_j, m the running max of the
+ *     scaled logits (natural-log units), l the running sum sum_j e^{s_j - m}.
+ *     The empty state is (o_acc, m, l) = (0, -inf, 0) (ra_state_init).
+ *   - Supported: q/k/v dtype RA_BF16 (bf16 MFMA, fp32 accumulation) or RA_F32
+ *     (fp32 arithmetic), all three the same; d in {64, 128}.
+ *   - Every call validates all arguments on the host before touching the GPU
+ *     and returns RA_OK (0) or a negative ra_status; the reason is then in
+ *     ra_last_error() (thread-local).  Work is enqueued asynchronously on
+ *     opts->stream (a hipStream_t; NULL = the default stream); a fault inside
+ *     a kernel surfaces at the caller's next synchronisation.
+ *   - Empty work (B == 0, Nq == 0, a block with no visible key) returns RA_OK
+ *     without a launch.
+ */
+#ifndef LIBRINGATTN_H
+#define LIBRINGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RA_OK = 0,
+    RA_E_NULL = -1,        /* a required pointer or tensor is NULL */
+    RA_E_DTYPE = -2,       /* unsupported or mismatched element type */
+    RA_E_SHAPE = -3,       /* inconsistent shapes; N % P != 0; Hq % Hkv != 0 */
+    RA_E_LAYOUT = -4,      /* stride[3] != 1 or a 16-byte alignment rule broken */
+    RA_E_RANGE = -5,       /* rank outside [0, P), P < 1, negative offset, size too large */
+    RA_E_UNSUPPORTED = -6, /* head_dim not 64 or 128 */
+    RA_E_HIP = -7          /* the HIP runtime refused a launch */
+} ra_status;
+
+typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
+
+typedef struct {
+    void *data;          /* device pointer, caller-owned */
+    int32_t dtype;       /* ra_dtype */
+    int64_t shape[4];
+    int64_t stride[4];   /* in elements */
+} ra_tensor;
+
+typedef struct {
+    void *stream;               /* hipStream_t; NULL = default stream */
+    float scale;                /* softmax scale; <= 0 selects 1/sqrt(d) */
+    const ra_tensor *m;         /* ra_finalize: running max, needed for lse_out */
+    const ra_tensor *o_out;     /* normalised output O [B, Nq, Hq, d], bf16 or fp32 */
+    const ra_tensor *lse_out;   /* log-sum-exp [B, Hq, Nq, 1] fp32, natural log; optional */
+} ra_opts;
+
+/* Fill the running state with the empty state: o_acc = 0, m = -inf, l = 0.
+ * o_acc fp32 [B, Nq, H, d]; m, l fp32 [B, H, Nq, 1]. */
+int ra_state_init(const ra_tensor *o_acc, const ra_tensor *m, const ra_tensor *l,
+                  const ra_opts *opts);
+
+/* One ring step ("Ring Attention" / "Computation"): attend the local queries
+ * q [B, Nq, Hq, d] (global positions q_off..) to one key/value block
+ * k_blk, v_blk [B, Nkv, Hkv, d] (global positions kv_off..) and fold the
+ * result into the running state (o_acc, m, l) in place (log-sum-exp
+ * rescaling to the common maximum).  A block with no visible key (causal
+ * SKIP) returns RA_OK without a launch.  Steps may come in any order; the
+ * result after all blocks equals full attention up to rounding. */
+int ra_step(const ra_tensor *q, const ra_tensor *k_blk, const ra_tensor *v_blk,
+            const ra_tensor *o_acc, const ra_tensor *m, const ra_tensor *l,
+            int64_t q_off, int64_t kv_off, int causal, const ra_opts *opts);
+
+/* Normalise the running state: O = o_acc / l, and LSE = m + ln l.
+ * O goes to opts->o_out when given (bf16 or fp32), else in place into o_acc.
+ * LSE goes to opts->lse_out when given, which then needs opts->m. */
+int ra_finalize(const ra_tensor *o_acc, const ra_tensor *l, const ra_opts *opts);
+
+/* One rank's whole share in one launch: the local query block
+ * q [B, N/P, Hq, d] of rank `rank` (global positions rank*N/P..) against the
+ * P blocks of k, v [B, N, Hkv, d] visited in ring order (block (rank - s) mod P
+ * at step s), causal blocks skipped per (q_off, kv_off), the running state
+ * kept on chip, normalised at the end.  Writes O to opts->o_out (required)
+ * and LSE to opts->lse_out (optional).  N % P != 0 or Nq != N/P is
+ * RA_E_SHAPE: uneven lengths are not padded silently. */
+int ra_rank_share(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                  int P, int rank, int causal, const ra_opts *opts);
+
+/* ---- host-only queries (no GPU needed) --------------------------------- */
+
+/* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1. */
+int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s);
+
+/* Class of the (query positions [q_off, q_off+nq), key positions
+ * [kv_off, kv_off+nkv)) pair: 0 = SKIP (no visible pair), 1 = FULL (all
+ * visible), 2 = PARTIAL. */
+int ra_classify(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal);
+
+/* Tile plan of one step as the kernels use it: out[ti * ceil(nkv/bn) + tj] =
+ * ra_classify of query tile ti (bm rows) and key tile tj (bn keys), tails
+ * ragged.  Returns the number of tiles written, or a negative ra_status. */
+int64_t ra_plan_tiles(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal,
+                      int64_t bm, int64_t bn, int8_t *out, int64_t out_len);
+
+/* Query/key tile shape (rows bm, keys bn) the kernels use for this dtype and d. */
+int ra_tile_shape(int32_t dtype, int64_t d, int64_t *bm, int64_t *bn);
+
+/* Algorithmic FLOP of one rank's share, 4 * Nq * Nkv * d * Hq * B per block,
+ * weighted 1 for FULL, 1/2 for PARTIAL (the causal diagonal), 0 for SKIP. */
+double ra_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d,
+                      int causal);
+
+/* Description of the last error on this thread ("" if none). */
+const char *ra_last_error(void);
+
+/* Library version string. */
+const char *ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRINGATTN_H */

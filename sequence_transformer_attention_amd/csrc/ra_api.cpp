@@ -1,0 +1,319 @@
+// ra_api.cpp -- the C ABI of libringattn: argument checks, planning, launches.
+//
+// Every entry point validates all of its arguments on the host first and only
+// then touches the HIP runtime, so a bad call never reaches the GPU.  The
+// operations are those of the glossary page "sequence parallelism
+// transformers", section "Ring Attention" (items "Ring Communication" and
+// "Computation"); the argument and layout rules are documented in
+// include/libringattn.h.
+#include "../../include/libringattn.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <limits>
+
+#include "ra_launch.h"
+#include "ra_plan.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return RA_OK;
+}
+
+size_t esize(int32_t dt) { return dt == RA_BF16 ? 2 : 4; }
+
+bool dtype_valid(int32_t dt) { return dt == RA_BF16 || dt == RA_F32; }
+
+// A [B, S, H, d] tensor: stride[3] == 1, 16-byte aligned data and strides of
+// every dimension that has more than one entry.
+int check_bshd(const ra_tensor* t, const char* name) {
+  if (!t) return fail(RA_E_NULL, "%s is NULL", name);
+  if (!dtype_valid(t->dtype)) return fail(RA_E_DTYPE, "%s: unknown dtype %d", name, (int)t->dtype);
+  int64_t numel = 1;
+  for (int i = 0; i < 4; ++i) {
+    if (t->shape[i] < 0) return fail(RA_E_SHAPE, "%s: negative shape[%d]", name, i);
+    numel *= t->shape[i];
+  }
+  if (numel == 0) return RA_OK;
+  if (!t->data) return fail(RA_E_NULL, "%s->data is NULL", name);
+  if (t->stride[3] != 1 && t->shape[3] > 1)
+    return fail(RA_E_LAYOUT, "%s: stride[3] must be 1 (got %lld)", name, (long long)t->stride[3]);
+  if (((uintptr_t)t->data) % 16 != 0) return fail(RA_E_LAYOUT, "%s: data not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i) {
+    if (t->shape[i] <= 1) continue;
+    if (t->stride[i] < 0) return fail(RA_E_LAYOUT, "%s: negative stride[%d]", name, i);
+    if ((t->stride[i] * (int64_t)esize(t->dtype)) % 16 != 0)
+      return fail(RA_E_LAYOUT, "%s: stride[%d] * element size is not a multiple of 16 bytes", name, i);
+  }
+  return RA_OK;
+}
+
+// A per-row statistic [B, H, S, 1], fp32.
+int check_rows(const ra_tensor* t, const char* name, int64_t B, int64_t H, int64_t S) {
+  if (!t) return fail(RA_E_NULL, "%s is NULL", name);
+  if (t->dtype != RA_F32) return fail(RA_E_DTYPE, "%s must be fp32", name);
+  if (t->shape[0] != B || t->shape[1] != H || t->shape[2] != S || t->shape[3] != 1)
+    return fail(RA_E_SHAPE, "%s: shape must be [%lld, %lld, %lld, 1], got [%lld, %lld, %lld, %lld]", name,
+                (long long)B, (long long)H, (long long)S, (long long)t->shape[0], (long long)t->shape[1],
+                (long long)t->shape[2], (long long)t->shape[3]);
+  if (B * H * S == 0) return RA_OK;
+  if (!t->data) return fail(RA_E_NULL, "%s->data is NULL", name);
+  if (((uintptr_t)t->data) % 4 != 0) return fail(RA_E_LAYOUT, "%s: data not 4-byte aligned", name);
+  for (int i = 0; i < 3; ++i)
+    if (t->stride[i] < 0) return fail(RA_E_LAYOUT, "%s: negative stride[%d]", name, i);
+  return RA_OK;
+}
+
+bool same_shape(const ra_tensor* a, const ra_tensor* b) {
+  for (int i = 0; i < 4; ++i)
+    if (a->shape[i] != b->shape[i]) return false;
+  return true;
+}
+
+float resolve_scale(const ra_opts* opts, int64_t d) {
+  if (opts && opts->scale > 0.f && isfinite(opts->scale)) return opts->scale;
+  return (float)(1.0 / sqrt((double)d));
+}
+
+hipStream_t stream_of(const ra_opts* opts) { return opts ? (hipStream_t)opts->stream : nullptr; }
+
+// q [B, Nq, Hq, d] and k, v [B, Nkv, Hkv, d]: dtypes, shapes, head_dim.
+int check_qkv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const char* kn, const char* vn) {
+  int e;
+  if ((e = check_bshd(q, "q")) || (e = check_bshd(k, kn)) || (e = check_bshd(v, vn))) return e;
+  if (q->dtype != k->dtype || q->dtype != v->dtype)
+    return fail(RA_E_DTYPE, "q, %s and %s must have the same dtype", kn, vn);
+  if (!same_shape(k, v)) return fail(RA_E_SHAPE, "%s and %s must have the same shape", kn, vn);
+  if (k->shape[0] != q->shape[0]) return fail(RA_E_SHAPE, "batch of q and %s differ", kn);
+  if (k->shape[3] != q->shape[3]) return fail(RA_E_SHAPE, "head_dim of q and %s differ", kn);
+  if (k->shape[2] < 1 || q->shape[2] < 1) return fail(RA_E_SHAPE, "head counts must be >= 1");
+  if (q->shape[2] % k->shape[2] != 0)
+    return fail(RA_E_SHAPE, "query heads (%lld) must be a multiple of kv heads (%lld)", (long long)q->shape[2],
+                (long long)k->shape[2]);
+  const int64_t d = q->shape[3];
+  if (d != 64 && d != 128) return fail(RA_E_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  const int64_t lim = std::numeric_limits<int32_t>::max();
+  if (q->shape[0] > lim || q->shape[1] > lim || q->shape[2] > lim)
+    return fail(RA_E_RANGE, "q dimensions exceed 2^31 - 1");
+  return RA_OK;
+}
+
+int check_grid(int64_t nq, int64_t bm, int64_t hq, int64_t B) {
+  const int64_t wg = ((nq + bm - 1) / bm) * hq * B;
+  if (wg > (int64_t)std::numeric_limits<int32_t>::max())
+    return fail(RA_E_RANGE, "too many query tiles for one launch (%lld)", (long long)wg);
+  return RA_OK;
+}
+
+void set_bshd(const ra_tensor* t, int64_t& sb, int64_t& ss, int64_t& sh) {
+  sb = t->stride[0];
+  ss = t->stride[1];
+  sh = t->stride[2];
+}
+
+void set_rows(const ra_tensor* t, int64_t& sb, int64_t& sh, int64_t& ss) {
+  sb = t->stride[0];
+  sh = t->stride[1];
+  ss = t->stride[2];
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_out(const ra_tensor* o, const ra_tensor* like, const char* name) {
+  int e = check_bshd(o, name);
+  if (e) return e;
+  if (!same_shape(o, like)) return fail(RA_E_SHAPE, "%s must have the shape of %s", name, "the queries");
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_state_init(const ra_tensor* o_acc, const ra_tensor* m, const ra_tensor* l, const ra_opts* opts) {
+  int e = check_bshd(o_acc, "o_acc");
+  if (e) return e;
+  if (o_acc->dtype != RA_F32) return fail(RA_E_DTYPE, "o_acc must be fp32");
+  const int64_t B = o_acc->shape[0], S = o_acc->shape[1], H = o_acc->shape[2], d = o_acc->shape[3];
+  if ((e = check_rows(m, "m", B, H, S)) || (e = check_rows(l, "l", B, H, S))) return e;
+  if (d % 4 != 0) return fail(RA_E_UNSUPPORTED, "head_dim must be a multiple of 4");
+  if (B * S * H * d == 0) return ok();
+  RaInitArgs a{};
+  a.oacc = (float*)o_acc->data;
+  set_bshd(o_acc, a.oa_sb, a.oa_ss, a.oa_sh);
+  a.m = (float*)m->data;
+  set_rows(m, a.m_sb, a.m_sh, a.m_ss);
+  a.l = (float*)l->data;
+  set_rows(l, a.l_sb, a.l_sh, a.l_ss);
+  a.B = (int32_t)B; a.H = (int32_t)H; a.S = (int32_t)S; a.d = (int32_t)d;
+  return launched(ra_launch_init(a, stream_of(opts)), "ra_state_init launch");
+}
+
+int ra_step(const ra_tensor* q, const ra_tensor* k_blk, const ra_tensor* v_blk, const ra_tensor* o_acc,
+            const ra_tensor* m, const ra_tensor* l, int64_t q_off, int64_t kv_off, int causal,
+            const ra_opts* opts) {
+  int e = check_qkv(q, k_blk, v_blk, "k_blk", "v_blk");
+  if (e) return e;
+  const int64_t B = q->shape[0], nq = q->shape[1], hq = q->shape[2], d = q->shape[3];
+  const int64_t nkv = k_blk->shape[1];
+  if ((e = check_bshd(o_acc, "o_acc"))) return e;
+  if (o_acc->dtype != RA_F32) return fail(RA_E_DTYPE, "o_acc must be fp32");
+  if (!same_shape(o_acc, q)) return fail(RA_E_SHAPE, "o_acc must have the shape of q");
+  if ((e = check_rows(m, "m", B, hq, nq)) || (e = check_rows(l, "l", B, hq, nq))) return e;
+  if (q_off < 0 || kv_off < 0) return fail(RA_E_RANGE, "q_off and kv_off must be >= 0");
+  const int64_t bm = q->dtype == RA_BF16 ? RA_BF16_BM : RA_F32_BM;
+  if ((e = check_grid(nq, bm, hq, B))) return e;
+  if (B == 0 || nq == 0 || ra_plan_class(q_off, nq, kv_off, nkv, causal) == RA_CLASS_SKIP) return ok();
+
+  RaAttnArgs a{};
+  a.q = q->data; set_bshd(q, a.q_sb, a.q_ss, a.q_sh);
+  a.k = k_blk->data; set_bshd(k_blk, a.k_sb, a.k_ss, a.k_sh);
+  a.v = v_blk->data; set_bshd(v_blk, a.v_sb, a.v_ss, a.v_sh);
+  a.B = (int32_t)B; a.Hq = (int32_t)hq; a.Hkv = (int32_t)k_blk->shape[2]; a.nq = (int32_t)nq;
+  a.nkv = nkv; a.q_off = q_off; a.kv_off = kv_off;
+  a.ring = 0; a.P = 1; a.rank = 0; a.causal = causal ? 1 : 0;
+  a.c = resolve_scale(opts, d) * 1.4426950408889634f;
+  a.state_in = 1; a.out_state = 1;
+  a.oacc = (float*)o_acc->data; set_bshd(o_acc, a.oa_sb, a.oa_ss, a.oa_sh);
+  a.m = (float*)m->data; set_rows(m, a.m_sb, a.m_sh, a.m_ss);
+  a.l = (float*)l->data; set_rows(l, a.l_sb, a.l_sh, a.l_ss);
+  hipStream_t st = stream_of(opts);
+  return launched(q->dtype == RA_BF16 ? ra_launch_attn_bf16(a, (int)d, st) : ra_launch_attn_f32(a, (int)d, st),
+                  "ra_step launch");
+}
+
+int ra_finalize(const ra_tensor* o_acc, const ra_tensor* l, const ra_opts* opts) {
+  int e = check_bshd(o_acc, "o_acc");
+  if (e) return e;
+  if (o_acc->dtype != RA_F32) return fail(RA_E_DTYPE, "o_acc must be fp32");
+  const int64_t B = o_acc->shape[0], S = o_acc->shape[1], H = o_acc->shape[2], d = o_acc->shape[3];
+  if ((e = check_rows(l, "l", B, H, S))) return e;
+  if (d != 64 && d != 128) return fail(RA_E_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  const ra_tensor* o_out = opts ? opts->o_out : nullptr;
+  const ra_tensor* lse = opts ? opts->lse_out : nullptr;
+  const ra_tensor* mt = opts ? opts->m : nullptr;
+  if (o_out && (e = check_out(o_out, o_acc, "o_out"))) return e;
+  if (lse) {
+    if (!mt) return fail(RA_E_NULL, "lse_out needs opts->m");
+    if ((e = check_rows(mt, "m", B, H, S)) || (e = check_rows(lse, "lse_out", B, H, S))) return e;
+  }
+  if (B * S * H == 0) return ok();
+  RaFinArgs a{};
+  a.oacc = (const float*)o_acc->data; set_bshd(o_acc, a.oa_sb, a.oa_ss, a.oa_sh);
+  a.l = (const float*)l->data; set_rows(l, a.l_sb, a.l_sh, a.l_ss);
+  if (o_out) {
+    a.o = o_out->data; set_bshd(o_out, a.o_sb, a.o_ss, a.o_sh); a.o_bf16 = o_out->dtype == RA_BF16;
+  } else {
+    a.o = o_acc->data; set_bshd(o_acc, a.o_sb, a.o_ss, a.o_sh); a.o_bf16 = 0;
+  }
+  if (lse) {
+    a.m = (const float*)mt->data; set_rows(mt, a.m_sb, a.m_sh, a.m_ss);
+    a.lse = (float*)lse->data; set_rows(lse, a.lse_sb, a.lse_sh, a.lse_ss);
+  }
+  a.B = (int32_t)B; a.S = (int32_t)S; a.H = (int32_t)H; a.d = (int32_t)d;
+  return launched(ra_launch_finalize(a, stream_of(opts)), "ra_finalize launch");
+}
+
+int ra_rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
+                  const ra_opts* opts) {
+  int e = check_qkv(q, k, v, "k", "v");
+  if (e) return e;
+  if (!opts || !opts->o_out) return fail(RA_E_NULL, "ra_rank_share needs opts->o_out");
+  if (P < 1) return fail(RA_E_RANGE, "P must be >= 1 (got %d)", P);
+  if (rank < 0 || rank >= P) return fail(RA_E_RANGE, "rank %d outside [0, %d)", rank, P);
+  const int64_t B = q->shape[0], nq = q->shape[1], hq = q->shape[2], d = q->shape[3];
+  const int64_t N = k->shape[1];
+  if (N % P != 0)
+    return fail(RA_E_SHAPE, "sequence length %lld is not divisible by P = %d (no implicit padding)", (long long)N, P);
+  const int64_t nb = N / P;
+  if (nq != nb) return fail(RA_E_SHAPE, "local query block has %lld rows, expected N/P = %lld", (long long)nq, (long long)nb);
+  if ((e = check_out(opts->o_out, q, "o_out"))) return e;
+  if (opts->lse_out && (e = check_rows(opts->lse_out, "lse_out", B, hq, nq))) return e;
+  const int64_t bm = q->dtype == RA_BF16 ? RA_BF16_BM : RA_F32_BM;
+  if ((e = check_grid(nq, bm, hq, B))) return e;
+  if (B == 0 || nq == 0) return ok();
+
+  RaAttnArgs a{};
+  a.q = q->data; set_bshd(q, a.q_sb, a.q_ss, a.q_sh);
+  a.k = k->data; set_bshd(k, a.k_sb, a.k_ss, a.k_sh);
+  a.v = v->data; set_bshd(v, a.v_sb, a.v_ss, a.v_sh);
+  a.B = (int32_t)B; a.Hq = (int32_t)hq; a.Hkv = (int32_t)k->shape[2]; a.nq = (int32_t)nq;
+  a.nkv = nb; a.q_off = (int64_t)rank * nb; a.kv_off = 0;
+  a.ring = 1; a.P = P; a.rank = rank; a.causal = causal ? 1 : 0;
+  a.c = resolve_scale(opts, d) * 1.4426950408889634f;
+  a.state_in = 0; a.out_state = 0;
+  a.o = opts->o_out->data; set_bshd(opts->o_out, a.o_sb, a.o_ss, a.o_sh); a.o_bf16 = opts->o_out->dtype == RA_BF16;
+  if (opts->lse_out) { a.lse = (float*)opts->lse_out->data; set_rows(opts->lse_out, a.lse_sb, a.lse_sh, a.lse_ss); }
+  hipStream_t st = stream_of(opts);
+  return launched(q->dtype == RA_BF16 ? ra_launch_attn_bf16(a, (int)d, st) : ra_launch_attn_f32(a, (int)d, st),
+                  "ra_rank_share launch");
+}
+
+int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s) {
+  if (P < 1) return -1;
+  return ra_plan_ring_block(P, rank, s);
+}
+
+int ra_classify(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal) {
+  return ra_plan_class(q_off, nq, kv_off, nkv, causal);
+}
+
+int64_t ra_plan_tiles(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal, int64_t bm, int64_t bn,
+                      int8_t* out, int64_t out_len) {
+  if (bm < 1 || bn < 1 || nq < 0 || nkv < 0) return fail(RA_E_RANGE, "tile sizes must be >= 1, lengths >= 0");
+  const int64_t ti = (nq + bm - 1) / bm, tj = (nkv + bn - 1) / bn;
+  if (ti * tj > out_len) return fail(RA_E_RANGE, "out holds %lld entries, %lld needed", (long long)out_len, (long long)(ti * tj));
+  if (ti * tj > 0 && !out) return fail(RA_E_NULL, "out is NULL");
+  for (int64_t i = 0; i < ti; ++i)
+    for (int64_t j = 0; j < tj; ++j) {
+      const int64_t rq = (i + 1) * bm <= nq ? bm : nq - i * bm;
+      const int64_t rk = (j + 1) * bn <= nkv ? bn : nkv - j * bn;
+      out[i * tj + j] = (int8_t)ra_plan_class(q_off + i * bm, rq, kv_off + j * bn, rk, causal);
+    }
+  return ti * tj;
+}
+
+int ra_tile_shape(int32_t dtype, int64_t d, int64_t* bm, int64_t* bn) {
+  if (!bm || !bn) return fail(RA_E_NULL, "bm and bn must not be NULL");
+  if (!dtype_valid(dtype)) return fail(RA_E_DTYPE, "unknown dtype %d", (int)dtype);
+  if (d != 64 && d != 128) return fail(RA_E_UNSUPPORTED, "head_dim %lld not supported", (long long)d);
+  *bm = dtype == RA_BF16 ? RA_BF16_BM : RA_F32_BM;
+  *bn = dtype == RA_BF16 ? RA_BF16_BN : RA_F32_BN;
+  return ok();
+}
+
+double ra_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d, int causal) {
+  if (P < 1 || N % P != 0 || rank < 0 || rank >= P) return -1.0;
+  const int64_t nb = N / P;
+  double f = 0.0;
+  const double unit = 4.0 * (double)d * (double)hq * (double)nb * (double)nb * (double)B;
+  for (int64_t s = 0; s < P; ++s) {
+    const int c = ra_plan_class(rank * nb, nb, ra_plan_ring_block(P, rank, s) * nb, nb, causal);
+    f += c == RA_CLASS_FULL ? unit : (c == RA_CLASS_PARTIAL ? 0.5 * unit : 0.0);
+  }
+  return f;
+}
+
+const char* ra_last_error(void) { return g_err; }
+
+const char* ra_version(void) { return "libringattn 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// ra_launch.h -- kernel argument blocks and launchers (internal to libringattn).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Attention over one or more key/value blocks for a query block.
+//   ring == 0: one step, keys at global kv_off.., k/v point at the block.
+//   ring == 1: P steps in ring order from `rank`; k/v point at the whole
+//              sequence [B, P*nkv, Hkv, d]; q_off = rank * nkv.
+//   state_in:  1 = start from (oacc, m, l); 0 = start from the empty state.
+//   out_state: 1 = write (oacc, m, l) back; 0 = write normalised o (+ lse).
+struct RaAttnArgs {
+  const void* q; int64_t q_sb, q_ss, q_sh;
+  const void* k; int64_t k_sb, k_ss, k_sh;
+  const void* v; int64_t v_sb, v_ss, v_sh;
+  int32_t B, Hq, Hkv, nq;
+  int64_t nkv;               // block length
+  int64_t q_off, kv_off;
+  int32_t ring, P, rank, causal;
+  float c;                   // softmax scale * log2(e)
+  int32_t state_in, out_state;
+  float* oacc; int64_t oa_sb, oa_ss, oa_sh;
+  float* m; int64_t m_sb, m_sh, m_ss;
+  float* l; int64_t l_sb, l_sh, l_ss;
+  void* o; int64_t o_sb, o_ss, o_sh; int32_t o_bf16;
+  float* lse; int64_t lse_sb, lse_sh, lse_ss;
+};
+
+// O = oacc / l (to o, bf16 or fp32, or in place), LSE = m + ln l (optional).
+struct RaFinArgs {
+  const float* oacc; int64_t oa_sb, oa_ss, oa_sh;
+  const float* m; int64_t m_sb, m_sh, m_ss;
+  const float* l; int64_t l_sb, l_sh, l_ss;
+  void* o; int64_t o_sb, o_ss, o_sh; int32_t o_bf16;
+  float* lse; int64_t lse_sb, lse_sh, lse_ss;
+  int32_t B, H, S, d;
+};
+
+// oacc = 0, m = -inf, l = 0.
+struct RaInitArgs {
+  float* oacc; int64_t oa_sb, oa_ss, oa_sh;
+  float* m; int64_t m_sb, m_sh, m_ss;
+  float* l; int64_t l_sb, l_sh, l_ss;
+  int32_t B, H, S, d;
+};
+
+// Tile shape of the attention kernels (query rows per workgroup, keys per tile).
+constexpr int RA_BF16_BM = 128, RA_BF16_BN = 64;
+constexpr int RA_F32_BM = 64, RA_F32_BN = 64;
+
+hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t s);
+hipError_t ra_launch_attn_f32(const RaAttnArgs& a, int d, hipStream_t s);
+hipError_t ra_launch_finalize(const RaFinArgs& a, hipStream_t s);
+hipError_t ra_launch_init(const RaInitArgs& a, hipStream_t s);

@@ -1,0 +1,47 @@
+// ra_plan.h -- ring order and causal block/tile classes, shared by the host
+// planner and the gfx950 kernels so both take bit-identical decisions.
+//
+// Ring order: glossary page "sequence parallelism transformers", section
+// "Ring Attention", item "Ring Communication" (rank i sends to i+1 and
+// receives from i-1; after s steps rank r holds the block of rank r - s).
+// Classes: a key at global position kv is visible to a query at global
+// position q iff !causal || kv <= q.  A (query range, key range) pair is SKIP
+// when no pair is visible, FULL when all are, PARTIAL otherwise.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#define RA_HD __host__ __device__ inline
+#else
+#define RA_HD inline
+#endif
+
+enum { RA_CLASS_SKIP = 0, RA_CLASS_FULL = 1, RA_CLASS_PARTIAL = 2 };
+
+RA_HD int64_t ra_plan_ring_block(int64_t P, int64_t rank, int64_t s) {
+  int64_t j = (rank - s) % P;
+  return j < 0 ? j + P : j;
+}
+
+RA_HD int ra_plan_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, int causal) {
+  if (nq <= 0 || nk <= 0) return RA_CLASS_SKIP;
+  if (!causal) return RA_CLASS_FULL;
+  const int64_t q_last = q0 + nq - 1, k_last = k0 + nk - 1;
+  if (k0 > q_last) return RA_CLASS_SKIP;   // earliest key is after the latest query
+  if (k_last <= q0) return RA_CLASS_FULL;  // latest key is at or before the earliest query
+  return RA_CLASS_PARTIAL;
+}
+
+// Number of key tiles (bn wide) of a block [k0, k0+nk) that hold at least one
+// key visible to queries [q0, q0+nq): 0 for SKIP; under causal masking the
+// tiles past the last query's position are dropped.
+RA_HD int64_t ra_plan_key_tiles(int64_t q0, int64_t nq, int64_t k0, int64_t nk, int causal,
+                                int64_t bn) {
+  if (ra_plan_class(q0, nq, k0, nk, causal) == RA_CLASS_SKIP) return 0;
+  int64_t n = nk;
+  if (causal) {
+    const int64_t last_visible = q0 + nq - 1 - k0;  // >= 0 here
+    if (last_visible + 1 < n) n = last_visible + 1;
+  }
+  return (n + bn - 1) / bn;
+}

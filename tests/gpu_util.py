@@ -1,0 +1,68 @@
+"""Helpers of the GPU parity tests: run the HIP path, gather rows, compare with the oracle."""
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from sequence_transformer_attention_amd import ringattn as ra
+
+# bf16 inputs with fp32 accumulation / fp32 path
+TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-5, 1e-5)}
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, oracle.default_threads()))
+
+
+def gather(O: torch.Tensor, lse: torch.Tensor, rows: np.ndarray):
+    """O [B, S, H, d], lse [B, H, S] (device) -> (O rows [n, d], lse rows [n]) as fp64 numpy."""
+    r = torch.as_tensor(rows, dtype=torch.long, device=O.device)
+    o = O[r[:, 0], r[:, 2], r[:, 1]].double().cpu().numpy()
+    l = lse[r[:, 0], r[:, 1], r[:, 2]].double().cpu().numpy()
+    return o, l
+
+
+def assert_close(o, l, o_ref, l_ref, dtype: str, what: str):
+    tol_o, tol_l = TOL[dtype]
+    assert np.isfinite(o).all() and np.isfinite(l).all(), f"{what}: non-finite output"
+    eo = float(np.abs(o - o_ref).max()) if o.size else 0.0
+    el = float(np.abs(l - l_ref).max()) if l.size else 0.0
+    say(f"{what}: max|dO| = {eo:.3e} (tol {tol_o}), max|dLSE| = {el:.3e} (tol {tol_l}), rows {len(l)}")
+    assert eo <= tol_o, f"{what}: max |O - O_ref| = {eo} > {tol_o}"
+    assert el <= tol_l, f"{what}: max |LSE - LSE_ref| = {el} > {tol_l}"
+    return eo, el
+
+
+def rank_share_gpu(q, k, v, P, rank, causal, o_dtype=torch.float32, scale=None):
+    """q, k, v on the device; returns (O [B, Nq, Hq, d], lse [B, Hq, Nq])."""
+    B, nq, hq, d = q.shape
+    O = torch.full((B, nq, hq, d), float("nan"), dtype=o_dtype, device=q.device)
+    lse = torch.full((B, hq, nq), float("nan"), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share(q, k, v, P, rank, causal, O, lse, scale=scale)
+    return O, lse
+
+
+def stepwise_gpu(q, k, v, P, rank, causal, o_dtype=torch.float32, scale=None, order=None):
+    """The same share as P ra_step calls (ring order unless `order`) + ra_finalize."""
+    B, nq, hq, d = q.shape
+    N = k.shape[1]
+    nb = N // P
+    dev = q.device
+    oacc = torch.empty((B, nq, hq, d), dtype=torch.float32, device=dev)
+    m = torch.empty((B, hq, nq), dtype=torch.float32, device=dev)
+    l = torch.empty((B, hq, nq), dtype=torch.float32, device=dev)
+    ra.ra_state_init(oacc, m, l)
+    steps = order if order is not None else [ra.ra_ring_block(P, rank, s) for s in range(P)]
+    for j in steps:
+        ra.ra_step(q, k[:, j * nb:(j + 1) * nb], v[:, j * nb:(j + 1) * nb], oacc, m, l,
+                   rank * nb, j * nb, causal, scale=scale)
+    O = torch.full((B, nq, hq, d), float("nan"), dtype=o_dtype, device=dev)
+    lse = torch.full((B, hq, nq), float("nan"), dtype=torch.float32, device=dev)
+    ra.ra_finalize(oacc, l, m=m, o_out=O, lse_out=lse)
+    return O, lse

@@ -1,0 +1,215 @@
+"""C-ABI tests that need no GPU.
+
+  * libringattn.so loads and exports every function include/libringattn.h declares;
+  * argument validation returns the documented negative status before any HIP
+    call (fake, never-dereferenced device addresses);
+  * the host planner (ring order, block classes, tile plans, FLOP rule)
+    matches the oracle and tests/golden/ring_schedules.txt bit-exactly.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+from sequence_transformer_attention_amd import ringattn as ra
+from sequence_transformer_attention_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libringattn.h")
+
+# These tests hand the library fake device addresses and rely on validation
+# rejecting the call first; never run them where a GPU could be reached.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(), reason="CPU-only ABI checks")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"ra_step", "ra_finalize", "ra_rank_share", "ra_state_init"} <= set(names)
+    L = ctypes.CDLL(ra.library_path())
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in libringattn.h but not exported"
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in ra.ra_version()
+
+
+# ----------------------------------------------------------------- validation
+def T(shape, dtype=ra.RA_BF16, stride=None, data=FAKE):
+    t = ra.RaTensor()
+    t.data = data
+    t.dtype = dtype
+    if stride is None:
+        stride = [0, 0, 0, 1]
+        acc = 1
+        for i in (3, 2, 1, 0):
+            stride[i] = acc
+            acc *= shape[i]
+    for i in range(4):
+        t.shape[i] = shape[i]
+        t.stride[i] = stride[i]
+    return t
+
+
+def rows(B, H, S, data=FAKE):
+    return T([B, H, S, 1], ra.RA_F32, [H * S, S, 1, 1], data)
+
+
+def P(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def step(q, k, v, oacc, m, l, q_off=0, kv_off=0, causal=1, opts=None):
+    L = ra.lib()
+    return L.ra_step(P(q), P(k), P(v), P(oacc), P(m), P(l), q_off, kv_off, causal, P(opts))
+
+
+def good_step_args(B=1, nq=256, nkv=256, hq=4, hkv=2, d=128, dt=ra.RA_BF16):
+    return dict(q=T([B, nq, hq, d], dt), k=T([B, nkv, hkv, d], dt), v=T([B, nkv, hkv, d], dt),
+                oacc=T([B, nq, hq, d], ra.RA_F32), m=rows(B, hq, nq), l=rows(B, hq, nq))
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda a: a.update(q=None), ra.RA_E_NULL),
+    (lambda a: a.update(m=None), ra.RA_E_NULL),
+    (lambda a: setattr(a["k"], "data", 0), ra.RA_E_NULL),
+    (lambda a: setattr(a["q"], "dtype", 7), ra.RA_E_DTYPE),
+    (lambda a: setattr(a["k"], "dtype", ra.RA_F32), ra.RA_E_DTYPE),
+    (lambda a: setattr(a["oacc"], "dtype", ra.RA_BF16), ra.RA_E_DTYPE),
+    (lambda a: a.update(v=T([1, 128, 2, 128])), ra.RA_E_SHAPE),
+    (lambda a: a.update(k=T([1, 256, 3, 128]), v=T([1, 256, 3, 128])), ra.RA_E_SHAPE),
+    (lambda a: a.update(oacc=T([1, 128, 4, 128], ra.RA_F32)), ra.RA_E_SHAPE),
+    (lambda a: a.update(l=rows(1, 4, 255)), ra.RA_E_SHAPE),
+    (lambda a: a.update(q=T([1, 256, 4, 128], stride=[256 * 4 * 128, 4 * 128, 128, 2])), ra.RA_E_LAYOUT),
+    (lambda a: a.update(q=T([1, 256, 4, 128], stride=[256 * 4 * 130, 4 * 130, 130, 1])), ra.RA_E_LAYOUT),
+    (lambda a: setattr(a["q"], "data", FAKE + 8), ra.RA_E_LAYOUT),
+    (lambda a: a.update(q=T([1, 256, 4, 96]), k=T([1, 256, 2, 96]), v=T([1, 256, 2, 96]),
+                        oacc=T([1, 256, 4, 96], ra.RA_F32)), ra.RA_E_UNSUPPORTED),
+])
+def test_ra_step_rejects_bad_arguments(mutate, status):
+    a = good_step_args()
+    mutate(a)
+    assert step(**a) == status
+    assert ra.ra_last_error() != ""
+
+
+def test_ra_step_rejects_negative_offsets():
+    assert step(**good_step_args(), q_off=-1) == ra.RA_E_RANGE
+    assert step(**good_step_args(), kv_off=-5) == ra.RA_E_RANGE
+
+
+def test_ra_step_skip_and_empty_return_ok_without_launch():
+    # causal block entirely in the future of every query: SKIP, no launch
+    assert step(**good_step_args(), q_off=0, kv_off=1000, causal=1) == ra.RA_OK
+    assert step(**good_step_args(nq=0)) == ra.RA_OK
+    assert step(**good_step_args(B=0)) == ra.RA_OK
+
+
+def share(q, k, v, Pn, rank, causal=1, o_out=None, lse=None, scale=0.0):
+    opts = ra.RaOpts()
+    opts.scale = scale
+    if o_out is not None:
+        opts.o_out = ctypes.pointer(o_out)
+    if lse is not None:
+        opts.lse_out = ctypes.pointer(lse)
+    return ra.lib().ra_rank_share(P(q), P(k), P(v), Pn, rank, causal, ctypes.byref(opts))
+
+
+def test_ra_rank_share_validation():
+    q, k, v = T([1, 512, 4, 128]), T([1, 4096, 1, 128]), T([1, 4096, 1, 128])
+    o = T([1, 512, 4, 128])
+    assert share(q, k, v, 8, 7) == ra.RA_E_NULL                   # no o_out
+    assert share(q, k, v, 0, 0, o_out=o) == ra.RA_E_RANGE         # P < 1
+    assert share(q, k, v, 8, 8, o_out=o) == ra.RA_E_RANGE         # rank outside [0, P)
+    assert share(q, k, v, 8, -1, o_out=o) == ra.RA_E_RANGE
+    k3, v3 = T([1, 4095, 1, 128]), T([1, 4095, 1, 128])
+    assert share(q, k3, v3, 8, 7, o_out=o) == ra.RA_E_SHAPE       # N % P != 0: no padding
+    assert "divisible" in ra.ra_last_error()
+    assert share(q, k, v, 4, 3, o_out=o) == ra.RA_E_SHAPE         # Nq != N / P
+    assert share(q, k, v, 8, 7, o_out=T([1, 512, 4, 64])) == ra.RA_E_SHAPE
+    assert share(q, k, v, 8, 7, o_out=o, lse=rows(1, 4, 511)) == ra.RA_E_SHAPE
+    assert share(T([1, 0, 4, 128]), T([1, 0, 1, 128]), T([1, 0, 1, 128]), 8, 7, o_out=T([1, 0, 4, 128])) == ra.RA_OK
+
+
+def test_ra_finalize_validation():
+    L = ra.lib()
+    oacc, l = T([1, 64, 2, 64], ra.RA_F32), rows(1, 2, 64)
+    opts = ra.RaOpts()
+    lse = rows(1, 2, 64)
+    opts.lse_out = ctypes.pointer(lse)
+    assert L.ra_finalize(P(oacc), P(l), ctypes.byref(opts)) == ra.RA_E_NULL   # lse needs m
+    assert L.ra_finalize(P(T([1, 64, 2, 64])), P(l), None) == ra.RA_E_DTYPE  # o_acc must be fp32
+    assert L.ra_finalize(P(oacc), P(rows(1, 2, 63)), None) == ra.RA_E_SHAPE
+    assert L.ra_finalize(P(T([1, 0, 2, 64], ra.RA_F32)), P(rows(1, 2, 0)), None) == ra.RA_OK
+
+
+def test_ra_state_init_validation():
+    L = ra.lib()
+    assert L.ra_state_init(P(T([1, 8, 2, 64])), P(rows(1, 2, 8)), P(rows(1, 2, 8)), None) == ra.RA_E_DTYPE
+    assert L.ra_state_init(P(T([1, 8, 2, 64], ra.RA_F32)), P(rows(1, 2, 7)), P(rows(1, 2, 8)), None) == ra.RA_E_SHAPE
+
+
+# ------------------------------------------------------------- host planner
+def test_ring_block_and_classes_match_golden_schedules():
+    path = os.path.join(ROOT, "tests", "golden", "ring_schedules.txt")
+    names = {"SKIP": 0, "FULL": 1, "PARTIAL": 2}
+    by = workloads.BY_NAME
+    n = 0
+    for line in open(path):
+        if line.startswith("#"):
+            continue
+        wname, r, s, j, kv_off, cls = line.split()
+        w = by[wname]
+        r, s, j, kv_off = int(r), int(s), int(j), int(kv_off)
+        nb = w.N // w.P
+        assert ra.ra_ring_block(w.P, r, s) == j
+        assert ra.ra_classify(r * nb, nb, j * nb, nb, w.causal) == names[cls]
+        n += 1
+    assert n > 100
+
+
+def test_classify_matches_oracle_exhaustively():
+    R = range(0, 13)
+    for q_off, nq, kv_off, nkv in itertools.product(R, R, R, R):
+        for causal in (0, 1):
+            assert ra.ra_classify(q_off, nq, kv_off, nkv, causal) == oracle.classify(q_off, nq, kv_off, nkv, causal)
+
+
+@pytest.mark.parametrize("bm,bn", [(128, 64), (64, 64), (3, 5), (16, 32)])
+def test_tile_plan_matches_oracle_per_tile(bm, bn):
+    for (q_off, nq, kv_off, nkv) in [(0, 300, 0, 300), (28672, 4096, 28672, 4096), (100, 77, 40, 190),
+                                     (4096, 4096, 0, 4096), (0, 130, 130, 70)]:
+        for causal in (0, 1):
+            plan = ra.ra_plan_tiles(q_off, nq, kv_off, nkv, causal, bm, bn)
+            tj = -(-nkv // bn)
+            for i in range(-(-nq // bm)):
+                for j in range(tj):
+                    rq = min(bm, nq - i * bm)
+                    rk = min(bn, nkv - j * bn)
+                    assert plan[i * tj + j] == oracle.classify(q_off + i * bm, rq, kv_off + j * bn, rk, causal)
+
+
+def test_share_flops_match_oracle():
+    for w in workloads.ALL:
+        for r in range(w.P):
+            assert ra.ra_share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal) == \
+                oracle.share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal)
+
+
+def test_tile_shape():
+    assert ra.ra_tile_shape(torch.bfloat16, 128) == (128, 64)
+    assert ra.ra_tile_shape(torch.float32, 64) == (64, 64)
+    with pytest.raises(ra.RaError):
+        ra.ra_tile_shape(torch.bfloat16, 96)

@@ -1,0 +1,36 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle computes a seeded sample of rows one by one: every row of the first
+and last query tiles of the first and last head, plus one random row per
+(query tile, head).  Each sampled row attends to all of its key blocks, so
+every block, the causal diagonal and the fully visible path are exercised.
+"""
+import pytest
+import torch
+
+import oracle
+from sequence_transformer_attention_amd import inputs, workloads
+from tests.gpu_util import assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu
+
+pytestmark = pytest.mark.gpu
+
+FULL = [workloads.RANK7_BF16, workloads.GQA_BF16, workloads.ULYSSES_BF16, workloads.STRESS_BF16]
+
+
+@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def test_full_size_sampled_rows(w):
+    say(f"{w.name}: drawing inputs")
+    x = inputs.workload_inputs(w)
+    d = {k: t.to("cuda") for k, t in x.items()}
+    r = w.ranks[0]
+    say(f"{w.name}: fused rank share (bf16 O)")
+    O, lse = rank_share_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.bfloat16)
+    say(f"{w.name}: stepwise ({w.P} steps + finalize)")
+    Os, lses = stepwise_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.float32)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(w.B, w.Hq, w.nq, w.seed).numpy()
+    say(f"{w.name}: oracle on {len(rows)} rows")
+    o_ref, l_ref = oracle.rank_share(x["q"], x["k"], x["v"], w.P, r, w.causal, rows=rows,
+                                     nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"{w.name} fused")
+    assert_close(*gather(Os, lses, rows), o_ref, l_ref, "bf16", f"{w.name} stepwise")

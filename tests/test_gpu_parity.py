@@ -1,0 +1,202 @@
+"""GPU parity of the HIP path against the fp64 oracle (small and shrunken workloads).
+
+Every case draws seeded inputs, runs libringattn through its C ABI on the
+GPU and compares element by element with the oracle on the same bytes:
+max |O - O_ref| <= 1e-2 and max |LSE - LSE_ref| <= 1e-3 for bf16 inputs,
+<= 1e-5 for both on the fp32 path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_transformer_attention_amd import inputs, workloads
+from sequence_transformer_attention_amd import ringattn as ra
+from tests.gpu_util import assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _dev(x):
+    return {k: v.to(DEV) for k, v in x.items()}
+
+
+# -------------------------------------------------------------- tiny fp32 workload
+def test_tiny_f32_every_rank_fused():
+    w = workloads.TINY_F32
+    x = inputs.workload_inputs(w)
+    d = _dev(x)
+    for r in w.ranks:
+        say(f"tiny_f32 fused rank {r}")
+        ql = inputs.local_q(w, x["q"], r)
+        O, lse = rank_share_gpu(inputs.local_q(w, d["q"], r).contiguous(), d["k"], d["v"], w.P, r, w.causal)
+        torch.cuda.synchronize()
+        rows = oracle.all_rows(w.B, w.Hq, w.nq)
+        o_ref, l_ref = oracle.rank_share(ql, x["k"], x["v"], w.P, r, w.causal, rows=rows, nthreads=oracle_threads())
+        assert_close(*gather(O, lse, rows), o_ref, l_ref, "f32", f"tiny rank {r}")
+
+
+def test_tiny_f32_every_rank_stepwise_state_after_each_step():
+    """Per-step running state (o_acc, m, l) against the oracle's merged partials."""
+    w = workloads.TINY_F32
+    x = inputs.workload_inputs(w)
+    d = _dev(x)
+    nb = w.nq
+    rows = oracle.all_rows(w.B, w.Hq, nb)
+    for r in w.ranks:
+        say(f"tiny_f32 stepwise rank {r}")
+        qd = inputs.local_q(w, d["q"], r).contiguous()
+        qh = inputs.local_q(w, x["q"], r)
+        oacc = torch.empty((w.B, nb, w.Hq, w.d), dtype=torch.float32, device=DEV)
+        m = torch.empty((w.B, w.Hq, nb), dtype=torch.float32, device=DEV)
+        l = torch.empty_like(m)
+        ra.ra_state_init(oacc, m, l)
+        st = oracle.identity_state(len(rows), w.d)
+        for s in range(w.P):
+            j = ra.ra_ring_block(w.P, r, s)
+            ra.ra_step(qd, d["k"][:, j * nb:(j + 1) * nb], d["v"][:, j * nb:(j + 1) * nb], oacc, m, l,
+                       r * nb, j * nb, w.causal)
+            part = oracle.block_partial(qh, x["k"][:, j * nb:(j + 1) * nb], x["v"][:, j * nb:(j + 1) * nb],
+                                        r * nb, j * nb, w.causal, rows=rows, nthreads=oracle_threads())
+            st = oracle.merge(st, part)
+            torch.cuda.synchronize()
+            mg = m.permute(0, 1, 2).reshape(-1).double().cpu().numpy()
+            lg = l.reshape(-1).double().cpu().numpy()
+            og = oacc.permute(0, 2, 1, 3).reshape(-1, w.d).double().cpu().numpy()
+            np.testing.assert_allclose(mg, st[0], atol=1e-5, rtol=0)
+            # l and o_acc are relative to m: compare after bringing both to the oracle's m
+            corr = np.exp(mg - st[0])
+            np.testing.assert_allclose(lg * corr, st[1], rtol=1e-5, atol=0)
+            np.testing.assert_allclose(og * corr[:, None], st[2], rtol=0, atol=1e-5 * st[1].max())
+        O = torch.empty((w.B, nb, w.Hq, w.d), dtype=torch.float32, device=DEV)
+        lse = torch.empty((w.B, w.Hq, nb), dtype=torch.float32, device=DEV)
+        ra.ra_finalize(oacc, l, m=m, o_out=O, lse_out=lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.finalize(st)
+        assert_close(*gather(O, lse, rows), o_ref, l_ref, "f32", f"tiny stepwise rank {r}")
+
+
+# ------------------------------------------------------------ shrunken bf16 workloads
+SHRUNK = [w.shrunk(16) for w in (workloads.RANK7_BF16, workloads.GQA_BF16,
+                                 workloads.ULYSSES_BF16, workloads.STRESS_BF16)]
+
+
+@pytest.mark.parametrize("w", SHRUNK, ids=[w.name for w in SHRUNK])
+def test_shrunken_bf16_workloads_all_rows(w):
+    x = inputs.workload_inputs(w)
+    d = _dev(x)
+    r = w.ranks[0]
+    rows = oracle.all_rows(w.B, w.Hq, w.nq)
+    say(f"{w.name} fused rank {r}")
+    O, lse = rank_share_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.float32)
+    Ob, lseb = rank_share_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.rank_share(x["q"], x["k"], x["v"], w.P, r, w.causal, rows=rows, nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"{w.name} fp32 O")
+    assert_close(*gather(Ob, lseb, rows), o_ref, l_ref, "bf16", f"{w.name} bf16 O")
+    say(f"{w.name} stepwise rank {r}")
+    Os, lses = stepwise_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal)
+    torch.cuda.synchronize()
+    assert_close(*gather(Os, lses, rows), o_ref, l_ref, "bf16", f"{w.name} stepwise")
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,nq,nkv,Hq,Hkv,d,q_off,kv_off,causal", [
+    (1, 200, 150, 2, 1, 128, 100, 60, True),     # ragged q and kv tails, diagonal inside
+    (2, 77, 333, 4, 2, 64, 300, 0, True),        # d = 64, GQA, B = 2, many ragged tiles
+    (1, 130, 70, 3, 3, 128, 0, 0, False),
+    (1, 1, 1, 1, 1, 128, 0, 0, True),            # single query, single key
+    (1, 64, 4096, 1, 1, 128, 5000, 1000, True),  # block partly in the future of the first rows
+    (1, 256, 64, 2, 2, 128, 0, 192, True),       # rows 0..191 see nothing of this block
+])
+def test_ra_step_edge_cases(dt, B, nq, nkv, Hq, Hkv, d, q_off, kv_off, causal):
+    say(f"edge {dt} B{B} nq{nq} nkv{nkv} Hq{Hq} Hkv{Hkv} d{d} q_off{q_off} kv_off{kv_off} causal{causal}")
+    x = inputs.draw_qkv(B, nq, nkv, Hq, Hkv, d, seed=nq + nkv, dtype=dt)
+    xd = _dev(x)
+    oacc = torch.empty((B, nq, Hq, d), dtype=torch.float32, device=DEV)
+    m = torch.empty((B, Hq, nq), dtype=torch.float32, device=DEV)
+    l = torch.empty_like(m)
+    ra.ra_state_init(oacc, m, l)
+    ra.ra_step(xd["q"], xd["k"], xd["v"], oacc, m, l, q_off, kv_off, causal)
+    rows = oracle.all_rows(B, Hq, nq)
+    mr, lr, orr = oracle.block_partial(x["q"], x["k"], x["v"], q_off, kv_off, causal, rows=rows,
+                                       nthreads=oracle_threads())
+    torch.cuda.synchronize()
+    mg = m.reshape(-1).double().cpu().numpy()
+    vis = lr > 0
+    # rows that see no key keep the empty state exactly
+    assert np.all(mg[~vis] == -np.inf)
+    assert np.all(l.reshape(-1).cpu().numpy()[~vis] == 0)
+    if vis.any():
+        O = torch.empty((B, nq, Hq, d), dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, Hq, nq), dtype=torch.float32, device=DEV)
+        ra.ra_finalize(oacc, l, m=m, o_out=O, lse_out=lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.finalize((mr[vis], lr[vis], orr[vis]))
+        assert_close(*gather(O, lse, rows[vis]), o_ref, l_ref, dt, "edge")
+
+
+def test_bhsd_strided_views_and_skip_leaves_state_untouched():
+    """[B, H, S, d] buffers passed as permuted views; a SKIP step launches nothing."""
+    B, S, H, d = 1, 300, 2, 128
+    x = inputs.draw_qkv(B, S, S, H, H, d, seed=99)
+    qh = x["q"].permute(0, 2, 1, 3).contiguous().to(DEV)   # [B, H, S, d] storage
+    kh = x["k"].permute(0, 2, 1, 3).contiguous().to(DEV)
+    vh = x["v"].permute(0, 2, 1, 3).contiguous().to(DEV)
+    q, k, v = (t.permute(0, 2, 1, 3) for t in (qh, kh, vh))   # [B, S, H, d] views
+    say("bhsd strided rank share")
+    O, lse = rank_share_gpu(q, k, v, 1, 0, True)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(B, H, S)
+    o_ref, l_ref = oracle.rank_share(x["q"], x["k"], x["v"], 1, 0, True, rows=rows, nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", "bhsd views")
+    oacc = torch.randn((B, S, H, d), device=DEV)
+    m = torch.randn((B, H, S), device=DEV)
+    l = torch.rand((B, H, S), device=DEV)
+    before = [t.clone() for t in (oacc, m, l)]
+    ra.ra_step(q, k, v, oacc, m, l, 0, 10_000, True)    # every key after every query
+    torch.cuda.synchronize()
+    for a, b in zip((oacc, m, l), before):
+        assert torch.equal(a, b)
+
+
+def test_run_to_run_bitwise_determinism_and_nan_poison():
+    w = workloads.RANK7_BF16.shrunk(16)
+    d = _dev(inputs.workload_inputs(w))
+    say("determinism")
+    O1, l1 = rank_share_gpu(d["q"], d["k"], d["v"], w.P, w.ranks[0], w.causal, torch.bfloat16)
+    O2, l2 = rank_share_gpu(d["q"], d["k"], d["v"], w.P, w.ranks[0], w.causal, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+    assert not torch.isnan(O1.float()).any() and not torch.isnan(l1).any()   # outputs were NaN-filled
+
+
+def test_stepwise_resume_from_host_checkpoint():
+    """Stop after k steps, copy the state to host memory and back, finish: bitwise equal."""
+    w = workloads.GQA_BF16.shrunk(16)
+    d = _dev(inputs.workload_inputs(w))
+    r, nb = w.ranks[0], w.nq
+    say("checkpoint/resume")
+
+    def run(checkpoint_at):
+        oacc = torch.empty((w.B, nb, w.Hq, w.d), dtype=torch.float32, device=DEV)
+        m = torch.empty((w.B, w.Hq, nb), dtype=torch.float32, device=DEV)
+        l = torch.empty_like(m)
+        ra.ra_state_init(oacc, m, l)
+        for s in range(w.P):
+            if s == checkpoint_at:
+                host = [t.cpu() for t in (oacc, m, l)]
+                oacc, m, l = (t.to(DEV) for t in host)
+            j = ra.ra_ring_block(w.P, r, s)
+            ra.ra_step(d["q"], d["k"][:, j * nb:(j + 1) * nb], d["v"][:, j * nb:(j + 1) * nb], oacc, m, l,
+                       r * nb, j * nb, w.causal)
+        torch.cuda.synchronize()
+        return oacc, m, l
+
+    a = run(-1)
+    b = run(w.P // 2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -8,25 +8,34 @@
 // per query row; section "Flash Attention with Sequence Parallelism", item
 // "Tiled Computation" -- each block is processed in tiles that stay on chip.
 //
-// bf16 path (attn_bf16_kernel), one workgroup = 4 waves = 128 query rows of
+// bf16 path (attn_bf16_kernel): one workgroup = 8 waves = 256 query rows of
 // one head; each wave owns 32 query rows.  Per key tile of 64 keys:
-//   S^T (keys x queries) = K Q^T   v_mfma_f32_32x32x16_bf16, K from LDS (A),
-//                                  Q fragment in VGPRs for the whole kernel (B)
+//   S^T (keys x queries) = K Q^T   v_mfma_f32_32x32x16_bf16; K from LDS is the
+//                                  A operand, the Q fragment stays in VGPRs
+//                                  for the whole kernel as the B operand
 //   online softmax                 the accumulator layout puts one query per
 //                                  lane (lane & 31) and 32 of its 64 keys in
 //                                  that lane's registers; the other 32 sit in
 //                                  lane ^ 32, so the row max needs one
-//                                  cross-lane exchange and the rescale factor
-//                                  is a per-lane scalar
+//                                  v_permlane32_swap and the rescale factor is
+//                                  a per-lane scalar
 //   O^T (channels x queries) += V^T P^T   P^T goes from the S^T accumulator
 //                                  registers straight into the B operand
-//                                  (bf16, round to nearest even); V^T is
-//                                  staged transposed in LDS for the A operand
-// K and V tiles move HBM -> VGPR (128-bit loads, prefetched one tile ahead)
-// -> LDS (double-buffered, one barrier per tile).  Logits are scaled in fp32
-// (never folded into bf16 Q); exponentials are base 2 with the scale folded
-// into one FMA: p = exp2(s * scale * log2(e) - m2), m2 the running max in
-// log2 units.
+//                                  (bf16, round to nearest even); the A
+//                                  operand V^T comes from row-major V in LDS
+//                                  through the transposing ds_read_b64_tr_b16
+// K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
+// staging) into two stages, row-major under an XOR swizzle of the 16-byte
+// slots (conflict-free K and transposing V reads); one barrier per tile.
+// Logits are scaled in fp32 (never folded into bf16 Q); exponentials are
+// base 2 with the scale folded into one FMA: p = exp2(s * scale * log2(e) - m2),
+// m2 the running max in log2 units.  m2 is moved only when a tile's max
+// exceeds it by more than kLazyTau, so the rescale of O is rare; the result
+// does not depend on which max is used as long as o, l and m agree
+// (O = o / l, LSE = m + ln l), and p stays <= 2^kLazyTau.
+//
+// fp32 path (attn_f32_kernel): one wave per 64 query rows, fp32 FMA
+// throughout, for the fp32 workloads.
 #include "ra_launch.h"
 #include "ra_plan.h"
 
@@ -52,22 +61,28 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return (bid % 8) * (nwg / 8) + bid / 8;
 }
 
-__device__ __forceinline__ unsigned bf16_at(const u32x4& v, int e) {
-  unsigned w = v[e >> 1];
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
+// ---------------------------------------------------------------------------
+// bf16 path.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+constexpr float kLazyTau = 8.0f;
+
+// Physical 16-byte slot of logical slot p in LDS row r.  Eight consecutive
+// rows map one logical slot to eight different bank groups (K reads, 16 B per
+// lane); four consecutive rows (aligned to 4) map a slot pair {2k, 2k+1} to
+// eight different bank groups (transposing V reads, 8 B per lane).
+__device__ __forceinline__ int swz(int r, int p) { return p ^ (((r & 3) << 1) | ((r >> 2) & 1)); }
 
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
-  constexpr int BM = RA_BF16_BM, BN = RA_BF16_BN, NT = 256;
-  constexpr int KROW = D + 8;   // bf16 per K row in LDS: 16-byte pad, rows shift 4 banks
-  constexpr int VROW = BN + 4;  // bf16 per V^T row in LDS: 8-byte pad, rows shift 2 banks
-  constexpr int KSZ = BN * KROW, VSZ = D * VROW, STAGE = KSZ + VSZ;
-  constexpr int NKC = BN * D / 8 / NT;     // 16-byte K chunks per thread per tile
-  constexpr int NVG = (BN / 4) * (D / 8);  // V groups of 4 keys x 8 channels
-  static_assert(NKC * NT * 8 == BN * D, "K tile split");
-  static_assert(NVG <= NT, "V tile split");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+__global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
+  constexpr int NW = 8, BM = NW * 32, BN = RA_BF16_BN, NT = NW * 64;
+  constexpr int SLOTS = D / 8;                 // 16-byte slots per row
+  constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
+  constexpr int NI = BN * SLOTS / NT;          // direct-load instructions per thread per tile
+  static_assert(NI * NT == BN * SLOTS, "tile split");
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE_BYTES];  // [stage][K|V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
@@ -77,7 +92,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
   int qt = logical % nqt;
   const int hb = logical / nqt;
   const int h = hb % a.Hq, b = hb / a.Hq;
-  if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
+  if (a.causal) qt = nqt - 1 - qt;
   const int hk = h / (a.Hq / a.Hkv);
 
   const int qrow_wg = qt * BM;
@@ -85,7 +100,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
   const int my_q = qrow_w + lr;
   const bool q_ok = my_q < a.nq;
 
-  // Q fragment (B operand of S^T = K Q^T): lane holds Q[my_q][16c + 8lg .. +7].
   bf16x8 qf[D / 16];
   {
     const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)my_q * a.q_ss +
@@ -98,8 +112,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
     }
   }
 
-  // Running state.  o[db][r] = O^T[32db + 8(r/4) + 4lg + r%4][my_q] (unnormalised);
-  // m2 = running max of s * c (log2 units); lsum = this lane's half of the row sum.
   f32x16 o[D / 32];
   float m2 = -INFINITY, lsum = 0.f;
 #pragma unroll
@@ -116,7 +128,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
       }
     const float mv = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q * a.m_ss];
     const float lv = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q * a.l_ss];
-    m2 = mv * kLog2e;  // -inf stays -inf
+    m2 = mv * kLog2e;
     lsum = lg == 0 ? lv : 0.f;
   }
 
@@ -133,73 +145,58 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
     return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
   };
 
-  u32x4 kreg[NKC];
-  u32x4 vreg[4];
-  const int vga = tid % (BN / 4), vdc = tid / (BN / 4);
-
-  auto load_tile = [&](int s, int u) {
+  // Issue the direct loads of key tile u of step s into stage buf.  Lane L of
+  // instruction (wave, i) fills physical slot (wave*NI + i)*64 + L; it loads
+  // the logical slot that the swizzle puts there.  Rows past the block end
+  // re-read the last valid row (finite data; masked in S, zero weight in P).
+  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
+  auto issue_tile = [&](int s, int u, int buf) {
     const int64_t r0 = step_row0(s) + (int64_t)u * BN;
     const int64_t left = a.nkv - (int64_t)u * BN;
-    const int nvalid = left < BN ? (int)left : BN;
-    const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + r0 * a.k_ss;
-    const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + r0 * a.v_ss;
+    const int last = (left < BN ? (int)left : BN) - 1;
 #pragma unroll
-    for (int i = 0; i < NKC; ++i) {
-      const int id = tid + i * NT, row = id / (D / 8), ch = id % (D / 8);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row < nvalid) w = *(const u32x4*)(kb + (int64_t)row * a.k_ss + ch * 8);
-      kreg[i] = w;
-    }
-    if (tid < NVG) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * vga + i;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (row < nvalid) w = *(const u32x4*)(vb + (int64_t)row * a.v_ss + vdc * 8);
-        vreg[i] = w;
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int inst = wave * NI + i;
+      const int ls = inst * 64 + lane;
+      const int r = ls / SLOTS, p = ls % SLOTS;
+      const int lp = swz(r, p);
+      const int64_t gr = r0 + (r < last ? r : last);
+      const __bf16* kg = kbase + gr * a.k_ss + lp * 8;
+      const __bf16* vg = vbase + gr * a.v_ss + lp * 8;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)kg, (lds_void_t*)(&smem[buf][0][inst * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)vg, (lds_void_t*)(&smem[buf][1][inst * 1024]), 16, 0, 0);
     }
   };
 
-  auto store_tile = [&](int buf) {
-    __bf16* Ks = smem + buf * STAGE;
-    __bf16* Vt = Ks + KSZ;
-#pragma unroll
-    for (int i = 0; i < NKC; ++i) {
-      const int id = tid + i * NT, row = id / (D / 8), ch = id % (D / 8);
-      *(u32x4*)(Ks + row * KROW + ch * 8) = kreg[i];
-    }
-    if (tid < NVG) {
-      // 4 keys x 8 channels -> V^T rows 8vdc..8vdc+7, keys 4vga..4vga+3
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2 w;
-        w[0] = bf16_at(vreg[0], e) | (bf16_at(vreg[1], e) << 16);
-        w[1] = bf16_at(vreg[2], e) | (bf16_at(vreg[3], e) << 16);
-        *(u32x2*)(Vt + (8 * vdc + e) * VROW + 4 * vga) = w;
-      }
-    }
-  };
+  // Per-lane constant parts of the LDS addresses.
+  // K (A operand of S^T): row 32bb + lr, logical slot 2c + lg.
+  // V (transposing read): source lane j = lane % 16 supplies row kv0 + j/4 and
+  // channels d0 + 4 (j % 4) .. + 3 with d0 = 32 db + 16 ((lane/16) % 2) and
+  // kv0 = 32 bb + 16 hh + 4 (lane / 32) (+ 8 for the second half).
+  const int vj = lane & 15, ve = vj >> 2, vc = vj & 3;
+  const int vgrp = lane >> 4;
 
   auto compute = [&](int s, int u, int buf) {
-    const __bf16* Ks = smem + buf * STAGE;
-    const __bf16* Vt = Ks + KSZ;
+    const char* Ks = smem[buf][0];
+    const char* Vs = smem[buf][1];
     const int64_t k0 = step_kv_off(s) + (int64_t)u * BN;
     const int64_t left = a.nkv - (int64_t)u * BN;
     const int nvalid = left < BN ? (int)left : BN;
     const int64_t q0w = a.q_off + qrow_w;
     const int nqw = min(32, a.nq - qrow_w);
     const int cls = ra_plan_class(q0w, nqw, k0, nvalid, a.causal);
-    if (cls == RA_CLASS_SKIP) return;  // wave-uniform: no visible key for these rows
+    if (cls == RA_CLASS_SKIP) return;
     const bool need_mask = cls == RA_CLASS_PARTIAL || nvalid < BN;
 
     f32x16 sacc[BN / 32];
 #pragma unroll
     for (int bb = 0; bb < BN / 32; ++bb) {
       sacc[bb] = f32x16{};
+      const int r = 32 * bb + lr;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 kf = *(const bf16x8*)(Ks + (32 * bb + lr) * KROW + 16 * c + 8 * lg);
+        const bf16x8 kf = *(const bf16x8*)(Ks + r * (D * 2) + swz(r, 2 * c + lg) * 16);
         sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[bb], 0, 0, 0);
       }
     }
@@ -218,51 +215,72 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
     for (int bb = 0; bb < BN / 32; ++bb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[bb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m2, mx * a.c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key yet: keep p = 0, alpha = 0
-    const float alpha = fast_exp2(m2 - m_use);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float t = mx * a.c;
+    // move the max only when it grows by more than kLazyTau (or on the first visible key)
+    const bool bump = t > m2 + kLazyTau;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? t : m2;
+      const float alpha = bump ? fast_exp2(m2 - t) : 1.f;  // 0 when m2 was -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m2 = m_new;
+    }
+    const float m_use = m2 == -INFINITY ? 0.f : m2;  // no visible key yet: p = 0
 
+    // The row sum takes the fp32 p (only the MFMA operand is rounded to bf16):
+    // rows with few visible keys would otherwise carry the 2^-9 rounding of a
+    // single term into l and the LSE.
     bf16x8 pf[BN / 32][2];
     float psum = 0.f;
 #pragma unroll
     for (int bb = 0; bb < BN / 32; ++bb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[bb][r], a.c, -m_use));
-        psum += p;
-        pf[bb][r >> 3][r & 7] = (__bf16)p;
-      }
-    lsum = lsum * alpha + psum;
-    m2 = m_new;
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        for (int t8 = 0; t8 < 8; ++t8) {
+          const float p = fast_exp2(fmaf(sacc[bb][8 * hh + t8], a.c, -m_use));
+          psum += p;
+          pf[bb][hh][t8] = (__bf16)p;
+        }
+    lsum += psum;
 
 #pragma unroll
     for (int bb = 0; bb < BN / 32; ++bb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) {
+        const int kv0 = 32 * bb + 16 * hh + 4 * (vgrp >> 1) + ve;
+        const int r1 = kv0, r2 = kv0 + 8;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const __bf16* vp = Vt + (32 * db + lr) * VROW + 32 * bb + 16 * hh + 4 * lg;
-          const bf16x4 lo = *(const bf16x4*)vp;
-          const bf16x4 hi = *(const bf16x4*)(vp + 8);
-          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const int ch = 32 * db + 16 * (vgrp & 1) + 4 * vc;   // first channel of this lane's 8 bytes
+          const int slot = ch >> 3, sub = (ch & 7) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(Vs + r1 * (D * 2) + swz(r1, slot) * 16 + sub));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(Vs + r2 * (D * 2) + swz(r2, slot) * 16 + sub));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[bb][hh], o[db], 0, 0, 0);
         }
+      }
   };
 
-  // Flat loop over (step, tile) in ring order; tile i+1 is fetched into
-  // registers while tile i is computed from LDS buffer i & 1.
+  // Flat loop over (step, tile) in ring order, two LDS stages: the loads of
+  // the next tile are issued right after the barrier that retires the stage
+  // they overwrite, and waited for at the top of the next iteration.
   int s = 0;
   while (s < nsteps && step_tiles(s) == 0) ++s;
   int u = 0, it = 0;
-  if (s < nsteps) load_tile(s, 0);
+  if (s < nsteps) issue_tile(s, 0, 0);
   while (s < nsteps) {
     const int nt = step_tiles(s);
-    store_tile(it & 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     int s2 = s, u2 = u + 1;
     if (u2 >= nt) {
@@ -270,15 +288,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(RaAttnArgs a) {
       ++s2;
       while (s2 < nsteps && step_tiles(s2) == 0) ++s2;
     }
-    if (s2 < nsteps) load_tile(s2, u2);
+    if (s2 < nsteps) issue_tile(s2, u2, (it + 1) & 1);
     compute(s, u, it & 1);
     s = s2;
     u = u2;
     ++it;
   }
 
-  // Epilogue: the two halves of each row sum live in lanes lr and lr + 32.
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  float ltot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (!q_ok) return;
   if (a.out_state) {
     float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh;
@@ -494,7 +515,7 @@ __global__ void __launch_bounds__(256) init_kernel(RaInitArgs a) {
 
 hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t st) {
   const int nqt = (a.nq + RA_BF16_BM - 1) / RA_BF16_BM;
-  const dim3 grid((unsigned)((int64_t)nqt * a.Hq * a.B)), block(256);
+  const dim3 grid((unsigned)((int64_t)nqt * a.Hq * a.B)), block(512);
   if (d == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, st, a);
   return hipGetLastError();

@@ -45,7 +45,7 @@ struct RaInitArgs {
 };
 
 // Tile shape of the attention kernels (query rows per workgroup, keys per tile).
-constexpr int RA_BF16_BM = 128, RA_BF16_BN = 64;
+constexpr int RA_BF16_BM = 256, RA_BF16_BN = 64;
 constexpr int RA_F32_BM = 64, RA_F32_BN = 64;
 
 hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t s);

@@ -209,7 +209,7 @@ def test_share_flops_match_oracle():
 
 
 def test_tile_shape():
-    assert ra.ra_tile_shape(torch.bfloat16, 128) == (128, 64)
+    assert ra.ra_tile_shape(torch.bfloat16, 128) == (256, 64)
     assert ra.ra_tile_shape(torch.float32, 64) == (64, 64)
     with pytest.raises(ra.RaError):
         ra.ra_tile_shape(torch.bfloat16, 96)

@@ -23,8 +23,9 @@ def test_full_size_sampled_rows(w):
     x = inputs.workload_inputs(w)
     d = {k: t.to("cuda") for k, t in x.items()}
     r = w.ranks[0]
-    say(f"{w.name}: fused rank share (bf16 O)")
+    say(f"{w.name}: fused rank share (bf16 O, as timed; fp32 O)")
     O, lse = rank_share_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.bfloat16)
+    O32, lse32 = rank_share_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.float32)
     say(f"{w.name}: stepwise ({w.P} steps + finalize)")
     Os, lses = stepwise_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, torch.float32)
     torch.cuda.synchronize()
@@ -32,5 +33,6 @@ def test_full_size_sampled_rows(w):
     say(f"{w.name}: oracle on {len(rows)} rows")
     o_ref, l_ref = oracle.rank_share(x["q"], x["k"], x["v"], w.P, r, w.causal, rows=rows,
                                      nthreads=oracle_threads())
-    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"{w.name} fused")
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"{w.name} fused bf16 O", out_bf16=True)
+    assert_close(*gather(O32, lse32, rows), o_ref, l_ref, "bf16", f"{w.name} fused fp32 O")
     assert_close(*gather(Os, lses, rows), o_ref, l_ref, "bf16", f"{w.name} stepwise")

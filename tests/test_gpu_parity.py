@@ -95,7 +95,7 @@ def test_shrunken_bf16_workloads_all_rows(w):
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.rank_share(x["q"], x["k"], x["v"], w.P, r, w.causal, rows=rows, nthreads=oracle_threads())
     assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"{w.name} fp32 O")
-    assert_close(*gather(Ob, lseb, rows), o_ref, l_ref, "bf16", f"{w.name} bf16 O")
+    assert_close(*gather(Ob, lseb, rows), o_ref, l_ref, "bf16", f"{w.name} bf16 O", out_bf16=True)
     say(f"{w.name} stepwise rank {r}")
     Os, lses = stepwise_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal)
     torch.cuda.synchronize()

@@ -39,6 +39,8 @@
 #include "ra_launch.h"
 #include "ra_plan.h"
 
+#include <type_traits>
+
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -65,7 +67,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 // bf16 path.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 constexpr float kLazyTau = 8.0f;
 
@@ -74,6 +75,15 @@ constexpr float kLazyTau = 8.0f;
 // lane); four consecutive rows (aligned to 4) map a slot pair {2k, 2k+1} to
 // eight different bank groups (transposing V reads, 8 B per lane).
 __device__ __forceinline__ int swz(int r, int p) { return p ^ (((r & 3) << 1) | ((r >> 2) & 1)); }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [I, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 template <int D>
 __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
@@ -169,17 +179,28 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     }
   };
 
-  // Per-lane constant parts of the LDS addresses.
-  // K (A operand of S^T): row 32bb + lr, logical slot 2c + lg.
-  // V (transposing read): source lane j = lane % 16 supplies row kv0 + j/4 and
-  // channels d0 + 4 (j % 4) .. + 3 with d0 = 32 db + 16 ((lane/16) % 2) and
-  // kv0 = 32 bb + 16 hh + 4 (lane / 32) (+ 8 for the second half).
-  const int vj = lane & 15, ve = vj >> 2, vc = vj & 3;
-  const int vgrp = lane >> 4;
+  // Per-lane LDS byte offsets inside a stage's K or V tile (rows of 2D bytes,
+  // 16-byte slot p of row r stored at slot p ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1)).
+  // K, A operand of S^T: row 32 bb + lr, logical slot 2c + lg, i.e. physical
+  //   2 (c ^ (lr & 3)) + (lg ^ ((lr >> 2) & 1)):  koff[c & 3] + 128 (c >> 2) + 64 D bb.
+  int koff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = lr * 2 * D + 32 * (j ^ (lr & 3)) + 16 * (lg ^ ((lr >> 2) & 1));
+  // V, transposing reads: source lane j = lane % 16 supplies row
+  //   32 bb + 16 hh + 8 half + 4 (lane / 32) + j / 4 and the 8 bytes at channel
+  //   32 db + 16 ((lane / 16) % 2) + 4 (j % 4); with ve = j / 4, vc = j % 4,
+  //   x = 2 ((lane / 16) % 2) + vc / 2 the physical slot is
+  //   4 (db ^ (ve >> 1)) + (x ^ (2 (ve & 1) + lane / 32)).
+  const int vj = lane & 15, ve = vj >> 2, vc = vj & 3, vgrp = lane >> 4;
+  const int vx = 2 * (vgrp & 1) + (vc >> 1);
+  const int vlane = (4 * lg + ve) * 2 * D + 16 * (vx ^ (2 * (ve & 1) + lg)) + 8 * (vc & 1);
+  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0][0]);
+  const unsigned vofs_even = smem_lds + TILE_BYTES + vlane + 64 * (ve >> 1);
+  const unsigned vofs_odd = smem_lds + TILE_BYTES + vlane - 64 * (ve >> 1);
 
   auto compute = [&](int s, int u, int buf) {
     const char* Ks = smem[buf][0];
-    const char* Vs = smem[buf][1];
+    const unsigned vst = (unsigned)buf * (2 * TILE_BYTES);
     const int64_t k0 = step_kv_off(s) + (int64_t)u * BN;
     const int64_t left = a.nkv - (int64_t)u * BN;
     const int nvalid = left < BN ? (int)left : BN;
@@ -193,10 +214,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
 #pragma unroll
     for (int bb = 0; bb < BN / 32; ++bb) {
       sacc[bb] = f32x16{};
-      const int r = 32 * bb + lr;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 kf = *(const bf16x8*)(Ks + r * (D * 2) + swz(r, 2 * c + lg) * 16);
+        const bf16x8 kf = *(const bf16x8*)(Ks + koff[c & 3] + 128 * (c >> 2) + 64 * D * bb);
         sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[bb], 0, 0, 0);
       }
     }
@@ -251,24 +271,33 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
         }
     lsum += psum;
 
+    // O^T += V^T P^T.  The transposing reads are issued as inline asm so that
+    // the compiler does not order them behind the in-flight direct loads of
+    // the next stage (it cannot prove they do not alias); the wait that
+    // follows carries their registers, so the MFMAs stay behind it.
+    static_for<0, 2 * (BN / 32)>([&](auto ig) {
+      constexpr int g = decltype(ig)::value, bb = g >> 1, hh = g & 1;
+      u32x2 lo[D / 32], hi[D / 32];
+#define RA_TR_READ(DB)                                                                         \
+  if constexpr (DB < D / 32) {                                                                 \
+    constexpr int off = 64 * DB + (32 * bb + 16 * hh) * 2 * D;                                 \
+    const unsigned va = ((DB & 1) ? vofs_odd : vofs_even) + vst;                               \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo[DB]) : "v"(va), "i"(off));    \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi[DB]) : "v"(va), "i"(off + 16 * D)); \
+  }
+      RA_TR_READ(0) RA_TR_READ(1) RA_TR_READ(2) RA_TR_READ(3)
+#undef RA_TR_READ
+      if constexpr (D == 128)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]),
+                     "+v"(lo[2]), "+v"(hi[2]), "+v"(lo[3]), "+v"(hi[3]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]));
 #pragma unroll
-    for (int bb = 0; bb < BN / 32; ++bb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int kv0 = 32 * bb + 16 * hh + 4 * (vgrp >> 1) + ve;
-        const int r1 = kv0, r2 = kv0 + 8;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int ch = 32 * db + 16 * (vgrp & 1) + 4 * vc;   // first channel of this lane's 8 bytes
-          const int slot = ch >> 3, sub = (ch & 7) * 2;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(Vs + r1 * (D * 2) + swz(r1, slot) * 16 + sub));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(Vs + r2 * (D * 2) + swz(r2, slot) * 16 + sub));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[bb][hh], o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x4 w = {lo[db][0], lo[db][1], hi[db][0], hi[db][1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[bb][hh], o[db], 0, 0, 0);
       }
+    });
   };
 
   // Flat loop over (step, tile) in ring order, two LDS stages: the loads of

@@ -92,7 +92,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
   constexpr int NI = BN * SLOTS / NT;          // direct-load instructions per thread per tile
   static_assert(NI * NT == BN * SLOTS, "tile split");
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE_BYTES];  // [stage][K|V]
+  static_assert(BN == 64, "the softmax below is written for two 32-key halves");
+  // [0], [1]: K stages; [2], [3]: V stages
+  __shared__ __attribute__((aligned(1024))) char smem[4][TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
@@ -102,7 +104,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   int qt = logical % nqt;
   const int hb = logical / nqt;
   const int h = hb % a.Hq, b = hb / a.Hq;
-  if (a.causal) qt = nqt - 1 - qt;
+  if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
   const int hk = h / (a.Hq / a.Hkv);
 
   const int qrow_wg = qt * BM;
@@ -110,6 +112,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int my_q = qrow_w + lr;
   const bool q_ok = my_q < a.nq;
 
+  // Q fragment (B operand of S^T = K Q^T): lane holds Q[my_q][16c + 8lg .. +7].
   bf16x8 qf[D / 16];
   {
     const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)my_q * a.q_ss +
@@ -122,6 +125,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     }
   }
 
+  // Running state.  o[db][r] = O^T[32db + 8(r/4) + 4lg + r%4][my_q] (unnormalised);
+  // m2 = running max of s * c (log2 units); lsum = this lane's half of the row sum.
   f32x16 o[D / 32];
   float m2 = -INFINITY, lsum = 0.f;
 #pragma unroll
@@ -138,49 +143,43 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       }
     const float mv = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q * a.m_ss];
     const float lv = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q * a.l_ss];
-    m2 = mv * kLog2e;
+    m2 = mv * kLog2e;  // -inf stays -inf
     lsum = lg == 0 ? lv : 0.f;
   }
 
   const int64_t q0_wg = a.q_off + qrow_wg;
   const int nq_wg = min(BM, a.nq - qrow_wg);
   const int nsteps = a.ring ? a.P : 1;
+  // key position of block (step) s; in ring mode also its first row in k/v
   auto step_kv_off = [&](int s) -> int64_t {
-    return a.ring ? ra_plan_ring_block(a.P, a.rank, s) * a.nkv : a.kv_off;
-  };
-  auto step_row0 = [&](int s) -> int64_t {
-    return a.ring ? ra_plan_ring_block(a.P, a.rank, s) * a.nkv : 0;
+    return a.ring ? (int64_t)ra_plan_ring_block32(a.P, a.rank, s) * a.nkv : a.kv_off;
   };
   auto step_tiles = [&](int s) -> int {
     return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
   };
 
-  // Issue the direct loads of key tile u of step s into stage buf.  Lane L of
-  // instruction (wave, i) fills physical slot (wave*NI + i)*64 + L; it loads
-  // the logical slot that the swizzle puts there.  Rows past the block end
-  // re-read the last valid row (finite data; masked in S, zero weight in P).
+  // Direct loads of one key tile: lane L of instruction (wave, i) fills
+  // physical slot (wave*NI + i)*64 + L of the tile and loads the logical slot
+  // that the swizzle puts there.  Rows past the block end re-read the last
+  // valid row (finite data; masked in S, zero weight in P).
   const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
-  auto issue_tile = [&](int s, int u, int buf) {
-    const int64_t r0 = step_row0(s) + (int64_t)u * BN;
-    const int64_t left = a.nkv - (int64_t)u * BN;
-    const int last = (left < BN ? (int)left : BN) - 1;
+  // row0: first row of the tile in k/v; nvalid: rows of the tile inside the block
+  auto issue = [&](const __bf16* base, int64_t stride, int64_t row0, int nvalid, int stage) {
+    const int last = nvalid - 1;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int inst = wave * NI + i;
       const int ls = inst * 64 + lane;
       const int r = ls / SLOTS, p = ls % SLOTS;
-      const int lp = swz(r, p);
-      const int64_t gr = r0 + (r < last ? r : last);
-      const __bf16* kg = kbase + gr * a.k_ss + lp * 8;
-      const __bf16* vg = vbase + gr * a.v_ss + lp * 8;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)kg, (lds_void_t*)(&smem[buf][0][inst * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)vg, (lds_void_t*)(&smem[buf][1][inst * 1024]), 16, 0, 0);
+      const int64_t gr = row0 + (r < last ? r : last);
+      const __bf16* g = base + gr * stride + swz(r, p) * 8;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(&smem[stage][inst * 1024]), 16, 0, 0);
     }
   };
 
-  // Per-lane LDS byte offsets inside a stage's K or V tile (rows of 2D bytes,
-  // 16-byte slot p of row r stored at slot p ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1)).
+  // Per-lane LDS byte offsets inside a K or V tile (rows of 2D bytes, 16-byte
+  // slot p of row r stored at slot p ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1)).
   // K, A operand of S^T: row 32 bb + lr, logical slot 2c + lg, i.e. physical
   //   2 (c ^ (lr & 3)) + (lg ^ ((lr >> 2) & 1)):  koff[c & 3] + 128 (c >> 2) + 64 D bb.
   int koff[4];
@@ -194,90 +193,109 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int vj = lane & 15, ve = vj >> 2, vc = vj & 3, vgrp = lane >> 4;
   const int vx = 2 * (vgrp & 1) + (vc >> 1);
   const int vlane = (4 * lg + ve) * 2 * D + 16 * (vx ^ (2 * (ve & 1) + lg)) + 8 * (vc & 1);
-  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0][0]);
-  const unsigned vofs_even = smem_lds + TILE_BYTES + vlane + 64 * (ve >> 1);
-  const unsigned vofs_odd = smem_lds + TILE_BYTES + vlane - 64 * (ve >> 1);
+  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
+  const unsigned vofs_even = smem_lds + 2 * TILE_BYTES + vlane + 64 * (ve >> 1);
+  const unsigned vofs_odd = smem_lds + 2 * TILE_BYTES + vlane - 64 * (ve >> 1);
 
-  auto compute = [&](int s, int u, int buf) {
-    const char* Ks = smem[buf][0];
-    const unsigned vst = (unsigned)buf * (2 * TILE_BYTES);
-    const int64_t k0 = step_kv_off(s) + (int64_t)u * BN;
-    const int64_t left = a.nkv - (int64_t)u * BN;
-    const int nvalid = left < BN ? (int)left : BN;
-    const int64_t q0w = a.q_off + qrow_w;
-    const int nqw = min(32, a.nq - qrow_w);
-    const int cls = ra_plan_class(q0w, nqw, k0, nvalid, a.causal);
-    if (cls == RA_CLASS_SKIP) return;
-    const bool need_mask = cls == RA_CLASS_PARTIAL || nvalid < BN;
+  // ---- schedule ----------------------------------------------------------
+  // The workgroup's key tiles c_0 .. c_{n-1} (ring order, causal tiles past
+  // the last query dropped) are processed in two phases each:
+  //   MFMA phase j:  S(j) = K(c_j) Q^T;  O^T += V(c_{j-1})^T P(j-1)^T
+  //   VALU phase j:  mask, row max, lazy rescale, P(j) = exp2(S(j) c - m), l
+  // Waves 0-3 run phase index (phi) as their own; waves 4-7 run one phase
+  // behind, so on every SIMD (waves w and w + 4) one wave issues MFMAs while
+  // the other does the softmax.  Every phase ends with a barrier.  K(c_k) is
+  // read in phases 2k and 2k+1, V(c_{k-1}) in the same two phases; the
+  // direct loads of K(c_{k+1}) and V(c_k) are issued at the start of phase
+  // 2k into the stages freed by phase 2k-1 and waited for before the barrier
+  // that ends phase 2k+1.  All waves run the same 2n + 2 barriers.
+  int n = 0;
+  for (int s = 0; s < nsteps; ++s) n += step_tiles(s);
 
-    f32x16 sacc[BN / 32];
+  if (n > 0) {  // workgroup-uniform
+    const int grp = wave >> 2;
+    // Load cursor: step ls, tile lu, with the step's tile count, key position
+    // and first row cached.  It walks c_0, c_1, ... once; the V load of c_k
+    // reuses the row and valid count of its K load, and the softmax of c_j
+    // reads the key position and valid count recorded with K(c_j).
+    int ls = 0;
+    while (step_tiles(ls) == 0) ++ls;
+    int lu = 0, lnt = step_tiles(ls);
+    int64_t lkv = step_kv_off(ls);
+    int64_t lrow = a.ring ? lkv : 0;
+    auto cur_nvalid = [&]() -> int {
+      const int64_t left = a.nkv - (int64_t)lu * BN;
+      return left < BN ? (int)left : BN;
+    };
+    auto cur_row = [&]() -> int64_t { return lrow + (int64_t)lu * BN; };
+    auto cur_pos = [&]() -> int64_t { return lkv + (int64_t)lu * BN; };
+    auto step_cursor = [&]() {
+      if (++lu < lnt) return;
+      lu = 0;
+      do {
+        ++ls;
+      } while (ls < nsteps && (lnt = step_tiles(ls)) == 0);
+      if (ls < nsteps) {
+        lkv = step_kv_off(ls);
+        lrow = a.ring ? lkv : 0;
+      }
+    };
+    // row / valid count of the tile whose V is issued next; (position, valid
+    // count) of tiles c_j with j even (hpos0, hval0) and odd (hpos1, hval1)
+    int64_t vrow = cur_row(), hpos0 = cur_pos(), hpos1 = 0, npos = 0;
+    int vval = cur_nvalid(), hval0 = vval, hval1 = 0;
+    issue(kbase, a.k_ss, vrow, vval, 0);
+    step_cursor();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    f32x16 sacc[2];
+    bf16x8 pf[2][2];
 #pragma unroll
-    for (int bb = 0; bb < BN / 32; ++bb) {
+    for (int bb = 0; bb < 2; ++bb) {
       sacc[bb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 kf = *(const bf16x8*)(Ks + koff[c & 3] + 128 * (c >> 2) + 64 * D * bb);
-        sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[bb], 0, 0, 0);
+      for (int hh = 0; hh < 2; ++hh) pf[bb][hh] = bf16x8{};
+    }
+
+    for (int phi = 0; phi <= 2 * n + 1; ++phi) {
+      if (!(phi & 1) && (phi >> 1) < n) {
+        const int k = phi >> 1;
+        issue(vbase, a.v_ss, vrow, vval, 2 + (k & 1));  // V(c_k)
+        if (k + 1 < n) {                                 // K(c_{k+1})
+          vrow = cur_row();
+          vval = cur_nvalid();
+          npos = cur_pos();
+          issue(kbase, a.k_ss, vrow, vval, (k + 1) & 1);
+          step_cursor();
+        }
       }
-    }
-    if (need_mask) {
-      const int64_t qpos = q0w + lr;
+      const int my = phi - grp;
+      if (my >= 0) {
+        const int j = my >> 1;
+        if (!(my & 1)) {
+          // ---- MFMA phase j ----
+          if (j < n) {
+            const char* Ks = smem[j & 1];
 #pragma unroll
-      for (int bb = 0; bb < BN / 32; ++bb)
+            for (int bb = 0; bb < 2; ++bb) {
+              sacc[bb] = f32x16{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kvi = 32 * bb + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (kvi >= nvalid || (a.causal && k0 + kvi > qpos)) sacc[bb][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int bb = 0; bb < BN / 32; ++bb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[bb][r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float t = mx * a.c;
-    // move the max only when it grows by more than kLazyTau (or on the first visible key)
-    const bool bump = t > m2 + kLazyTau;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      const float m_new = bump ? t : m2;
-      const float alpha = bump ? fast_exp2(m2 - t) : 1.f;  // 0 when m2 was -inf
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m2 = m_new;
-    }
-    const float m_use = m2 == -INFINITY ? 0.f : m2;  // no visible key yet: p = 0
-
-    // The row sum takes the fp32 p (only the MFMA operand is rounded to bf16):
-    // rows with few visible keys would otherwise carry the 2^-9 rounding of a
-    // single term into l and the LSE.
-    bf16x8 pf[BN / 32][2];
-    float psum = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < BN / 32; ++bb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-          const float p = fast_exp2(fmaf(sacc[bb][8 * hh + t8], a.c, -m_use));
-          psum += p;
-          pf[bb][hh][t8] = (__bf16)p;
-        }
-    lsum += psum;
-
-    // O^T += V^T P^T.  The transposing reads are issued as inline asm so that
-    // the compiler does not order them behind the in-flight direct loads of
-    // the next stage (it cannot prove they do not alias); the wait that
-    // follows carries their registers, so the MFMAs stay behind it.
-    static_for<0, 2 * (BN / 32)>([&](auto ig) {
-      constexpr int g = decltype(ig)::value, bb = g >> 1, hh = g & 1;
-      u32x2 lo[D / 32], hi[D / 32];
+              for (int c = 0; c < D / 16; ++c) {
+                const bf16x8 kf = *(const bf16x8*)(Ks + koff[c & 3] + 128 * (c >> 2) + 64 * D * bb);
+                sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[bb], 0, 0, 0);
+              }
+            }
+          }
+          if (j >= 1) {
+            // O^T += V^T P^T of tile j-1.  The transposing reads are inline
+            // asm so the compiler does not order them behind the in-flight
+            // direct loads (it cannot prove they do not alias); the wait that
+            // follows carries their registers, so the MFMAs stay behind it.
+            const unsigned vst = (unsigned)((j - 1) & 1) * TILE_BYTES;
+            static_for<0, 4>([&](auto ig) {
+              constexpr int g = decltype(ig)::value, bb = g >> 1, hh = g & 1;
+              u32x2 lo[D / 32], hi[D / 32];
 #define RA_TR_READ(DB)                                                                         \
   if constexpr (DB < D / 32) {                                                                 \
     constexpr int off = 64 * DB + (32 * bb + 16 * hh) * 2 * D;                                 \
@@ -285,45 +303,108 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo[DB]) : "v"(va), "i"(off));    \
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi[DB]) : "v"(va), "i"(off + 16 * D)); \
   }
-      RA_TR_READ(0) RA_TR_READ(1) RA_TR_READ(2) RA_TR_READ(3)
+              RA_TR_READ(0) RA_TR_READ(1) RA_TR_READ(2) RA_TR_READ(3)
 #undef RA_TR_READ
-      if constexpr (D == 128)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]),
-                     "+v"(lo[2]), "+v"(hi[2]), "+v"(lo[3]), "+v"(hi[3]));
-      else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]));
+              if constexpr (D == 128)
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]),
+                             "+v"(lo[2]), "+v"(hi[2]), "+v"(lo[3]), "+v"(hi[3]));
+              else
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]));
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const u32x4 w = {lo[db][0], lo[db][1], hi[db][0], hi[db][1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[bb][hh], o[db], 0, 0, 0);
+              for (int db = 0; db < D / 32; ++db) {
+                const u32x4 w = {lo[db][0], lo[db][1], hi[db][0], hi[db][1]};
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[bb][hh], o[db], 0, 0, 0);
+              }
+            });
+          }
+        } else if (j < n) {
+          // ---- VALU phase j: softmax of tile c_j ----
+          const int64_t k0 = (j & 1) ? hpos1 : hpos0;
+          const int nvalid = (j & 1) ? hval1 : hval0;
+          const int64_t q0w = a.q_off + qrow_w;
+          const int nqw = min(32, a.nq - qrow_w);
+          const int cls = ra_plan_class(q0w, nqw, k0, nvalid, a.causal);
+          if (cls != RA_CLASS_FULL || nvalid < BN) {
+            // Keys kvi < lim of this tile are visible to this lane's query:
+            // lim = valid keys, cut at the query's own position under causal
+            // masking, 0 for SKIP (no visible key for these rows: p = 0).  The
+            // key index of register r is 32 bb + 8 (r / 4) + (r % 4) + 4 lg.
+            int64_t lim64 = cls == RA_CLASS_SKIP ? 0 : nvalid;
+            if (a.causal) {
+              const int64_t vis = q0w + lr - k0 + 1;
+              lim64 = vis < lim64 ? (vis > 0 ? vis : 0) : lim64;
+            }
+            const int lim = (int)lim64 - 4 * lg;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                sacc[bb][r] = (32 * bb + 8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : sacc[bb][r];
+          }
+          float mx = -INFINITY;
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[bb][r]);
+          {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          }
+          const float t = mx * a.c;
+          const bool bump = t > m2 + kLazyTau;  // move the max only when it grows by more than kLazyTau
+          if (__builtin_amdgcn_ballot_w64(bump)) {
+            const float alpha = bump ? fast_exp2(m2 - t) : 1.f;  // 0 when m2 was -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m2 = bump ? t : m2;
+          }
+          const float m_use = m2 == -INFINITY ? 0.f : m2;  // no visible key yet: p = 0
+          // The row sum takes the fp32 p (only the MFMA operand is rounded to
+          // bf16): rows with few visible keys would otherwise carry the 2^-9
+          // rounding of one term into l and the LSE.
+          float psum = 0.f;
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int t8 = 0; t8 < 8; ++t8) {
+                const float p = fast_exp2(fmaf(sacc[bb][8 * hh + t8], a.c, -m_use));
+                psum += p;
+                pf[bb][hh][t8] = (__bf16)p;
+              }
+          lsum += psum;
+        }
       }
-    });
-  };
-
-  // Flat loop over (step, tile) in ring order, two LDS stages: the loads of
-  // the next tile are issued right after the barrier that retires the stage
-  // they overwrite, and waited for at the top of the next iteration.
-  int s = 0;
-  while (s < nsteps && step_tiles(s) == 0) ++s;
-  int u = 0, it = 0;
-  if (s < nsteps) issue_tile(s, 0, 0);
-  while (s < nsteps) {
-    const int nt = step_tiles(s);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    int s2 = s, u2 = u + 1;
-    if (u2 >= nt) {
-      u2 = 0;
-      ++s2;
-      while (s2 < nsteps && step_tiles(s2) == 0) ++s2;
+      // c_{k+1}'s position and valid count go into its history slot only now:
+      // waves 4-7 read c_{k-1}'s (same slot) earlier in this phase.
+      if (!(phi & 1) && (phi >> 1) + 1 < n) {
+        if (((phi >> 1) + 1) & 1) {
+          hpos1 = npos;
+          hval1 = vval;
+        } else {
+          hpos0 = npos;
+          hval0 = vval;
+        }
+      }
+      // Phase barrier.  Only the odd ones publish LDS data (the direct loads
+      // issued two phases earlier), so only they wait for vmcnt; the even
+      // ones just order this phase's LDS reads before the next loads.  Inline
+      // asm with a memory clobber keeps the compiler from moving LDS accesses
+      // across it (and from adding its own full waits).
+      if (phi < 2 * n + 1) {
+        if (phi & 1)
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+          asm volatile("s_barrier" ::: "memory");
+      }
     }
-    if (s2 < nsteps) issue_tile(s2, u2, (it + 1) & 1);
-    compute(s, u, it & 1);
-    s = s2;
-    u = u2;
-    ++it;
   }
 
+  // Epilogue: the two halves of each row sum live in lanes lr and lr + 32.
   float ltot;
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);

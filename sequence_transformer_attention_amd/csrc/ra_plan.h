@@ -23,6 +23,12 @@ RA_HD int64_t ra_plan_ring_block(int64_t P, int64_t rank, int64_t s) {
   return j < 0 ? j + P : j;
 }
 
+// 32-bit form for device loops (P, rank, s < 2^31).
+RA_HD int ra_plan_ring_block32(int P, int rank, int s) {
+  int j = (rank - s) % P;
+  return j < 0 ? j + P : j;
+}
+
 RA_HD int ra_plan_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, int causal) {
   if (nq <= 0 || nk <= 0) return RA_CLASS_SKIP;
   if (!causal) return RA_CLASS_FULL;

@@ -70,11 +70,17 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr float kLazyTau = 8.0f;
 
-// Physical 16-byte slot of logical slot p in LDS row r.  Eight consecutive
-// rows map one logical slot to eight different bank groups (K reads, 16 B per
-// lane); four consecutive rows (aligned to 4) map a slot pair {2k, 2k+1} to
-// eight different bank groups (transposing V reads, 8 B per lane).
-__device__ __forceinline__ int swz(int r, int p) { return p ^ (((r & 3) << 1) | ((r >> 2) & 1)); }
+// Physical 16-byte slot of logical slot p in LDS row r: p ^ f(r), with
+// f(r) = 4 (r & 3) + ((r >> 2) & 3) (the two low 2-bit fields of r swapped),
+// cut to the row's slot count.  With 64 LDS banks (256 bytes per cycle) a
+// 128-bit read of 16 consecutive rows at one logical slot, and a transposing
+// 64-bit read of 4 consecutive rows (aligned to 4) at 4 consecutive slots
+// (aligned to 4), both touch 16 different 16-byte bank groups.  f depends on
+// r & 15 only, so row offsets that are multiples of 16 keep the pattern.
+template <int SLOTS>
+__device__ __forceinline__ int swz(int r, int p) {
+  return p ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (SLOTS - 1));
+}
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i in [I, N).
 template <int I, int N, typename F>
@@ -173,29 +179,33 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       const int ls = inst * 64 + lane;
       const int r = ls / SLOTS, p = ls % SLOTS;
       const int64_t gr = row0 + (r < last ? r : last);
-      const __bf16* g = base + gr * stride + swz(r, p) * 8;
+      const __bf16* g = base + gr * stride + swz<SLOTS>(r, p) * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(&smem[stage][inst * 1024]), 16, 0, 0);
     }
   };
 
-  // Per-lane LDS byte offsets inside a K or V tile (rows of 2D bytes, 16-byte
-  // slot p of row r stored at slot p ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1)).
-  // K, A operand of S^T: row 32 bb + lr, logical slot 2c + lg, i.e. physical
-  //   2 (c ^ (lr & 3)) + (lg ^ ((lr >> 2) & 1)):  koff[c & 3] + 128 (c >> 2) + 64 D bb.
-  int koff[4];
+  // Per-lane LDS byte offsets inside a K or V tile (rows of 2D bytes).
+  // K, A operand of S^T for key block bb: row 32 bb + lr, logical slot 2c + lg:
+  //   koff[c] + 64 D bb.
+  int koff[D / 16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) koff[j] = lr * 2 * D + 32 * (j ^ (lr & 3)) + 16 * (lg ^ ((lr >> 2) & 1));
-  // V, transposing reads: source lane j = lane % 16 supplies row
-  //   32 bb + 16 hh + 8 half + 4 (lane / 32) + j / 4 and the 8 bytes at channel
-  //   32 db + 16 ((lane / 16) % 2) + 4 (j % 4); with ve = j / 4, vc = j % 4,
-  //   x = 2 ((lane / 16) % 2) + vc / 2 the physical slot is
-  //   4 (db ^ (ve >> 1)) + (x ^ (2 (ve & 1) + lane / 32)).
+  for (int c = 0; c < D / 16; ++c) koff[c] = lr * 2 * D + 16 * swz<SLOTS>(lr, 2 * c + lg);
+  // V, transposing reads for key block bb, half hh, second 8 rows (+8): source
+  // lane j = lane % 16 supplies row 32 bb + 16 hh + 8 half + 4 (lane / 32) + j / 4
+  // and the 8 bytes at channel 32 db + 16 ((lane / 16) % 2) + 4 (j % 4), i.e.
+  // logical slot 4 db + 2 ((lane / 16) % 2) + (j % 4) / 2, byte 8 (j % 2):
+  //   voff[half][db] + 2D (32 bb + 16 hh).
   const int vj = lane & 15, ve = vj >> 2, vc = vj & 3, vgrp = lane >> 4;
   const int vx = 2 * (vgrp & 1) + (vc >> 1);
-  const int vlane = (4 * lg + ve) * 2 * D + 16 * (vx ^ (2 * (ve & 1) + lg)) + 8 * (vc & 1);
   const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
-  const unsigned vofs_even = smem_lds + 2 * TILE_BYTES + vlane + 64 * (ve >> 1);
-  const unsigned vofs_odd = smem_lds + 2 * TILE_BYTES + vlane - 64 * (ve >> 1);
+  unsigned voff[2][D / 32];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int r = 4 * lg + ve + 8 * half;
+      voff[half][db] = smem_lds + 2 * TILE_BYTES + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
+    }
 
   // ---- schedule ----------------------------------------------------------
   // The workgroup's key tiles c_0 .. c_{n-1} (ring order, causal tiles past
@@ -276,16 +286,23 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
         if (!(my & 1)) {
           // ---- MFMA phase j ----
           if (j < n) {
+            // all K fragments of the tile first, then the MFMAs, so the LDS
+            // latency is paid once per tile rather than once per MFMA
             const char* Ks = smem[j & 1];
+            bf16x8 kf[2][D / 16];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+              for (int c = 0; c < D / 16; ++c) kf[bb][c] = *(const bf16x8*)(Ks + koff[c] + 64 * D * bb);
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
               sacc[bb] = f32x16{};
 #pragma unroll
-              for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 kf = *(const bf16x8*)(Ks + koff[c & 3] + 128 * (c >> 2) + 64 * D * bb);
-                sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[bb], 0, 0, 0);
-              }
+              for (int c = 0; c < D / 16; ++c)
+                sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bb][c], qf[c], sacc[bb], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // the LDS reads first
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 16), 0);  // then the MFMAs
           }
           if (j >= 1) {
             // O^T += V^T P^T of tile j-1.  The transposing reads are inline
@@ -293,29 +310,65 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
             // direct loads (it cannot prove they do not alias); the wait that
             // follows carries their registers, so the MFMAs stay behind it.
             const unsigned vst = (unsigned)((j - 1) & 1) * TILE_BYTES;
-            static_for<0, 4>([&](auto ig) {
-              constexpr int g = decltype(ig)::value, bb = g >> 1, hh = g & 1;
-              u32x2 lo[D / 32], hi[D / 32];
-#define RA_TR_READ(DB)                                                                         \
-  if constexpr (DB < D / 32) {                                                                 \
-    constexpr int off = 64 * DB + (32 * bb + 16 * hh) * 2 * D;                                 \
-    const unsigned va = ((DB & 1) ? vofs_odd : vofs_even) + vst;                               \
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo[DB]) : "v"(va), "i"(off));    \
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi[DB]) : "v"(va), "i"(off + 16 * D)); \
+            u32x2 lo[2][D / 32], hi[2][D / 32];
+#define RA_TR_READ(BUF, G, DB)                                                                   \
+  if constexpr (DB < D / 32) {                                                                   \
+    constexpr int off = (32 * ((G) >> 1) + 16 * ((G) & 1)) * 2 * D;                             \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo[BUF][DB]) : "v"(voff[0][DB] + vst), "i"(off)); \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi[BUF][DB]) : "v"(voff[1][DB] + vst), "i"(off)); \
   }
-              RA_TR_READ(0) RA_TR_READ(1) RA_TR_READ(2) RA_TR_READ(3)
+#define RA_TR_GROUP(BUF, G) RA_TR_READ(BUF, G, 0) RA_TR_READ(BUF, G, 1) RA_TR_READ(BUF, G, 2) RA_TR_READ(BUF, G, 3)
+#define RA_TR_WAIT(BUF, N)                                                                       \
+  if constexpr (D == 128)                                                                        \
+    asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(lo[BUF][0]), "+v"(hi[BUF][0]), "+v"(lo[BUF][1]), \
+                 "+v"(hi[BUF][1]), "+v"(lo[BUF][2]), "+v"(hi[BUF][2]), "+v"(lo[BUF][3]), "+v"(hi[BUF][3])); \
+  else                                                                                           \
+    asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(lo[BUF][0]), "+v"(hi[BUF][0]), "+v"(lo[BUF][1]), \
+                 "+v"(hi[BUF][1]));
+#define RA_PV(BUF, G)                                                                            \
+  _Pragma("unroll") for (int db = 0; db < D / 32; ++db) {                                        \
+    const u32x4 w = {lo[BUF][db][0], lo[BUF][db][1], hi[BUF][db][0], hi[BUF][db][1]};            \
+    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),               \
+                                                    pf[(G) >> 1][(G) & 1], o[db], 0, 0, 0);      \
+  }
+            // O^T += V^T P^T of tile j-1, four (key block, half) groups; the
+            // reads of group g+1 are in flight while group g's MFMAs issue.
+            // The transposing reads are inline asm so the compiler does not
+            // order them behind the in-flight direct loads (it cannot prove
+            // they do not alias); each wait carries the registers it
+            // guarantees, so the MFMAs stay behind it.  lgkmcnt counts only
+            // these reads here (LDS completes in order; scalar loads only add).
+            if constexpr (D == 128) {
+              RA_TR_GROUP(0, 0)
+              RA_TR_GROUP(1, 1)
+              RA_TR_WAIT(0, 8)
+              RA_PV(0, 0)
+              RA_TR_GROUP(0, 2)
+              RA_TR_WAIT(1, 8)
+              RA_PV(1, 1)
+              RA_TR_GROUP(1, 3)
+              RA_TR_WAIT(0, 8)
+              RA_PV(0, 2)
+              RA_TR_WAIT(1, 0)
+              RA_PV(1, 3)
+            } else {
+              RA_TR_GROUP(0, 0)
+              RA_TR_GROUP(1, 1)
+              RA_TR_WAIT(0, 4)
+              RA_PV(0, 0)
+              RA_TR_GROUP(0, 2)
+              RA_TR_WAIT(1, 4)
+              RA_PV(1, 1)
+              RA_TR_GROUP(1, 3)
+              RA_TR_WAIT(0, 4)
+              RA_PV(0, 2)
+              RA_TR_WAIT(1, 0)
+              RA_PV(1, 3)
+            }
+#undef RA_PV
+#undef RA_TR_WAIT
+#undef RA_TR_GROUP
 #undef RA_TR_READ
-              if constexpr (D == 128)
-                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]),
-                             "+v"(lo[2]), "+v"(hi[2]), "+v"(lo[3]), "+v"(hi[3]));
-              else
-                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]));
-#pragma unroll
-              for (int db = 0; db < D / 32; ++db) {
-                const u32x4 w = {lo[db][0], lo[db][1], hi[db][0], hi[db][1]};
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[bb][hh], o[db], 0, 0, 0);
-              }
-            });
           }
         } else if (j < n) {
           // ---- VALU phase j: softmax of tile c_j ----

@@ -99,8 +99,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   constexpr int NI = BN * SLOTS / NT;          // direct-load instructions per thread per tile
   static_assert(NI * NT == BN * SLOTS, "tile split");
   static_assert(BN == 64, "the softmax below is written for two 32-key halves");
-  // [0], [1]: K stages; [2], [3]: V stages
-  __shared__ __attribute__((aligned(1024))) char smem[4][TILE_BYTES];
+  // [0], [1]: K stages; [2], [3], [4]: V stages
+  __shared__ __attribute__((aligned(1024))) char smem[5][TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
@@ -156,9 +156,15 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int64_t q0_wg = a.q_off + qrow_wg;
   const int nq_wg = min(BM, a.nq - qrow_wg);
   const int nsteps = a.ring ? a.P : 1;
-  // key position of block (step) s; in ring mode also its first row in k/v
+  // Key position (ring mode: also first row in k/v) of the block folded at
+  // loop step s.  The blocks arrive in ring order (block (rank - s) mod P at
+  // ring step s); the rank's own block (ring step 0) is resident from the
+  // start and is folded last.  Every other block is then walked in lockstep
+  // by all query tiles of a head (the own block's causal tile count differs
+  // per query tile and would spread them apart), which keeps the K/V stream
+  // they share in L2.  The merge is order-independent: only rounding changes.
   auto step_kv_off = [&](int s) -> int64_t {
-    return a.ring ? (int64_t)ra_plan_ring_block32(a.P, a.rank, s) * a.nkv : a.kv_off;
+    return a.ring ? (int64_t)ra_plan_ring_block32(a.P, a.rank, (s + 1) % a.P) * a.nkv : a.kv_off;
   };
   auto step_tiles = [&](int s) -> int {
     return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
@@ -171,11 +177,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
   // row0: first row of the tile in k/v; nvalid: rows of the tile inside the block
+  // Each tile is loaded by one group of four waves (2 NI instructions each):
+  // K by waves 4-7, V by waves 0-3, each in its softmax phase.
   auto issue = [&](const __bf16* base, int64_t stride, int64_t row0, int nvalid, int stage) {
     const int last = nvalid - 1;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int inst = wave * NI + i;
+    for (int i = 0; i < 2 * NI; ++i) {
+      const int inst = (wave & 3) * 2 * NI + i;
       const int ls = inst * 64 + lane;
       const int r = ls / SLOTS, p = ls % SLOTS;
       const int64_t gr = row0 + (r < last ? r : last);
@@ -223,7 +231,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   for (int s = 0; s < nsteps; ++s) n += step_tiles(s);
 
   if (n > 0) {  // workgroup-uniform
-    const int grp = wave >> 2;
+    const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7
     // Load cursor: step ls, tile lu, with the step's tile count, key position
     // and first row cached.  It walks c_0, c_1, ... once; the V load of c_k
     // reuses the row and valid count of its K load, and the softmax of c_j
@@ -254,7 +262,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // count) of tiles c_j with j even (hpos0, hval0) and odd (hpos1, hval1)
     int64_t vrow = cur_row(), hpos0 = cur_pos(), hpos1 = 0, npos = 0;
     int vval = cur_nvalid(), hval0 = vval, hval1 = 0;
-    issue(kbase, a.k_ss, vrow, vval, 0);
+    if (grp == 1) issue(kbase, a.k_ss, vrow, vval, 0);  // K(c_0)
+    else issue(vbase, a.v_ss, vrow, vval, 2);             // V(c_0)
     step_cursor();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -269,16 +278,22 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     }
 
     for (int phi = 0; phi <= 2 * n + 1; ++phi) {
-      if (!(phi & 1) && (phi >> 1) < n) {
+      // Loads.  Phase 2k: waves 4-7 issue K(c_{k+1}) (into the K stage read in
+      // phases 2k-2, 2k-1).  Phase 2k+1: waves 0-3 issue V(c_{k+1}) (into V
+      // stage (k+1) % 3, read in phases 2k-2, 2k-1).  (vrow, vval) describe
+      // c_{k+1} from phase 2k on.
+      bool v_issued = false;
+      if (!(phi & 1) && (phi >> 1) + 1 < n) {
         const int k = phi >> 1;
-        issue(vbase, a.v_ss, vrow, vval, 2 + (k & 1));  // V(c_k)
-        if (k + 1 < n) {                                 // K(c_{k+1})
-          vrow = cur_row();
-          vval = cur_nvalid();
-          npos = cur_pos();
-          issue(kbase, a.k_ss, vrow, vval, (k + 1) & 1);
-          step_cursor();
-        }
+        vrow = cur_row();
+        vval = cur_nvalid();
+        npos = cur_pos();
+        if (grp == 1) issue(kbase, a.k_ss, vrow, vval, (k + 1) & 1);
+        step_cursor();
+      }
+      if ((phi & 1) && (phi >> 1) + 1 < n && grp == 0) {
+        issue(vbase, a.v_ss, vrow, vval, 2 + ((phi >> 1) + 1) % 3);
+        v_issued = true;
       }
       const int my = phi - grp;
       if (my >= 0) {
@@ -309,7 +324,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
             // asm so the compiler does not order them behind the in-flight
             // direct loads (it cannot prove they do not alias); the wait that
             // follows carries their registers, so the MFMAs stay behind it.
-            const unsigned vst = (unsigned)((j - 1) & 1) * TILE_BYTES;
+            const unsigned vst = (unsigned)((j - 1) % 3) * TILE_BYTES;
             u32x2 lo[2][D / 32], hi[2][D / 32];
 #define RA_TR_READ(BUF, G, DB)                                                                   \
   if constexpr (DB < D / 32) {                                                                   \
@@ -448,11 +463,16 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       // ones just order this phase's LDS reads before the next loads.  Inline
       // asm with a memory clobber keeps the compiler from moving LDS accesses
       // across it (and from adding its own full waits).
+      // Odd barriers publish the loads issued two phases earlier: K(c_{k+1})
+      // of waves 4-7 (phase 2k) and V(c_k) of waves 0-3 (phase 2k-1); a V
+      // group issued in this phase may stay in flight.
       if (phi < 2 * n + 1) {
-        if (phi & 1)
-          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        else
+        if (!(phi & 1))
           asm volatile("s_barrier" ::: "memory");
+        else if (v_issued)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NI) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       }
     }
   }

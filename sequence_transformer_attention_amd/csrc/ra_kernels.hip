@@ -102,7 +102,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // [0], [1]: K stages; [2], [3], [4]: V stages
   __shared__ __attribute__((aligned(1024))) char smem[5][TILE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform: keep it (and the schedule built on it) in SGPRs
+  const int wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
 
   const int nqt = (a.nq + BM - 1) / BM;
@@ -170,25 +172,47 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
   };
 
-  // Direct loads of one key tile: lane L of instruction (wave, i) fills
-  // physical slot (wave*NI + i)*64 + L of the tile and loads the logical slot
-  // that the swizzle puts there.  Rows past the block end re-read the last
-  // valid row (finite data; masked in S, zero weight in P).
-  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
-  // row0: first row of the tile in k/v; nvalid: rows of the tile inside the block
-  // Each tile is loaded by one group of four waves (2 NI instructions each):
-  // K by waves 4-7, V by waves 0-3, each in its softmax phase.
-  auto issue = [&](const __bf16* base, int64_t stride, int64_t row0, int nvalid, int stage) {
-    const int last = nvalid - 1;
+  // Direct loads of one key tile.  Each tile is loaded by one group of four
+  // waves, 2 NI instructions each: K by waves 4-7, V by waves 0-3, each in its
+  // softmax phase.  Lane L of instruction inst = (wave & 3) 2 NI + i fills
+  // physical slot inst * 64 + L of the tile (row r, physical slot p) and loads
+  // the logical slot that the swizzle puts there.  The global address is a
+  // uniform tile base plus a per-lane 32-bit offset fixed for the kernel.  In
+  // the last tile of a block, rows past the block end re-read the last valid
+  // row (finite data; masked in S, zero weight in P).
+  const char* gbase = (wave >> 2) ? (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh)
+                                  : (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
+  const int64_t gstride = (wave >> 2) ? a.k_ss : a.v_ss;  // elements; 64 rows fit 32-bit offsets
+  auto gslot = [&](int i, int& r) -> unsigned {
+    const int ls = ((wave & 3) * 2 * NI + i) * 64 + lane;
+    r = ls / SLOTS;
+    return 16u * (unsigned)swz<SLOTS>(r, ls % SLOTS);
+  };
+  unsigned goff[2 * NI];
 #pragma unroll
-    for (int i = 0; i < 2 * NI; ++i) {
-      const int inst = (wave & 3) * 2 * NI + i;
-      const int ls = inst * 64 + lane;
-      const int r = ls / SLOTS, p = ls % SLOTS;
-      const int64_t gr = row0 + (r < last ? r : last);
-      const __bf16* g = base + gr * stride + swz<SLOTS>(r, p) * 8;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(&smem[stage][inst * 1024]), 16, 0, 0);
+  for (int i = 0; i < 2 * NI; ++i) {
+    int r;
+    const unsigned sl = gslot(i, r);
+    goff[i] = (unsigned)r * (unsigned)gstride * 2u + sl;
+  }
+  // row0: first row of the tile in k/v; nvalid: rows of the tile inside the block
+  auto issue = [&](int64_t row0, int nvalid, int stage) {
+    const char* tb = gbase + row0 * gstride * 2;
+    if (nvalid == BN) {
+#pragma unroll
+      for (int i = 0; i < 2 * NI; ++i)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(tb + goff[i]),
+                                         (lds_void_t*)(&smem[stage][((wave & 3) * 2 * NI + i) * 1024]), 16, 0, 0);
+    } else {
+      const int last = nvalid - 1;
+#pragma unroll
+      for (int i = 0; i < 2 * NI; ++i) {
+        int r;
+        const unsigned sl = gslot(i, r);
+        const unsigned off = (unsigned)(r < last ? r : last) * (unsigned)gstride * 2u + sl;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(tb + off),
+                                         (lds_void_t*)(&smem[stage][((wave & 3) * 2 * NI + i) * 1024]), 16, 0, 0);
+      }
     }
   };
 
@@ -262,8 +286,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // count) of tiles c_j with j even (hpos0, hval0) and odd (hpos1, hval1)
     int64_t vrow = cur_row(), hpos0 = cur_pos(), hpos1 = 0, npos = 0;
     int vval = cur_nvalid(), hval0 = vval, hval1 = 0;
-    if (grp == 1) issue(kbase, a.k_ss, vrow, vval, 0);  // K(c_0)
-    else issue(vbase, a.v_ss, vrow, vval, 2);             // V(c_0)
+    issue(vrow, vval, grp ? 0 : 2);  // K(c_0) by waves 4-7, V(c_0) by waves 0-3
     step_cursor();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -288,11 +311,11 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
         vrow = cur_row();
         vval = cur_nvalid();
         npos = cur_pos();
-        if (grp == 1) issue(kbase, a.k_ss, vrow, vval, (k + 1) & 1);
+        if (grp == 1) issue(vrow, vval, (k + 1) & 1);
         step_cursor();
       }
       if ((phi & 1) && (phi >> 1) + 1 < n && grp == 0) {
-        issue(vbase, a.v_ss, vrow, vval, 2 + ((phi >> 1) + 1) % 3);
+        issue(vrow, vval, 2 + ((phi >> 1) + 1) % 3);
         v_issued = true;
       }
       const int my = phi - grp;

@@ -91,20 +91,28 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Position in the workgroup's key tile sequence: loop step s, tile u of the
+// step's nt tiles, the step's first key position kv.
+struct TileCursor {
+  int s, u, nt;
+  int64_t kv;
+};
+
 template <int D>
 __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
-  constexpr int NW = 8, BM = NW * 32, BN = RA_BF16_BN, NT = NW * 64;
+  constexpr int NW = 8, BM = NW * 32, BN = RA_BF16_BN;
   constexpr int SLOTS = D / 8;                 // 16-byte slots per row
   constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
-  constexpr int NI = BN * SLOTS / NT;          // direct-load instructions per thread per tile
-  static_assert(NI * NT == BN * SLOTS, "tile split");
-  static_assert(BN == 64, "the softmax below is written for two 32-key halves");
-  // [0], [1]: K stages; [2], [3], [4]: V stages
-  __shared__ __attribute__((aligned(1024))) char smem[5][TILE_BYTES];
+  constexpr int NL = TILE_BYTES / 1024 / NW;   // 1 KiB direct loads per wave per tile
+  constexpr int KC = D / 16;                   // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;                   // 32-channel blocks of O^T
+  static_assert(NL * 1024 * NW == TILE_BYTES, "tile split");
+  static_assert(BM == RA_BF16_BM && BN == 64, "64-key tiles, processed as two 32-key units");
+  // [0], [1], [2]: K stages; [3] .. [6]: V stages
+  __shared__ __attribute__((aligned(1024))) char smem[7][TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // the wave index is uniform: keep it (and the schedule built on it) in SGPRs
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep per-wave values in SGPRs
   const int lr = lane & 31, lg = lane >> 5;
 
   const int nqt = (a.nq + BM - 1) / BM;
@@ -121,12 +129,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const bool q_ok = my_q < a.nq;
 
   // Q fragment (B operand of S^T = K Q^T): lane holds Q[my_q][16c + 8lg .. +7].
-  bf16x8 qf[D / 16];
+  bf16x8 qf[KC];
   {
-    const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)my_q * a.q_ss +
+    const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)(q_ok ? my_q : 0) * a.q_ss +
                        (int64_t)h * a.q_sh + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+    for (int c = 0; c < KC; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (q_ok) w = *(const u32x4*)(qp + 16 * c);
       qf[c] = __builtin_bit_cast(bf16x8, w);
@@ -135,14 +143,14 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
 
   // Running state.  o[db][r] = O^T[32db + 8(r/4) + 4lg + r%4][my_q] (unnormalised);
   // m2 = running max of s * c (log2 units); lsum = this lane's half of the row sum.
-  f32x16 o[D / 32];
+  f32x16 o[DB];
   float m2 = -INFINITY, lsum = 0.f;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   if (a.state_in && q_ok) {
     const float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 x = *(const f32x4*)(op + 32 * db + 8 * j + 4 * lg);
@@ -172,332 +180,424 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
   };
 
-  // Direct loads of one key tile.  Each tile is loaded by one group of four
-  // waves, 2 NI instructions each: K by waves 4-7, V by waves 0-3, each in its
-  // softmax phase.  Lane L of instruction inst = (wave & 3) 2 NI + i fills
-  // physical slot inst * 64 + L of the tile (row r, physical slot p) and loads
-  // the logical slot that the swizzle puts there.  The global address is a
-  // uniform tile base plus a per-lane 32-bit offset fixed for the kernel.  In
-  // the last tile of a block, rows past the block end re-read the last valid
-  // row (finite data; masked in S, zero weight in P).
-  const char* gbase = (wave >> 2) ? (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh)
-                                  : (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
-  const int64_t gstride = (wave >> 2) ? a.k_ss : a.v_ss;  // elements; 64 rows fit 32-bit offsets
+  // Direct loads.  All eight waves load a share (NL KiB) of each K and V
+  // tile: lane L of instruction inst = wave NL + i fills physical slot
+  // inst * 64 + L of the tile (row r, physical slot p) and loads the logical
+  // slot that the swizzle puts there.  The loads are buffer loads: a scalar
+  // descriptor based at the tile's first row plus a per-lane 32-bit offset
+  // fixed for the kernel.  In the last tile of a block, rows past the block
+  // end re-read the last valid row (finite data; masked in S, zero weight in P).
+  const char* kbase = (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
+  const char* vbase = (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (waves w and w + 4 share a SIMD)
   auto gslot = [&](int i, int& r) -> unsigned {
-    const int ls = ((wave & 3) * 2 * NI + i) * 64 + lane;
+    const int ls = (wv * NL + i) * 64 + lane;
     r = ls / SLOTS;
     return 16u * (unsigned)swz<SLOTS>(r, ls % SLOTS);
   };
-  unsigned goff[2 * NI];
+  unsigned koffg[NL], voffg[NL];  // row strides of k and v: at most 2^24 elements
 #pragma unroll
-  for (int i = 0; i < 2 * NI; ++i) {
+  for (int i = 0; i < NL; ++i) {
     int r;
     const unsigned sl = gslot(i, r);
-    goff[i] = (unsigned)r * (unsigned)gstride * 2u + sl;
+    koffg[i] = (unsigned)r * (unsigned)a.k_ss * 2u + sl;
+    voffg[i] = (unsigned)r * (unsigned)a.v_ss * 2u + sl;
   }
-  // row0: first row of the tile in k/v; nvalid: rows of the tile inside the block
-  auto issue = [&](int64_t row0, int nvalid, int stage) {
-    const char* tb = gbase + row0 * gstride * 2;
+  // Tile at row row0 of base (k or v, row stride `stride`) with nvalid valid
+  // rows into LDS stage `stage`.
+  auto issue = [&](const char* base, int64_t stride, const unsigned* goff, int64_t row0, int nvalid, int stage)
+      __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + row0 * stride * 2), (short)0, (int)(unsigned)(BN * stride * 2), 0x00020000);
+    char* dst = &smem[stage][0] + wv * NL * 1024;
     if (nvalid == BN) {
 #pragma unroll
-      for (int i = 0; i < 2 * NI; ++i)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(tb + goff[i]),
-                                         (lds_void_t*)(&smem[stage][((wave & 3) * 2 * NI + i) * 1024]), 16, 0, 0);
+      for (int i = 0; i < NL; ++i) {
+        const unsigned off = goff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, off, 0, 0, 0);
+      }
     } else {
       const int last = nvalid - 1;
 #pragma unroll
-      for (int i = 0; i < 2 * NI; ++i) {
+      for (int i = 0; i < NL; ++i) {
         int r;
         const unsigned sl = gslot(i, r);
-        const unsigned off = (unsigned)(r < last ? r : last) * (unsigned)gstride * 2u + sl;
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(tb + off),
-                                         (lds_void_t*)(&smem[stage][((wave & 3) * 2 * NI + i) * 1024]), 16, 0, 0);
+        const unsigned off = (unsigned)(r < last ? r : last) * (unsigned)stride * 2u + sl;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, off, 0, 0, 0);
       }
     }
   };
 
-  // Per-lane LDS byte offsets inside a K or V tile (rows of 2D bytes).
-  // K, A operand of S^T for key block bb: row 32 bb + lr, logical slot 2c + lg:
-  //   koff[c] + 64 D bb.
-  int koff[D / 16];
+  // Per-lane LDS byte addresses inside a K or V tile (rows of 2D bytes).
+  // K, A operand of S^T for the 32-key unit at row 32 h of the tile: row
+  // 32 h + lr, logical slot 2c + lg: kaddr[c] + (K stage) + 64 D h.
+  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
+  unsigned kaddr[KC];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) koff[c] = lr * 2 * D + 16 * swz<SLOTS>(lr, 2 * c + lg);
-  // V, transposing reads for key block bb, half hh, second 8 rows (+8): source
-  // lane j = lane % 16 supplies row 32 bb + 16 hh + 8 half + 4 (lane / 32) + j / 4
-  // and the 8 bytes at channel 32 db + 16 ((lane / 16) % 2) + 4 (j % 4), i.e.
-  // logical slot 4 db + 2 ((lane / 16) % 2) + (j % 4) / 2, byte 8 (j % 2):
-  //   voff[half][db] + 2D (32 bb + 16 hh).
+  for (int c = 0; c < KC; ++c) kaddr[c] = smem_lds + lr * 2 * D + 16 * swz<SLOTS>(lr, 2 * c + lg);
+  // V, transposing reads for the unit at row 32 h, 16-key group hh, second 8
+  // rows (+8): source lane j = lane % 16 supplies row 32 h + 16 hh + 8 half +
+  // 4 (lane / 32) + j / 4 and the 8 bytes at channel 32 db + 16 ((lane / 16) % 2)
+  // + 4 (j % 4), i.e. logical slot 4 db + 2 ((lane / 16) % 2) + (j % 4) / 2,
+  // byte 8 (j % 2): voff[half][db] + (V stage) + 2D (32 h + 16 hh).
   const int vj = lane & 15, ve = vj >> 2, vc = vj & 3, vgrp = lane >> 4;
   const int vx = 2 * (vgrp & 1) + (vc >> 1);
-  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
-  unsigned voff[2][D / 32];
+  unsigned voff[2][DB];
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < DB; ++db) {
       const int r = 4 * lg + ve + 8 * half;
-      voff[half][db] = smem_lds + 2 * TILE_BYTES + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
+      voff[half][db] = smem_lds + 3 * TILE_BYTES + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
     }
 
   // ---- schedule ----------------------------------------------------------
   // The workgroup's key tiles c_0 .. c_{n-1} (ring order, causal tiles past
-  // the last query dropped) are processed in two phases each:
-  //   MFMA phase j:  S(j) = K(c_j) Q^T;  O^T += V(c_{j-1})^T P(j-1)^T
-  //   VALU phase j:  mask, row max, lazy rescale, P(j) = exp2(S(j) c - m), l
-  // Waves 0-3 run phase index (phi) as their own; waves 4-7 run one phase
-  // behind, so on every SIMD (waves w and w + 4) one wave issues MFMAs while
-  // the other does the softmax.  Every phase ends with a barrier.  K(c_k) is
-  // read in phases 2k and 2k+1, V(c_{k-1}) in the same two phases; the
-  // direct loads of K(c_{k+1}) and V(c_k) are issued at the start of phase
-  // 2k into the stages freed by phase 2k-1 and waited for before the barrier
-  // that ends phase 2k+1.  All waves run the same 2n + 2 barriers.
+  // the last query dropped; 64 keys each) are processed as 32-key units
+  // u = 2t + h (half h of tile t).  Every wave runs the same software
+  // pipeline, one step per unit: step u issues the MFMAs of
+  //   S(u+1) = K(u+1) Q^T   and   O^T += V(u-1)^T P(u-1)^T
+  // interleaved with the vector work of the softmax of S(u) (mask, row max,
+  // lazy max update, P(u) = exp2(S c - m), row sum), which depends on
+  // neither; the rescale of O after a max update follows the step.  Two waves
+  // share each SIMD, so both the matrix cores and the vector ALUs are fed by
+  // two instruction streams.  The K fragments of unit u+1 are read in the
+  // second half of step u-1, the V^T fragments of unit u-1 in the first half
+  // of step u.  One barrier per tile: iteration t (units 2t, 2t+1) starts by
+  // publishing K(c_{t+1}) and V(c_t) (loaded two iterations earlier) and then
+  // issues the loads of K(c_{t+3}) and V(c_{t+2}) (three K and four V stages).
   int n = 0;
   for (int s = 0; s < nsteps; ++s) n += step_tiles(s);
 
   if (n > 0) {  // workgroup-uniform
-    const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7
-    // Load cursor: step ls, tile lu, with the step's tile count, key position
-    // and first row cached.  It walks c_0, c_1, ... once; the V load of c_k
-    // reuses the row and valid count of its K load, and the softmax of c_j
-    // reads the key position and valid count recorded with K(c_j).
-    int ls = 0;
-    while (step_tiles(ls) == 0) ++ls;
-    int lu = 0, lnt = step_tiles(ls);
-    int64_t lkv = step_kv_off(ls);
-    int64_t lrow = a.ring ? lkv : 0;
-    auto cur_nvalid = [&]() -> int {
-      const int64_t left = a.nkv - (int64_t)lu * BN;
+    auto cur_init = [&](TileCursor& c) {
+      c.s = 0;
+      while (step_tiles(c.s) == 0) ++c.s;
+      c.u = 0;
+      c.nt = step_tiles(c.s);
+      c.kv = step_kv_off(c.s);
+    };
+    auto cur_next = [&](TileCursor& c) {
+      if (++c.u < c.nt) return;
+      c.u = 0;
+      do {
+        ++c.s;
+      } while (c.s < nsteps && (c.nt = step_tiles(c.s)) == 0);
+      if (c.s < nsteps) c.kv = step_kv_off(c.s);
+    };
+    auto cur_pos = [&](const TileCursor& c) -> int64_t { return c.kv + (int64_t)c.u * BN; };
+    auto cur_valid = [&](const TileCursor& c) -> int {
+      const int64_t left = a.nkv - (int64_t)c.u * BN;
       return left < BN ? (int)left : BN;
     };
-    auto cur_row = [&]() -> int64_t { return lrow + (int64_t)lu * BN; };
-    auto cur_pos = [&]() -> int64_t { return lkv + (int64_t)lu * BN; };
-    auto step_cursor = [&]() {
-      if (++lu < lnt) return;
-      lu = 0;
-      do {
-        ++ls;
-      } while (ls < nsteps && (lnt = step_tiles(ls)) == 0);
-      if (ls < nsteps) {
-        lkv = step_kv_off(ls);
-        lrow = a.ring ? lkv : 0;
+    const int64_t roff = a.ring ? 0 : a.kv_off;  // key position - row in k/v
+    TileCursor klc, vlc, cc;  // K load cursor, V load cursor, compute cursor (tile t)
+    cur_init(klc);
+    cur_init(vlc);
+    cur_init(cc);
+    // Next tile to load for K and for V (position, valid rows).  Past the
+    // last tile the last one is loaded again: a harmless copy into a stage
+    // that nobody reads, which keeps the loads unconditional.
+    int64_t kl_pos = 0, vl_pos = 0;
+    int kl_nv = 0, vl_nv = 0, kl_rem = n, vl_rem = n;
+    auto adv = [&](TileCursor& c, int64_t& pos, int& nv, int& rem) __attribute__((always_inline)) {
+      if (rem > 0) {
+        pos = cur_pos(c);
+        nv = cur_valid(c);
+        cur_next(c);
+        --rem;
       }
     };
-    // row / valid count of the tile whose V is issued next; (position, valid
-    // count) of tiles c_j with j even (hpos0, hval0) and odd (hpos1, hval1)
-    int64_t vrow = cur_row(), hpos0 = cur_pos(), hpos1 = 0, npos = 0;
-    int vval = cur_nvalid(), hval0 = vval, hval1 = 0;
-    issue(vrow, vval, grp ? 0 : 2);  // K(c_0) by waves 4-7, V(c_0) by waves 0-3
-    step_cursor();
+    auto load_k = [&](int t) __attribute__((always_inline)) {
+      issue(kbase, a.k_ss, koffg, kl_pos - roff, kl_nv, t % 3);
+    };
+    auto load_v = [&](int t) __attribute__((always_inline)) {
+      issue(vbase, a.v_ss, voffg, vl_pos - roff, vl_nv, 3 + (t & 3));
+    };
+
+    f32x16 sacc[2];           // S^T of units with even / odd index
+    bf16x8 pf[2][2];          // P^T of units with even / odd index, per 16-key group
+    bf16x8 kf[KC];            // K fragments of the next S^T
+    u32x2 vlo[2][DB], vhi[2][DB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      sacc[i] = f32x16{};
+      pf[i][0] = pf[i][1] = bf16x8{};
+    }
+
+    // ---- LDS reads: inline asm with explicit waits that carry the registers
+    // they guarantee (the compiler's waits would order them behind the
+    // in-flight direct loads: it cannot prove they do not alias).  LDS reads
+    // complete in order; scalar loads only make a wait stricter.
+    auto kread = [&kf, &kaddr](int t, int hf) __attribute__((always_inline)) {
+      const unsigned kb = (unsigned)(t % 3) * TILE_BYTES + (unsigned)hf * 64 * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const unsigned ad = kaddr[c] + kb;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(kf[c]) : "v"(ad));
+      }
+    };
+    // wait until at most N LDS reads are in flight; the K fragments are older
+    auto kwait0 = [&kf]() __attribute__((always_inline)) {
+      if constexpr (KC == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]), "+v"(kf[4]),
+                     "+v"(kf[5]), "+v"(kf[6]), "+v"(kf[7]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]));
+    };
+    // V^T fragments, 16-key group HH of half hf of tile t.
+    auto vread = [&vlo, &vhi, &voff](auto HH, int t, int hf) __attribute__((always_inline)) {
+      constexpr int hh = decltype(HH)::value;
+      const unsigned vst = (unsigned)(t & 3) * TILE_BYTES + (unsigned)hf * 64 * D + (unsigned)hh * 32 * D;
+#pragma unroll
+      for (int x = 0; x < DB; ++x) {
+        const unsigned a0 = voff[0][x] + vst, a1 = voff[1][x] + vst;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vlo[hh][x]) : "v"(a0));
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vhi[hh][x]) : "v"(a1));
+      }
+    };
+    // group 0 done (group 1 and the next K reads may be in flight), group 1
+    // done (the next K reads may be in flight)
+    auto vwait0 = [&vlo, &vhi]() __attribute__((always_inline)) {
+      if constexpr (D == 128)
+        asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(vlo[0][0]), "+v"(vhi[0][0]), "+v"(vlo[0][1]), "+v"(vhi[0][1]),
+                     "+v"(vlo[0][2]), "+v"(vhi[0][2]), "+v"(vlo[0][3]), "+v"(vhi[0][3]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(vlo[0][0]), "+v"(vhi[0][0]), "+v"(vlo[0][1]), "+v"(vhi[0][1]));
+    };
+    auto vwait1 = [&vlo, &vhi](auto KN) __attribute__((always_inline)) {
+      constexpr int pend = decltype(KN)::value ? KC : 0;  // K reads issued after group 1
+      if constexpr (D == 128)
+        asm volatile("s_waitcnt lgkmcnt(%8)" : "+v"(vlo[1][0]), "+v"(vhi[1][0]), "+v"(vlo[1][1]), "+v"(vhi[1][1]),
+                     "+v"(vlo[1][2]), "+v"(vhi[1][2]), "+v"(vlo[1][3]), "+v"(vhi[1][3]) : "n"(pend));
+      else
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(vlo[1][0]), "+v"(vhi[1][0]), "+v"(vlo[1][1]), "+v"(vhi[1][1])
+                     : "n"(pend));
+    };
+
+    // Softmax of the unit whose S^T is in sacc[x], at key position k0 with
+    // nvalid valid keys.  Mask (a rare branch before the step's region): keys
+    // kvi < lim of the unit are visible to this lane's query: lim = valid keys,
+    // cut at the query's own position under causal masking, 0 for SKIP (no
+    // visible key for these rows: p = 0).  The key index of register r is
+    // 8 (r / 4) + (r % 4) + 4 lg.
+    const int64_t q0w = a.q_off + qrow_w;
+    const int nqw = min(32, a.nq - qrow_w);
+    auto sm_mask = [&](int x, int64_t k0, int nvalid) __attribute__((always_inline)) {
+      // every key valid and, under causal masking, at or before the wave's
+      // first query: nothing to mask (rows past nq are never stored)
+      const bool plain = nvalid == 32 && (!a.causal || k0 + 31 <= q0w);
+      if (__builtin_expect(!plain, 0)) {
+        const int cls = ra_plan_class(q0w, nqw, k0, nvalid, a.causal);
+        int64_t lim64 = cls == RA_CLASS_SKIP ? 0 : nvalid;
+        if (a.causal) {
+          const int64_t vis = q0w + lr - k0 + 1;
+          lim64 = vis < lim64 ? (vis > 0 ? vis : 0) : lim64;
+        }
+        const int lim = (int)lim64 - 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[x][r] = (8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : sacc[x][r];
+      }
+    };
+    // The softmax in eight steps, one per slot of a pipeline step: partial
+    // maxima, row max and lazy max update, four groups of four exponentials
+    // (fp32 row sum, bf16 P), and the row-sum update.  Tree reductions keep
+    // the dependent chains short.  Each step pins its results with an empty
+    // asm statement (the compiler would otherwise sink the arithmetic towards
+    // its consumers, out of the region it is meant to overlap with).
+    float sm_m[4], sm_ps[4], sm_alpha = 1.f, sm_muse = 0.f;
+    auto sm_step = [&](auto X, auto ST) __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value, st = decltype(ST)::value;
+      const f32x16& s = sacc[x];
+      if constexpr (st == 0) {
+        sm_m[0] = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        sm_m[1] = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
+        asm volatile("" : "+v"(sm_m[0]), "+v"(sm_m[1]));
+      } else if constexpr (st == 1) {
+        sm_m[2] = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
+        sm_m[3] = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
+        sm_m[0] = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+        asm volatile("" : "+v"(sm_m[0]));
+      } else if constexpr (st == 2) {
+        float mx = sm_m[0];
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float tm = mx * a.c;
+        const bool bump = tm > m2 + kLazyTau;  // move the max only when it grows by more than kLazyTau
+        sm_alpha = bump ? fast_exp2(m2 - tm) : 1.f;  // 0 when m2 was -inf
+        m2 = bump ? tm : m2;
+        sm_muse = m2 == -INFINITY ? 0.f : m2;  // no visible key yet: p = 0
+        asm volatile("" : "+v"(sm_alpha), "+v"(sm_muse), "+v"(m2));
+      } else if constexpr (st < 7) {
+        // The row sum takes the fp32 p (only the MFMA operand is rounded to
+        // bf16): rows with few visible keys would otherwise carry the 2^-9
+        // rounding of one term into l and the LSE.
+        constexpr int g = st - 3, hh = g >> 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(fmaf(s[4 * g + i], a.c, -sm_muse));
+          sm_ps[i] = g == 0 ? p : sm_ps[i] + p;
+          pf[x][hh][4 * (g & 1) + i] = (__bf16)p;
+        }
+        asm volatile("" : "+v"(sm_ps[0]), "+v"(sm_ps[1]), "+v"(sm_ps[2]), "+v"(sm_ps[3]), "+v"(pf[x][hh]));
+      } else {
+        lsum = lsum * sm_alpha + ((sm_ps[0] + sm_ps[1]) + (sm_ps[2] + sm_ps[3]));
+        asm volatile("" : "+v"(lsum));
+      }
+    };
+    // O *= alpha after a max update (rare: the max moves by more than
+    // kLazyTau only a few times per row).
+    auto sm_rescale = [&]() __attribute__((always_inline)) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(sm_alpha != 1.f) != 0, 0)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= sm_alpha;
+      }
+    };
+
+    // MFMA m of a step: m < KC: step c = m of S^T(u+1) into sacc[XN]; else
+    // O^T += V^T P^T(u-1) for 16-key group hh and channel block db, P from
+    // pf[XP].  (Their results are not pinned: an instruction that reads an
+    // MFMA result waits for the MFMA to finish.)
+    auto mma = [&](auto XN, auto XP, auto M) __attribute__((always_inline)) {
+      constexpr int xn = decltype(XN)::value, xp = decltype(XP)::value, m = decltype(M)::value;
+      if constexpr (m < KC) {
+        if constexpr (m == 0)
+          sacc[xn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
+        else
+          sacc[xn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m], qf[m], sacc[xn], 0, 0, 0);
+      } else {
+        constexpr int hh = (m - KC) / DB, db = (m - KC) % DB;
+        const u32x4 w = {vlo[hh][db][0], vlo[hh][db][1], vhi[hh][db][0], vhi[hh][db][1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[xp][hh], o[db], 0, 0, 0);
+      }
+    };
+    constexpr int MPS = (KC + 2 * DB) / 8;  // MFMAs per slot
+    static_assert(MPS * 8 == KC + 2 * DB, "eight slots per step");
+    const std::integral_constant<int, 0> X0;
+    const std::integral_constant<int, 1> X1;
+    const std::integral_constant<int, 0> H0;
+    const std::integral_constant<int, 1> H1;
+    // Pipeline step for unit u (S^T(u) in sacc[X], P(u-1) in pf[1-X]): SN: the
+    // next unit exists (its K fragments are in kf: S^T(u+1) into sacc[1-X]);
+    // PV: the previous unit exists (V^T of tile pt half ph); SM: unit u exists
+    // (softmax); KN: read the K fragments of unit u+2 (tile kt, half kh) in the
+    // second half.  Eight slots of one softmax step and MPS MFMAs each, kept
+    // in order by scheduling barriers: S^T(u+1) in slots 0-3 (its K fragments
+    // arrived during the previous step), O^T in slots 4-7 (the V^T reads
+    // issued in slots 0 and 1 land meanwhile).
+    auto step = [&](auto X, auto SN, auto PV, auto SM, auto KN, int pt, int ph, int kt, int kh, int lt)
+        __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value;
+      constexpr bool sn = decltype(SN)::value, pv = decltype(PV)::value, sm = decltype(SM)::value;
+      constexpr bool kn = decltype(KN)::value;
+      static_for<0, 8>([&](auto SL) {
+        constexpr int sl = decltype(SL)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (sl == 0) {
+          if constexpr (sn) kwait0();
+          if constexpr (pv) vread(H0, pt, ph);
+        }
+        if constexpr (sl == 1 && pv) vread(H1, pt, ph);
+        if constexpr (sl == 4) {
+          if constexpr (pv) vwait0();
+          if constexpr (kn) kread(kt, kh);
+        }
+        if constexpr (sl == 6 && pv) vwait1(KN);  // the K reads for the next step (if any) are younger
+        // this iteration's tile loads (lt < 0: none): K in the first step, V in the second
+        if constexpr (sl == 2) {
+          if (lt >= 0) {
+            if constexpr (x == 0) load_k(lt);
+            else load_v(lt);
+          }
+        }
+        if constexpr (sm) sm_step(X, SL);
+        static_for<sl * MPS, (sl + 1) * MPS>([&](auto M) {
+          constexpr int m = decltype(M)::value;
+          if constexpr (m < KC) {
+            if constexpr (sn) mma(std::integral_constant<int, 1 - x>{}, std::integral_constant<int, 1 - x>{}, M);
+          } else if constexpr (pv) {
+            mma(std::integral_constant<int, 1 - x>{}, std::integral_constant<int, 1 - x>{}, M);
+          }
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (sm) sm_rescale();
+    };
+    auto half_valid = [](int nv, int hf) { const int x = nv - 32 * hf; return x < 0 ? 0 : (x > 32 ? 32 : x); };
+    const std::true_type T;
+    const std::false_type F;
+
+    // Prologue: K(c_0..2), V(c_0..1); S^T of unit 0; K fragments of unit 1.
+    for (int t = 0; t < 3; ++t) {
+      adv(klc, kl_pos, kl_nv, kl_rem);
+      load_k(t);
+    }
+    for (int t = 0; t < 2; ++t) {
+      adv(vlc, vl_pos, vl_nv, vl_rem);
+      load_v(t);
+    }
+    adv(klc, kl_pos, kl_nv, kl_rem);  // K(c_3), V(c_2): loaded in iteration 0
+    adv(vlc, vl_pos, vl_nv, vl_rem);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    kread(0, 0);
+    kwait0();
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], c == 0 ? f32x16{} : sacc[0], 0, 0, 0);
+    kread(0, 1);  // unit 1 (waited for at the first step)
 
-    f32x16 sacc[2];
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      sacc[bb] = f32x16{};
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) pf[bb][hh] = bf16x8{};
-    }
-
-    for (int phi = 0; phi <= 2 * n + 1; ++phi) {
-      // Loads.  Phase 2k: waves 4-7 issue K(c_{k+1}) (into the K stage read in
-      // phases 2k-2, 2k-1).  Phase 2k+1: waves 0-3 issue V(c_{k+1}) (into V
-      // stage (k+1) % 3, read in phases 2k-2, 2k-1).  (vrow, vval) describe
-      // c_{k+1} from phase 2k on.
-      bool v_issued = false;
-      if (!(phi & 1) && (phi >> 1) + 1 < n) {
-        const int k = phi >> 1;
-        vrow = cur_row();
-        vval = cur_nvalid();
-        npos = cur_pos();
-        if (grp == 1) issue(vrow, vval, (k + 1) & 1);
-        step_cursor();
+    // Iteration head: the barrier that publishes K(c_{t+1}) and V(c_t): all
+    // loads but those of the previous iteration (K(c_{t+2}), V(c_{t+1})) are
+    // complete.
+    auto head = [&](int t) __attribute__((always_inline)) {
+      if (t > 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NL) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if ((phi & 1) && (phi >> 1) + 1 < n && grp == 0) {
-        issue(vrow, vval, 2 + ((phi >> 1) + 1) % 3);
-        v_issued = true;
-      }
-      const int my = phi - grp;
-      if (my >= 0) {
-        const int j = my >> 1;
-        if (!(my & 1)) {
-          // ---- MFMA phase j ----
-          if (j < n) {
-            // all K fragments of the tile first, then the MFMAs, so the LDS
-            // latency is paid once per tile rather than once per MFMA
-            const char* Ks = smem[j & 1];
-            bf16x8 kf[2][D / 16];
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-              for (int c = 0; c < D / 16; ++c) kf[bb][c] = *(const bf16x8*)(Ks + koff[c] + 64 * D * bb);
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-              sacc[bb] = f32x16{};
-#pragma unroll
-              for (int c = 0; c < D / 16; ++c)
-                sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bb][c], qf[c], sacc[bb], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // the LDS reads first
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 16), 0);  // then the MFMAs
-          }
-          if (j >= 1) {
-            // O^T += V^T P^T of tile j-1.  The transposing reads are inline
-            // asm so the compiler does not order them behind the in-flight
-            // direct loads (it cannot prove they do not alias); the wait that
-            // follows carries their registers, so the MFMAs stay behind it.
-            const unsigned vst = (unsigned)((j - 1) % 3) * TILE_BYTES;
-            u32x2 lo[2][D / 32], hi[2][D / 32];
-#define RA_TR_READ(BUF, G, DB)                                                                   \
-  if constexpr (DB < D / 32) {                                                                   \
-    constexpr int off = (32 * ((G) >> 1) + 16 * ((G) & 1)) * 2 * D;                             \
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo[BUF][DB]) : "v"(voff[0][DB] + vst), "i"(off)); \
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi[BUF][DB]) : "v"(voff[1][DB] + vst), "i"(off)); \
-  }
-#define RA_TR_GROUP(BUF, G) RA_TR_READ(BUF, G, 0) RA_TR_READ(BUF, G, 1) RA_TR_READ(BUF, G, 2) RA_TR_READ(BUF, G, 3)
-#define RA_TR_WAIT(BUF, N)                                                                       \
-  if constexpr (D == 128)                                                                        \
-    asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(lo[BUF][0]), "+v"(hi[BUF][0]), "+v"(lo[BUF][1]), \
-                 "+v"(hi[BUF][1]), "+v"(lo[BUF][2]), "+v"(hi[BUF][2]), "+v"(lo[BUF][3]), "+v"(hi[BUF][3])); \
-  else                                                                                           \
-    asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(lo[BUF][0]), "+v"(hi[BUF][0]), "+v"(lo[BUF][1]), \
-                 "+v"(hi[BUF][1]));
-#define RA_PV(BUF, G)                                                                            \
-  _Pragma("unroll") for (int db = 0; db < D / 32; ++db) {                                        \
-    const u32x4 w = {lo[BUF][db][0], lo[BUF][db][1], hi[BUF][db][0], hi[BUF][db][1]};            \
-    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),               \
-                                                    pf[(G) >> 1][(G) & 1], o[db], 0, 0, 0);      \
-  }
-            // O^T += V^T P^T of tile j-1, four (key block, half) groups; the
-            // reads of group g+1 are in flight while group g's MFMAs issue.
-            // The transposing reads are inline asm so the compiler does not
-            // order them behind the in-flight direct loads (it cannot prove
-            // they do not alias); each wait carries the registers it
-            // guarantees, so the MFMAs stay behind it.  lgkmcnt counts only
-            // these reads here (LDS completes in order; scalar loads only add).
-            if constexpr (D == 128) {
-              RA_TR_GROUP(0, 0)
-              RA_TR_GROUP(1, 1)
-              RA_TR_WAIT(0, 8)
-              RA_PV(0, 0)
-              RA_TR_GROUP(0, 2)
-              RA_TR_WAIT(1, 8)
-              RA_PV(1, 1)
-              RA_TR_GROUP(1, 3)
-              RA_TR_WAIT(0, 8)
-              RA_PV(0, 2)
-              RA_TR_WAIT(1, 0)
-              RA_PV(1, 3)
-            } else {
-              RA_TR_GROUP(0, 0)
-              RA_TR_GROUP(1, 1)
-              RA_TR_WAIT(0, 4)
-              RA_PV(0, 0)
-              RA_TR_GROUP(0, 2)
-              RA_TR_WAIT(1, 4)
-              RA_PV(1, 1)
-              RA_TR_GROUP(1, 3)
-              RA_TR_WAIT(0, 4)
-              RA_PV(0, 2)
-              RA_TR_WAIT(1, 0)
-              RA_PV(1, 3)
-            }
-#undef RA_PV
-#undef RA_TR_WAIT
-#undef RA_TR_GROUP
-#undef RA_TR_READ
-          }
-        } else if (j < n) {
-          // ---- VALU phase j: softmax of tile c_j ----
-          const int64_t k0 = (j & 1) ? hpos1 : hpos0;
-          const int nvalid = (j & 1) ? hval1 : hval0;
-          const int64_t q0w = a.q_off + qrow_w;
-          const int nqw = min(32, a.nq - qrow_w);
-          const int cls = ra_plan_class(q0w, nqw, k0, nvalid, a.causal);
-          if (cls != RA_CLASS_FULL || nvalid < BN) {
-            // Keys kvi < lim of this tile are visible to this lane's query:
-            // lim = valid keys, cut at the query's own position under causal
-            // masking, 0 for SKIP (no visible key for these rows: p = 0).  The
-            // key index of register r is 32 bb + 8 (r / 4) + (r % 4) + 4 lg.
-            int64_t lim64 = cls == RA_CLASS_SKIP ? 0 : nvalid;
-            if (a.causal) {
-              const int64_t vis = q0w + lr - k0 + 1;
-              lim64 = vis < lim64 ? (vis > 0 ? vis : 0) : lim64;
-            }
-            const int lim = (int)lim64 - 4 * lg;
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                sacc[bb][r] = (32 * bb + 8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : sacc[bb][r];
-          }
-          float mx = -INFINITY;
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[bb][r]);
-          {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-          }
-          const float t = mx * a.c;
-          const bool bump = t > m2 + kLazyTau;  // move the max only when it grows by more than kLazyTau
-          if (__builtin_amdgcn_ballot_w64(bump)) {
-            const float alpha = bump ? fast_exp2(m2 - t) : 1.f;  // 0 when m2 was -inf
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-            m2 = bump ? t : m2;
-          }
-          const float m_use = m2 == -INFINITY ? 0.f : m2;  // no visible key yet: p = 0
-          // The row sum takes the fp32 p (only the MFMA operand is rounded to
-          // bf16): rows with few visible keys would otherwise carry the 2^-9
-          // rounding of one term into l and the LSE.
-          float psum = 0.f;
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-              for (int t8 = 0; t8 < 8; ++t8) {
-                const float p = fast_exp2(fmaf(sacc[bb][8 * hh + t8], a.c, -m_use));
-                psum += p;
-                pf[bb][hh][t8] = (__bf16)p;
-              }
-          lsum += psum;
-        }
-      }
-      // c_{k+1}'s position and valid count go into its history slot only now:
-      // waves 4-7 read c_{k-1}'s (same slot) earlier in this phase.
-      if (!(phi & 1) && (phi >> 1) + 1 < n) {
-        if (((phi >> 1) + 1) & 1) {
-          hpos1 = npos;
-          hval1 = vval;
-        } else {
-          hpos0 = npos;
-          hval0 = vval;
-        }
-      }
-      // Phase barrier.  Only the odd ones publish LDS data (the direct loads
-      // issued two phases earlier), so only they wait for vmcnt; the even
-      // ones just order this phase's LDS reads before the next loads.  Inline
-      // asm with a memory clobber keeps the compiler from moving LDS accesses
-      // across it (and from adding its own full waits).
-      // Odd barriers publish the loads issued two phases earlier: K(c_{k+1})
-      // of waves 4-7 (phase 2k) and V(c_k) of waves 0-3 (phase 2k-1); a V
-      // group issued in this phase may stay in flight.
-      if (phi < 2 * n + 1) {
-        if (!(phi & 1))
-          asm volatile("s_barrier" ::: "memory");
-        else if (v_issued)
-          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NI) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // Every iteration runs the same two steps (a second variant of a step in
+    // the loop costs registers everywhere): at t = 0 the P V of the
+    // nonexistent unit -1 adds P = 0 times the finite V of c_0; in the last
+    // iteration S^T of the nonexistent unit 2n and the K reads past the end
+    // fill registers that are never used (stale but in-bounds LDS).  Unit 2t
+    // has its S^T in sacc[0], unit 2t+1 in sacc[1].
+    int64_t pt = cur_pos(cc);  // tile t: key position, valid rows, any masking
+    int vt = cur_valid(cc);
+    auto needs_mask = [&](int64_t p, int v) { return v < BN || (a.causal && p + BN - 1 > q0w); };
+    bool mt = needs_mask(pt, vt);
+    for (int t = 0; t < n; ++t) {
+      head(t);
+      // The two waves of a SIMD (w, w + 4) run the same steps; issue goes to
+      // the older wave first, which would finish the iteration long before
+      // the other and then wait at the barrier.  Each wave takes the higher
+      // priority for one of the two steps instead.
+      if (grp) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(1);
+      if (__builtin_expect(mt, 0)) sm_mask(0, pt, half_valid(vt, 0));
+      step(X0, T, T, T, T, t > 0 ? t - 1 : 0, t > 0 ? 1 : 0, t + 1, 0, t + 3);
+      if (grp) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+      if (__builtin_expect(mt, 0)) sm_mask(1, pt + 32, half_valid(vt, 1));
+      step(X1, T, T, T, T, t, 0, t + 1, 1, t + 2);
+      // tail: descriptors of the next iteration
+      adv(klc, kl_pos, kl_nv, kl_rem);
+      adv(vlc, vl_pos, vl_nv, vl_rem);
+      if (t + 1 < n) {
+        cur_next(cc);
+        pt = cur_pos(cc);
+        vt = cur_valid(cc);
+        mt = needs_mask(pt, vt);
       }
     }
+    // drain: O^T += V^T P^T of the last unit (half 1 of the last tile, P in pf[1])
+    step(X0, F, T, F, F, n - 1, 1, 0, 0, -1);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Epilogue: the two halves of each row sum live in lanes lr and lr + 32.
@@ -510,7 +610,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   if (a.out_state) {
     float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 x = {o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
@@ -526,7 +626,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     if (a.o_bf16) {
       __bf16* op = (__bf16*)a.o + base;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           bf16x4 x = {(__bf16)(o[db][4 * j] * inv), (__bf16)(o[db][4 * j + 1] * inv),
@@ -536,7 +636,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     } else {
       float* op = (float*)a.o + base;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           f32x4 x = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,

@@ -54,6 +54,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max of three without the NaN canonicalisation fmaxf brings along (the
+// inputs are MFMA results or -inf, never signalling NaNs)
+__device__ __forceinline__ float vmax3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
 
 // Workgroups are handed to the 8 XCDs round-robin.  Give XCD x the contiguous
 // logical range [x * n/8, (x+1) * n/8) so that all query tiles of a head (and
@@ -108,8 +115,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   constexpr int DB = D / 32;                   // 32-channel blocks of O^T
   static_assert(NL * 1024 * NW == TILE_BYTES, "tile split");
   static_assert(BM == RA_BF16_BM && BN == 64, "64-key tiles, processed as two 32-key units");
-  // [0], [1], [2]: K stages; [3] .. [6]: V stages
-  __shared__ __attribute__((aligned(1024))) char smem[7][TILE_BYTES];
+  // [0] .. [3]: K stages; [4] .. [7]: V stages (tile c_t in K and V stage t % 4)
+  __shared__ __attribute__((aligned(1024))) char smem[8][TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep per-wave values in SGPRs
@@ -204,13 +211,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     koffg[i] = (unsigned)r * (unsigned)a.k_ss * 2u + sl;
     voffg[i] = (unsigned)r * (unsigned)a.v_ss * 2u + sl;
   }
-  // Tile at row row0 of base (k or v, row stride `stride`) with nvalid valid
-  // rows into LDS stage `stage`.
-  auto issue = [&](const char* base, int64_t stride, const unsigned* goff, int64_t row0, int nvalid, int stage)
+  // Tile at address tb (row stride `stride` elements) with nvalid valid rows
+  // into LDS stage `stage`.
+  auto issue = [&](const char* tb, int64_t stride, const unsigned* goff, int nvalid, auto STAGE)
       __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + row0 * stride * 2), (short)0, (int)(unsigned)(BN * stride * 2), 0x00020000);
-    char* dst = &smem[stage][0] + wv * NL * 1024;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, (int)(unsigned)(BN * stride * 2), 0x00020000);
+    char* dst = &smem[decltype(STAGE)::value][0] + wv * NL * 1024;
     if (nvalid == BN) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
@@ -249,7 +256,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int r = 4 * lg + ve + 8 * half;
-      voff[half][db] = smem_lds + 3 * TILE_BYTES + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
+      voff[half][db] = smem_lds + 4 * TILE_BYTES + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
     }
 
   // ---- schedule ----------------------------------------------------------
@@ -266,54 +273,70 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // second half of step u-1, the V^T fragments of unit u-1 in the first half
   // of step u.  One barrier per tile: iteration t (units 2t, 2t+1) starts by
   // publishing K(c_{t+1}) and V(c_t) (loaded two iterations earlier) and then
-  // issues the loads of K(c_{t+3}) and V(c_{t+2}) (three K and four V stages).
+  // issues the loads of K(c_{t+3}) and V(c_{t+2}).  Tile c_t sits in K and V
+  // stage t % 4; the loop body covers four iterations, so every LDS offset
+  // of a read is an immediate on a per-lane base fixed for the kernel.
   int n = 0;
   for (int s = 0; s < nsteps; ++s) n += step_tiles(s);
 
   if (n > 0) {  // workgroup-uniform
-    auto cur_init = [&](TileCursor& c) {
-      c.s = 0;
-      while (step_tiles(c.s) == 0) ++c.s;
-      c.u = 0;
-      c.nt = step_tiles(c.s);
-      c.kv = step_kv_off(c.s);
-    };
-    auto cur_next = [&](TileCursor& c) {
-      if (++c.u < c.nt) return;
-      c.u = 0;
-      do {
-        ++c.s;
-      } while (c.s < nsteps && (c.nt = step_tiles(c.s)) == 0);
-      if (c.s < nsteps) c.kv = step_kv_off(c.s);
-    };
-    auto cur_pos = [&](const TileCursor& c) -> int64_t { return c.kv + (int64_t)c.u * BN; };
-    auto cur_valid = [&](const TileCursor& c) -> int {
-      const int64_t left = a.nkv - (int64_t)c.u * BN;
-      return left < BN ? (int)left : BN;
-    };
     const int64_t roff = a.ring ? 0 : a.kv_off;  // key position - row in k/v
-    TileCursor klc, vlc, cc;  // K load cursor, V load cursor, compute cursor (tile t)
-    cur_init(klc);
-    cur_init(vlc);
-    cur_init(cc);
-    // Next tile to load for K and for V (position, valid rows).  Past the
-    // last tile the last one is loaded again: a harmless copy into a stage
-    // that nobody reads, which keeps the loads unconditional.
-    int64_t kl_pos = 0, vl_pos = 0;
-    int kl_nv = 0, vl_nv = 0, kl_rem = n, vl_rem = n;
-    auto adv = [&](TileCursor& c, int64_t& pos, int& nv, int& rem) __attribute__((always_inline)) {
+    const int64_t kstep = (int64_t)BN * a.k_ss * 2, vstep = (int64_t)BN * a.v_ss * 2;
+    // Cursor over the tiles: loop step cs, tile cu of its cnt tiles, the
+    // tile's key position, keys left in the block from it on, K and V
+    // addresses of its first row.
+    int cs = 0, cu = 0, cnt = 0;
+    int64_t cp = 0, cleft = 0;
+    const char* cka = kbase;
+    const char* cva = vbase;
+    auto cur_set = [&]() {
+      cu = 0;
+      cnt = step_tiles(cs);
+      cp = step_kv_off(cs);
+      cleft = a.nkv;
+      cka = kbase + (cp - roff) * a.k_ss * 2;
+      cva = vbase + (cp - roff) * a.v_ss * 2;
+    };
+    while (step_tiles(cs) == 0) ++cs;
+    cur_set();
+    // Descriptors of tiles t .. t+3 (key position, valid rows, K and V
+    // addresses) in slots t % 4 .. (t + 3) % 4.  Past the last tile a slot
+    // keeps the descriptor it held (an earlier tile): the loads made with it
+    // land in stages nobody reads, which keeps the loads unconditional.
+    int rem = n;
+    int64_t dp[4];
+    int dv[4];
+    const char* dka[4];
+    const char* dva[4];
+    auto fill = [&](auto SLOT) __attribute__((always_inline)) {
+      constexpr int j = decltype(SLOT)::value;
       if (rem > 0) {
-        pos = cur_pos(c);
-        nv = cur_valid(c);
-        cur_next(c);
-        --rem;
+        dp[j] = cp;
+        dv[j] = cleft < BN ? (int)cleft : BN;
+        dka[j] = cka;
+        dva[j] = cva;
+        if (--rem > 0) {
+          if (++cu < cnt) {
+            cp += BN;
+            cleft -= BN;
+            cka += kstep;
+            cva += vstep;
+          } else {
+            do {
+              ++cs;
+            } while (cs < nsteps && step_tiles(cs) == 0);
+            if (cs < nsteps) cur_set();
+          }
+        }
       }
     };
-    auto load_k = [&](int t) __attribute__((always_inline)) {
-      issue(kbase, a.k_ss, koffg, kl_pos - roff, kl_nv, t % 3);
+    auto load_k = [&](auto ST) __attribute__((always_inline)) {
+      constexpr int j = decltype(ST)::value;
+      issue(dka[j], a.k_ss, koffg, dv[j], ST);
     };
-    auto load_v = [&](int t) __attribute__((always_inline)) {
-      issue(vbase, a.v_ss, voffg, vl_pos - roff, vl_nv, 3 + (t & 3));
+    auto load_v = [&](auto ST) __attribute__((always_inline)) {
+      constexpr int j = decltype(ST)::value;
+      issue(dva[j], a.v_ss, voffg, dv[j], std::integral_constant<int, 4 + j>{});
     };
 
     f32x16 sacc[2];           // S^T of units with even / odd index
@@ -329,14 +352,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // ---- LDS reads: inline asm with explicit waits that carry the registers
     // they guarantee (the compiler's waits would order them behind the
     // in-flight direct loads: it cannot prove they do not alias).  LDS reads
-    // complete in order; scalar loads only make a wait stricter.
-    auto kread = [&kf, &kaddr](int t, int hf) __attribute__((always_inline)) {
-      const unsigned kb = (unsigned)(t % 3) * TILE_BYTES + (unsigned)hf * 64 * D;
+    // complete in order; scalar loads only make a wait stricter.  KO / VO:
+    // byte offset of the unit in the K / V region (stage * tile + half * 64D),
+    // an immediate; rt: a run-time offset added to the bases (0 in the loop).
+    auto kread = [&kf, &kaddr](auto KO) __attribute__((always_inline)) {
+      constexpr unsigned ko = decltype(KO)::value;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const unsigned ad = kaddr[c] + kb;
-        asm volatile("ds_read_b128 %0, %1" : "=v"(kf[c]) : "v"(ad));
-      }
+      for (int c = 0; c < KC; ++c) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[c]) : "v"(kaddr[c]), "i"(ko));
     };
     // wait until at most N LDS reads are in flight; the K fragments are older
     auto kwait0 = [&kf]() __attribute__((always_inline)) {
@@ -346,15 +368,15 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]));
     };
-    // V^T fragments, 16-key group HH of half hf of tile t.
-    auto vread = [&vlo, &vhi, &voff](auto HH, int t, int hf) __attribute__((always_inline)) {
+    // V^T fragments, 16-key group HH of the unit at offset VO (+ rt).
+    auto vread = [&vlo, &vhi, &voff](auto HH, auto VO, unsigned rt) __attribute__((always_inline)) {
       constexpr int hh = decltype(HH)::value;
-      const unsigned vst = (unsigned)(t & 3) * TILE_BYTES + (unsigned)hf * 64 * D + (unsigned)hh * 32 * D;
+      constexpr unsigned vo = decltype(VO)::value + (unsigned)hh * 32 * D;
 #pragma unroll
       for (int x = 0; x < DB; ++x) {
-        const unsigned a0 = voff[0][x] + vst, a1 = voff[1][x] + vst;
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vlo[hh][x]) : "v"(a0));
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vhi[hh][x]) : "v"(a1));
+        const unsigned a0 = voff[0][x] + rt, a1 = voff[1][x] + rt;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vlo[hh][x]) : "v"(a0), "i"(vo));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vhi[hh][x]) : "v"(a1), "i"(vo));
       }
     };
     // group 0 done (group 1 and the next K reads may be in flight), group 1
@@ -412,18 +434,20 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       constexpr int x = decltype(X)::value, st = decltype(ST)::value;
       const f32x16& s = sacc[x];
       if constexpr (st == 0) {
-        sm_m[0] = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        sm_m[1] = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
+        sm_m[0] = vmax3(s[0], s[1], s[2]);
+        sm_m[1] = vmax3(s[3], s[4], s[5]);
+        sm_m[0] = vmax3(sm_m[0], s[6], s[7]);
         asm volatile("" : "+v"(sm_m[0]), "+v"(sm_m[1]));
       } else if constexpr (st == 1) {
-        sm_m[2] = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
-        sm_m[3] = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
-        sm_m[0] = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+        sm_m[2] = vmax3(s[8], s[9], s[10]);
+        sm_m[3] = vmax3(s[11], s[12], s[13]);
+        sm_m[2] = vmax3(sm_m[2], s[14], s[15]);
+        sm_m[0] = vmax3(sm_m[0], sm_m[1], sm_m[2]);
+        sm_m[0] = vmax3(sm_m[0], sm_m[3], sm_m[3]);
         asm volatile("" : "+v"(sm_m[0]));
       } else if constexpr (st == 2) {
-        float mx = sm_m[0];
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm_m[0]), __float_as_uint(sm_m[0]), false, false);
+        const float mx = vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
         const float tm = mx * a.c;
         const bool bump = tm > m2 + kLazyTau;  // move the max only when it grows by more than kLazyTau
         sm_alpha = bump ? fast_exp2(m2 - tm) : 1.f;  // 0 when m2 was -inf
@@ -483,13 +507,14 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     const std::integral_constant<int, 1> H1;
     // Pipeline step for unit u (S^T(u) in sacc[X], P(u-1) in pf[1-X]): SN: the
     // next unit exists (its K fragments are in kf: S^T(u+1) into sacc[1-X]);
-    // PV: the previous unit exists (V^T of tile pt half ph); SM: unit u exists
-    // (softmax); KN: read the K fragments of unit u+2 (tile kt, half kh) in the
-    // second half.  Eight slots of one softmax step and MPS MFMAs each, kept
-    // in order by scheduling barriers: S^T(u+1) in slots 0-3 (its K fragments
-    // arrived during the previous step), O^T in slots 4-7 (the V^T reads
-    // issued in slots 0 and 1 land meanwhile).
-    auto step = [&](auto X, auto SN, auto PV, auto SM, auto KN, int pt, int ph, int kt, int kh, int lt)
+    // PV: the previous unit exists (its V^T at offset VO + vrt); SM: unit u
+    // exists (softmax); KN: read the K fragments of unit u+2 (offset KO) in
+    // the second half; load(): this step's tile load, issued in slot 2.
+    // Eight slots of one softmax step and MPS MFMAs each, kept in order by
+    // scheduling barriers: S^T(u+1) in slots 0-3 (its K fragments arrived
+    // during the previous step), O^T in slots 4-7 (the V^T reads issued in
+    // slots 0 and 1 land meanwhile).
+    auto step = [&](auto X, auto SN, auto PV, auto SM, auto KN, auto VO, unsigned vrt, auto KO, auto load)
         __attribute__((always_inline)) {
       constexpr int x = decltype(X)::value;
       constexpr bool sn = decltype(SN)::value, pv = decltype(PV)::value, sm = decltype(SM)::value;
@@ -499,21 +524,15 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (sl == 0) {
           if constexpr (sn) kwait0();
-          if constexpr (pv) vread(H0, pt, ph);
+          if constexpr (pv) vread(H0, VO, vrt);
         }
-        if constexpr (sl == 1 && pv) vread(H1, pt, ph);
+        if constexpr (sl == 1 && pv) vread(H1, VO, vrt);
         if constexpr (sl == 4) {
           if constexpr (pv) vwait0();
-          if constexpr (kn) kread(kt, kh);
+          if constexpr (kn) kread(KO);
         }
         if constexpr (sl == 6 && pv) vwait1(KN);  // the K reads for the next step (if any) are younger
-        // this iteration's tile loads (lt < 0: none): K in the first step, V in the second
-        if constexpr (sl == 2) {
-          if (lt >= 0) {
-            if constexpr (x == 0) load_k(lt);
-            else load_v(lt);
-          }
-        }
+        if constexpr (sl == 2) load();
         if constexpr (sm) sm_step(X, SL);
         static_for<sl * MPS, (sl + 1) * MPS>([&](auto M) {
           constexpr int m = decltype(M)::value;
@@ -530,74 +549,102 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     auto half_valid = [](int nv, int hf) { const int x = nv - 32 * hf; return x < 0 ? 0 : (x > 32 ? 32 : x); };
     const std::true_type T;
     const std::false_type F;
+    // byte offset of half H of the tile in stage S (K and V regions alike)
+    auto uoff = [](auto S, auto H) {
+      return std::integral_constant<unsigned, (unsigned)decltype(S)::value * TILE_BYTES +
+                                                  (unsigned)decltype(H)::value * 64 * D>{};
+    };
+    using std::integral_constant;
 
-    // Prologue: K(c_0..2), V(c_0..1); S^T of unit 0; K fragments of unit 1.
-    for (int t = 0; t < 3; ++t) {
-      adv(klc, kl_pos, kl_nv, kl_rem);
-      load_k(t);
+    // Prologue: descriptors of c_0..3; K(c_0..2), V(c_0..1); V stage 3
+    // cleared (the first step's P V reads it with P = 0); S^T of unit 0; K
+    // fragments of unit 1.
+    fill(integral_constant<int, 0>{});
+#pragma unroll
+    for (int j = 1; j < 4; ++j) dp[j] = dp[0], dv[j] = dv[0], dka[j] = dka[0], dva[j] = dva[0];
+    fill(integral_constant<int, 1>{});
+    fill(integral_constant<int, 2>{});
+    fill(integral_constant<int, 3>{});
+    load_k(integral_constant<int, 0>{});
+    load_k(integral_constant<int, 1>{});
+    load_k(integral_constant<int, 2>{});
+    load_v(integral_constant<int, 0>{});
+    load_v(integral_constant<int, 1>{});
+    {
+      constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane
+#pragma unroll
+      for (int i = 0; i < per; ++i) *(u32x4*)(&smem[7][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
-    for (int t = 0; t < 2; ++t) {
-      adv(vlc, vl_pos, vl_nv, vl_rem);
-      load_v(t);
-    }
-    adv(klc, kl_pos, kl_nv, kl_rem);  // K(c_3), V(c_2): loaded in iteration 0
-    adv(vlc, vl_pos, vl_nv, vl_rem);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    kread(0, 0);
+    kread(uoff(integral_constant<int, 0>{}, H0));
     kwait0();
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], c == 0 ? f32x16{} : sacc[0], 0, 0, 0);
-    kread(0, 1);  // unit 1 (waited for at the first step)
+    kread(uoff(integral_constant<int, 0>{}, H1));  // unit 1 (waited for at the first step)
 
     // Iteration head: the barrier that publishes K(c_{t+1}) and V(c_t): all
     // loads but those of the previous iteration (K(c_{t+2}), V(c_{t+1})) are
     // complete.
-    auto head = [&](int t) __attribute__((always_inline)) {
-      if (t > 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NL) : "memory");
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    auto head = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NL) : "memory");
+      __builtin_amdgcn_sched_barrier(0);
     };
     // Every iteration runs the same two steps (a second variant of a step in
     // the loop costs registers everywhere): at t = 0 the P V of the
-    // nonexistent unit -1 adds P = 0 times the finite V of c_0; in the last
-    // iteration S^T of the nonexistent unit 2n and the K reads past the end
-    // fill registers that are never used (stale but in-bounds LDS).  Unit 2t
-    // has its S^T in sacc[0], unit 2t+1 in sacc[1].
-    int64_t pt = cur_pos(cc);  // tile t: key position, valid rows, any masking
-    int vt = cur_valid(cc);
+    // nonexistent unit -1 adds P = 0 times the zeros of V stage 3; in the
+    // last iteration S^T of the nonexistent unit 2n and the K reads past the
+    // end fill registers that are never used (stale but in-bounds LDS).  Unit
+    // 2t has its S^T in sacc[0], unit 2t+1 in sacc[1].
     auto needs_mask = [&](int64_t p, int v) { return v < BN || (a.causal && p + BN - 1 > q0w); };
-    bool mt = needs_mask(pt, vt);
-    for (int t = 0; t < n; ++t) {
-      head(t);
+    bool mt = needs_mask(dp[0], dv[0]);
+    auto iter = [&](auto J) __attribute__((always_inline)) {  // iteration t, J = t % 4
+      constexpr int j = decltype(J)::value;
+      const integral_constant<int, j> SJ;
+      const integral_constant<int, (j + 1) & 3> SJ1;
+      const integral_constant<int, (j + 2) & 3> SJ2;
+      const integral_constant<int, (j + 3) & 3> SJ3;
       // The two waves of a SIMD (w, w + 4) run the same steps; issue goes to
       // the older wave first, which would finish the iteration long before
       // the other and then wait at the barrier.  Each wave takes the higher
       // priority for one of the two steps instead.
       if (grp) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(1);
-      if (__builtin_expect(mt, 0)) sm_mask(0, pt, half_valid(vt, 0));
-      step(X0, T, T, T, T, t > 0 ? t - 1 : 0, t > 0 ? 1 : 0, t + 1, 0, t + 3);
+      if (__builtin_expect(mt, 0)) sm_mask(0, dp[j], half_valid(dv[j], 0));
+      // unit 2t: P V of unit 2t-1 (c_{t-1}, half 1), K of unit 2t+2 (c_{t+1}, half 0), load K(c_{t+3})
+      step(X0, T, T, T, T, uoff(SJ3, H1), 0u, uoff(SJ1, H0), [&]() __attribute__((always_inline)) { load_k(SJ3); });
       if (grp) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
-      if (__builtin_expect(mt, 0)) sm_mask(1, pt + 32, half_valid(vt, 1));
-      step(X1, T, T, T, T, t, 0, t + 1, 1, t + 2);
-      // tail: descriptors of the next iteration
-      adv(klc, kl_pos, kl_nv, kl_rem);
-      adv(vlc, vl_pos, vl_nv, vl_rem);
-      if (t + 1 < n) {
-        cur_next(cc);
-        pt = cur_pos(cc);
-        vt = cur_valid(cc);
-        mt = needs_mask(pt, vt);
-      }
+      if (__builtin_expect(mt, 0)) sm_mask(1, dp[j] + 32, half_valid(dv[j], 1));
+      // unit 2t+1: P V of unit 2t (c_t, half 0), K of unit 2t+3 (c_{t+1}, half 1), load V(c_{t+2})
+      step(X1, T, T, T, T, uoff(SJ, H0), 0u, uoff(SJ1, H1), [&]() __attribute__((always_inline)) { load_v(SJ2); });
+      fill(SJ);  // slot of c_t now holds c_{t+4}
+      mt = needs_mask(dp[(j + 1) & 3], dv[(j + 1) & 3]);
+    };
+    int t = 0;
+    for (;;) {
+      iter(integral_constant<int, 0>{});
+      if (++t == n) break;
+      head();
+      iter(integral_constant<int, 1>{});
+      if (++t == n) break;
+      head();
+      iter(integral_constant<int, 2>{});
+      if (++t == n) break;
+      head();
+      iter(integral_constant<int, 3>{});
+      if (++t == n) break;
+      head();
     }
-    // drain: O^T += V^T P^T of the last unit (half 1 of the last tile, P in pf[1])
-    step(X0, F, T, F, F, n - 1, 1, 0, 0, -1);
+    // drain: O^T += V^T P^T of the last unit (half 1 of c_{n-1}, P in pf[1])
+    step(X0, F, T, F, F, uoff(integral_constant<int, 0>{}, H1), (unsigned)((n - 1) & 3) * TILE_BYTES,
+         uoff(integral_constant<int, 0>{}, H0), []() {});
     __builtin_amdgcn_s_setprio(0);
+    // the last iterations' loads (into stages nobody reads) land before the
+    // workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // Epilogue: the two halves of each row sum live in lanes lr and lr + 32.

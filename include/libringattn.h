@@ -31,8 +31,8 @@
  *     must be 1; data and stride[0..2] * element size must be multiples of
  *     16 bytes (128-bit loads).  Any other strides are accepted, so a
  *     [B, H, S, d] buffer can be passed as a permuted view; the sequence
- *     stride of k and v (stride[1]) must be at most 2^24 elements
- *     (RA_E_RANGE otherwise).
+ *     stride of k and v (stride[1]) must be at most 2^24 elements and a
+ *     k/v block at most 2^29 keys long (RA_E_RANGE otherwise).
  *   - Per-row statistics m, l, lse are fp32 with shape [B, H, S, 1]
  *     (stride[3] ignored), any strides.
  *   - Query position i of the local block is global position q_off + i; key j

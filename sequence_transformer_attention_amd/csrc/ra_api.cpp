@@ -110,6 +110,8 @@ int check_qkv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const 
   const int64_t lim = std::numeric_limits<int32_t>::max();
   if (q->shape[0] > lim || q->shape[1] > lim || q->shape[2] > lim)
     return fail(RA_E_RANGE, "q dimensions exceed 2^31 - 1");
+  // the kernels walk a block's keys with 32-bit counters
+  if (k->shape[1] > (int64_t(1) << 29)) return fail(RA_E_RANGE, "%s/%s hold more than 2^29 keys per block", kn, vn);
   // the tile loads address the rows of one key tile with 32-bit byte offsets
   if (k->stride[1] > (int64_t(1) << 24) || v->stride[1] > (int64_t(1) << 24))
     return fail(RA_E_RANGE, "%s/%s sequence stride exceeds 2^24 elements", kn, vn);

@@ -76,6 +76,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr float kLazyTau = 8.0f;
+constexpr float kRedoSum = 256.0f;  // 2^kLazyTau
 
 // Physical 16-byte slot of logical slot p in LDS row r: p ^ f(r), with
 // f(r) = 4 (r & 3) + ((r >> 2) & 3) (the two low 2-bit fields of r swapped),
@@ -197,7 +198,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const char* kbase = (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
   const char* vbase = (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (waves w and w + 4 share a SIMD)
   auto gslot = [&](int i, int& r) -> unsigned {
     const int ls = (wv * NL + i) * 64 + lane;
     r = ls / SLOTS;
@@ -213,11 +213,17 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   }
   // Tile at address tb (row stride `stride` elements) with nvalid valid rows
   // into LDS stage `stage`.
+  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
   auto issue = [&](const char* tb, int64_t stride, const unsigned* goff, int nvalid, auto STAGE)
       __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, (int)(unsigned)(BN * stride * 2), 0x00020000);
-    char* dst = &smem[decltype(STAGE)::value][0] + wv * NL * 1024;
+    // LDS destination: the wave's share of the stage.  The base goes through
+    // an empty asm so that the per-stage addresses are formed here (one
+    // scalar add) instead of being hoisted into registers for the kernel.
+    unsigned lb = smem_lds + (unsigned)wv * NL * 1024;
+    asm volatile("" : "+s"(lb));
+    char* dst = (char*)&smem[0][0] + (lb - smem_lds) + decltype(STAGE)::value * TILE_BYTES;
     if (nvalid == BN) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
@@ -239,7 +245,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // Per-lane LDS byte addresses inside a K or V tile (rows of 2D bytes).
   // K, A operand of S^T for the 32-key unit at row 32 h of the tile: row
   // 32 h + lr, logical slot 2c + lg: kaddr[c] + (K stage) + 64 D h.
-  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
   unsigned kaddr[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) kaddr[c] = smem_lds + lr * 2 * D + 16 * swz<SLOTS>(lr, 2 * c + lg);
@@ -281,43 +286,49 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
 
   if (n > 0) {  // workgroup-uniform
     const int64_t roff = a.ring ? 0 : a.kv_off;  // key position - row in k/v
+    const int64_t q0w = a.q_off + qrow_w;        // the wave's first query position
     const int64_t kstep = (int64_t)BN * a.k_ss * 2, vstep = (int64_t)BN * a.v_ss * 2;
     // Cursor over the tiles: loop step cs, tile cu of its cnt tiles, the
-    // tile's key position, keys left in the block from it on, K and V
-    // addresses of its first row.
-    int cs = 0, cu = 0, cnt = 0;
-    int64_t cp = 0, cleft = 0;
+    // tile's key position relative to the wave's first query (saturated at
+    // +-2^30: a tile that far before the queries is fully visible, one that
+    // far after them is never walked under causal masking, and the position
+    // is not used without it; a block holds at most 2^29 keys, so the
+    // position stays on its side of zero), keys left in the block from it
+    // on, K and V addresses of its first row.
+    constexpr int kRelSat = 1 << 30;
+    int cs = 0, cu = 0, cnt = 0, crel = 0, cleft = 0;
     const char* cka = kbase;
     const char* cva = vbase;
     auto cur_set = [&]() {
       cu = 0;
       cnt = step_tiles(cs);
-      cp = step_kv_off(cs);
-      cleft = a.nkv;
-      cka = kbase + (cp - roff) * a.k_ss * 2;
-      cva = vbase + (cp - roff) * a.v_ss * 2;
+      const int64_t kv = step_kv_off(cs), rel = kv - q0w;
+      crel = rel < -kRelSat ? -kRelSat : (rel > kRelSat ? kRelSat : (int)rel);
+      cleft = (int)a.nkv;
+      cka = kbase + (kv - roff) * a.k_ss * 2;
+      cva = vbase + (kv - roff) * a.v_ss * 2;
     };
     while (step_tiles(cs) == 0) ++cs;
     cur_set();
-    // Descriptors of tiles t .. t+3 (key position, valid rows, K and V
-    // addresses) in slots t % 4 .. (t + 3) % 4.  Past the last tile a slot
+    // Descriptors of tiles t .. t+3 (relative key position, valid rows, K and
+    // V addresses, whether the tile needs a mask) in slots t % 4 .. (t + 3) % 4.  Past the last tile a slot
     // keeps the descriptor it held (an earlier tile): the loads made with it
     // land in stages nobody reads, which keeps the loads unconditional.
     int rem = n;
-    int64_t dp[4];
-    int dv[4];
+    int drel[4], dv[4];  // dv: valid rows, + 128 if the tile needs a mask
     const char* dka[4];
     const char* dva[4];
     auto fill = [&](auto SLOT) __attribute__((always_inline)) {
       constexpr int j = decltype(SLOT)::value;
       if (rem > 0) {
-        dp[j] = cp;
-        dv[j] = cleft < BN ? (int)cleft : BN;
+        drel[j] = crel;
+        const int nv = cleft < BN ? cleft : BN;
+        dv[j] = nv + ((nv < BN || (a.causal && crel + BN - 1 > 0)) ? 128 : 0);
         dka[j] = cka;
         dva[j] = cva;
         if (--rem > 0) {
           if (++cu < cnt) {
-            cp += BN;
+            crel += BN;
             cleft -= BN;
             cka += kstep;
             cva += vstep;
@@ -332,11 +343,11 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     };
     auto load_k = [&](auto ST) __attribute__((always_inline)) {
       constexpr int j = decltype(ST)::value;
-      issue(dka[j], a.k_ss, koffg, dv[j], ST);
+      issue(dka[j], a.k_ss, koffg, dv[j] & 127, ST);
     };
     auto load_v = [&](auto ST) __attribute__((always_inline)) {
       constexpr int j = decltype(ST)::value;
-      issue(dva[j], a.v_ss, voffg, dv[j], std::integral_constant<int, 4 + j>{});
+      issue(dva[j], a.v_ss, voffg, dv[j] & 127, std::integral_constant<int, 4 + j>{});
     };
 
     f32x16 sacc[2];           // S^T of units with even / odd index
@@ -404,7 +415,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // cut at the query's own position under causal masking, 0 for SKIP (no
     // visible key for these rows: p = 0).  The key index of register r is
     // 8 (r / 4) + (r % 4) + 4 lg.
-    const int64_t q0w = a.q_off + qrow_w;
     const int nqw = min(32, a.nq - qrow_w);
     auto sm_mask = [&](int x, int64_t k0, int nvalid) __attribute__((always_inline)) {
       // every key valid and, under causal masking, at or before the wave's
@@ -423,63 +433,72 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
           sacc[x][r] = (8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : sacc[x][r];
       }
     };
-    // The softmax in eight steps, one per slot of a pipeline step: partial
-    // maxima, row max and lazy max update, four groups of four exponentials
-    // (fp32 row sum, bf16 P), and the row-sum update.  Tree reductions keep
-    // the dependent chains short.  Each step pins its results with an empty
-    // asm statement (the compiler would otherwise sink the arithmetic towards
-    // its consumers, out of the region it is meant to overlap with).
-    float sm_m[4], sm_ps[4], sm_alpha = 1.f, sm_muse = 0.f;
+    // Softmax of unit u against the running max m2 (log2 units) as it
+    // stands: p = exp2(s c - m2), two keys per slot of the pipeline step, and
+    // the fp32 row sum (only the MFMA operand is rounded to bf16: rows with
+    // few visible keys would otherwise carry the 2^-9 rounding of one term
+    // into l and the LSE).  The row max is not computed on this path.  When a
+    // lane's sum of p exceeds 2^kLazyTau or is not finite (m2 still -inf, or
+    // an overflow), the whole unit is redone after the step against its
+    // exact row max, which becomes m2 (sm_fix).  So m2 moves only on a redo,
+    // every p stays below 2^kLazyTau, and o, l and m2 always agree: the
+    // result does not depend on which max was used.  Each step pins its
+    // results with an empty asm statement (the compiler would otherwise sink
+    // the arithmetic towards its consumers, out of the region it is meant to
+    // overlap with).
+    float sm_ps[4], sm_tot = 0.f;
     auto sm_step = [&](auto X, auto ST) __attribute__((always_inline)) {
-      constexpr int x = decltype(X)::value, st = decltype(ST)::value;
+      constexpr int x = decltype(X)::value, k = decltype(ST)::value;
       const f32x16& s = sacc[x];
-      if constexpr (st == 0) {
-        sm_m[0] = vmax3(s[0], s[1], s[2]);
-        sm_m[1] = vmax3(s[3], s[4], s[5]);
-        sm_m[0] = vmax3(sm_m[0], s[6], s[7]);
-        asm volatile("" : "+v"(sm_m[0]), "+v"(sm_m[1]));
-      } else if constexpr (st == 1) {
-        sm_m[2] = vmax3(s[8], s[9], s[10]);
-        sm_m[3] = vmax3(s[11], s[12], s[13]);
-        sm_m[2] = vmax3(sm_m[2], s[14], s[15]);
-        sm_m[0] = vmax3(sm_m[0], sm_m[1], sm_m[2]);
-        sm_m[0] = vmax3(sm_m[0], sm_m[3], sm_m[3]);
-        asm volatile("" : "+v"(sm_m[0]));
-      } else if constexpr (st == 2) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm_m[0]), __float_as_uint(sm_m[0]), false, false);
-        const float mx = vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
-        const float tm = mx * a.c;
-        const bool bump = tm > m2 + kLazyTau;  // move the max only when it grows by more than kLazyTau
-        sm_alpha = bump ? fast_exp2(m2 - tm) : 1.f;  // 0 when m2 was -inf
-        m2 = bump ? tm : m2;
-        sm_muse = m2 == -INFINITY ? 0.f : m2;  // no visible key yet: p = 0
-        asm volatile("" : "+v"(sm_alpha), "+v"(sm_muse), "+v"(m2));
-      } else if constexpr (st < 7) {
-        // The row sum takes the fp32 p (only the MFMA operand is rounded to
-        // bf16): rows with few visible keys would otherwise carry the 2^-9
-        // rounding of one term into l and the LSE.
-        constexpr int g = st - 3, hh = g >> 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(s[4 * g + i], a.c, -sm_muse));
-          sm_ps[i] = g == 0 ? p : sm_ps[i] + p;
-          pf[x][hh][4 * (g & 1) + i] = (__bf16)p;
-        }
-        asm volatile("" : "+v"(sm_ps[0]), "+v"(sm_ps[1]), "+v"(sm_ps[2]), "+v"(sm_ps[3]), "+v"(pf[x][hh]));
-      } else {
-        lsum = lsum * sm_alpha + ((sm_ps[0] + sm_ps[1]) + (sm_ps[2] + sm_ps[3]));
-        asm volatile("" : "+v"(lsum));
+      const float p0 = fast_exp2(fmaf(s[2 * k], a.c, -m2));
+      const float p1 = fast_exp2(fmaf(s[2 * k + 1], a.c, -m2));
+      if constexpr (k < 4) sm_ps[k] = p0 + p1;
+      else sm_ps[k - 4] += p0 + p1;
+      pf[x][k >> 2][2 * (k & 3)] = (__bf16)p0;
+      pf[x][k >> 2][2 * (k & 3) + 1] = (__bf16)p1;
+      asm volatile("" : "+v"(sm_ps[k & 3]), "+v"(pf[x][k >> 2]));
+      if constexpr (k == 7) {
+        sm_tot = (sm_ps[0] + sm_ps[1]) + (sm_ps[2] + sm_ps[3]);
+        asm volatile("" : "+v"(sm_tot));
       }
     };
-    // O *= alpha after a max update (rare: the max moves by more than
-    // kLazyTau only a few times per row).
-    auto sm_rescale = [&]() __attribute__((always_inline)) {
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(sm_alpha != 1.f) != 0, 0)) {
+    // After the step: redo the unit if any lane asks for it, then add its
+    // row sum.  The redo moves m2 to the exact row max, rescales o and l by
+    // alpha = exp2(m2_old - m2_new) (0 when m2 was -inf) and recomputes p
+    // (0 for rows with no visible key yet).
+    auto sm_fix = [&](auto X) __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(sm_tot <= kRedoSum)) != 0, 0)) {
+        const f32x16& s = sacc[x];
+        float mx = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax3(s[6], s[7], s[8]));
+        mx = vmax3(mx, vmax3(s[9], s[10], s[11]), vmax3(s[12], s[13], s[14]));
+        mx = vmax3(mx, s[15], s[15]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float tm = vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1])) * a.c;
+        const bool up = tm > m2;
+        const float alpha = up ? fast_exp2(m2 - tm) : 1.f;
+        m2 = up ? tm : m2;
+        const float muse = m2 == -INFINITY ? 0.f : m2;
+        float tot = 0.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int k = 0; k < 8; ++k) {
+          const float p0 = fast_exp2(fmaf(s[2 * k], a.c, -muse));
+          const float p1 = fast_exp2(fmaf(s[2 * k + 1], a.c, -muse));
+          tot += p0 + p1;
+          pf[x][k >> 2][2 * (k & 3)] = (__bf16)p0;
+          pf[x][k >> 2][2 * (k & 3) + 1] = (__bf16)p1;
+          asm volatile("" : "+v"(pf[x][k >> 2]), "+v"(tot));
+        }
+        sm_tot = tot;
+        lsum *= alpha;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= sm_alpha;
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
       }
+      lsum += sm_tot;
     };
 
     // MFMA m of a step: m < KC: step c = m of S^T(u+1) into sacc[XN]; else
@@ -544,7 +563,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
         });
       });
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (sm) sm_rescale();
+      if constexpr (sm) sm_fix(X);
     };
     auto half_valid = [](int nv, int hf) { const int x = nv - 32 * hf; return x < 0 ? 0 : (x > 32 ? 32 : x); };
     const std::true_type T;
@@ -561,7 +580,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // fragments of unit 1.
     fill(integral_constant<int, 0>{});
 #pragma unroll
-    for (int j = 1; j < 4; ++j) dp[j] = dp[0], dv[j] = dv[0], dka[j] = dka[0], dva[j] = dva[0];
+    for (int j = 1; j < 4; ++j) drel[j] = drel[0], dv[j] = dv[0], dka[j] = dka[0], dva[j] = dva[0];
     fill(integral_constant<int, 1>{});
     fill(integral_constant<int, 2>{});
     fill(integral_constant<int, 3>{});
@@ -598,30 +617,20 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // last iteration S^T of the nonexistent unit 2n and the K reads past the
     // end fill registers that are never used (stale but in-bounds LDS).  Unit
     // 2t has its S^T in sacc[0], unit 2t+1 in sacc[1].
-    auto needs_mask = [&](int64_t p, int v) { return v < BN || (a.causal && p + BN - 1 > q0w); };
-    bool mt = needs_mask(dp[0], dv[0]);
     auto iter = [&](auto J) __attribute__((always_inline)) {  // iteration t, J = t % 4
       constexpr int j = decltype(J)::value;
       const integral_constant<int, j> SJ;
       const integral_constant<int, (j + 1) & 3> SJ1;
       const integral_constant<int, (j + 2) & 3> SJ2;
       const integral_constant<int, (j + 3) & 3> SJ3;
-      // The two waves of a SIMD (w, w + 4) run the same steps; issue goes to
-      // the older wave first, which would finish the iteration long before
-      // the other and then wait at the barrier.  Each wave takes the higher
-      // priority for one of the two steps instead.
-      if (grp) __builtin_amdgcn_s_setprio(0);
-      else __builtin_amdgcn_s_setprio(1);
-      if (__builtin_expect(mt, 0)) sm_mask(0, dp[j], half_valid(dv[j], 0));
+      const bool mt = dv[j] >= 128;
+      if (__builtin_expect(mt, 0)) sm_mask(0, q0w + drel[j], half_valid(dv[j] & 127, 0));
       // unit 2t: P V of unit 2t-1 (c_{t-1}, half 1), K of unit 2t+2 (c_{t+1}, half 0), load K(c_{t+3})
       step(X0, T, T, T, T, uoff(SJ3, H1), 0u, uoff(SJ1, H0), [&]() __attribute__((always_inline)) { load_k(SJ3); });
-      if (grp) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
-      if (__builtin_expect(mt, 0)) sm_mask(1, dp[j] + 32, half_valid(dv[j], 1));
+      if (__builtin_expect(mt, 0)) sm_mask(1, q0w + drel[j] + 32, half_valid(dv[j] & 127, 1));
       // unit 2t+1: P V of unit 2t (c_t, half 0), K of unit 2t+3 (c_{t+1}, half 1), load V(c_{t+2})
       step(X1, T, T, T, T, uoff(SJ, H0), 0u, uoff(SJ1, H1), [&]() __attribute__((always_inline)) { load_v(SJ2); });
       fill(SJ);  // slot of c_t now holds c_{t+4}
-      mt = needs_mask(dp[(j + 1) & 3], dv[(j + 1) & 3]);
     };
     int t = 0;
     for (;;) {
@@ -641,7 +650,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // drain: O^T += V^T P^T of the last unit (half 1 of c_{n-1}, P in pf[1])
     step(X0, F, T, F, F, uoff(integral_constant<int, 0>{}, H1), (unsigned)((n - 1) & 3) * TILE_BYTES,
          uoff(integral_constant<int, 0>{}, H0), []() {});
-    __builtin_amdgcn_s_setprio(0);
     // the last iterations' loads (into stages nobody reads) land before the
     // workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -97,6 +97,8 @@ def good_step_args(B=1, nq=256, nkv=256, hq=4, hkv=2, d=128, dt=ra.RA_BF16):
     (lambda a: setattr(a["q"], "data", FAKE + 8), ra.RA_E_LAYOUT),
     # k row stride beyond 2^24 elements (the tile loads use 32-bit row offsets)
     (lambda a: a.update(k=T([1, 256, 2, 128], stride=[256 * (1 << 25), 1 << 25, 128, 1])), ra.RA_E_RANGE),
+    # k/v blocks longer than 2^29 keys (32-bit key counters in the kernels)
+    (lambda a: a.update(k=T([1, (1 << 29) + 1, 2, 128]), v=T([1, (1 << 29) + 1, 2, 128])), ra.RA_E_RANGE),
     (lambda a: a.update(q=T([1, 256, 4, 96]), k=T([1, 256, 2, 96]), v=T([1, 256, 2, 96]),
                         oacc=T([1, 256, 4, 96], ra.RA_F32)), ra.RA_E_UNSUPPORTED),
 ])

@@ -9,30 +9,37 @@
 // "Tiled Computation" -- each block is processed in tiles that stay on chip.
 //
 // bf16 path (attn_bf16_kernel): one workgroup = 8 waves = 256 query rows of
-// one head; each wave owns 32 query rows.  Per key tile of 64 keys:
+// one head; each wave owns 32 query rows; the two waves that share a SIMD
+// (w and w + 4) feed its matrix core and vector ALU from two instruction
+// streams.  Keys come in tiles of 64, processed as two 32-key units:
 //   S^T (keys x queries) = K Q^T   v_mfma_f32_32x32x16_bf16; K from LDS is the
 //                                  A operand, the Q fragment stays in VGPRs
 //                                  for the whole kernel as the B operand
 //   online softmax                 the accumulator layout puts one query per
-//                                  lane (lane & 31) and 32 of its 64 keys in
-//                                  that lane's registers; the other 32 sit in
-//                                  lane ^ 32, so the row max needs one
-//                                  v_permlane32_swap and the rescale factor is
-//                                  a per-lane scalar
-//   O^T (channels x queries) += V^T P^T   P^T goes from the S^T accumulator
-//                                  registers straight into the B operand
-//                                  (bf16, round to nearest even); the A
-//                                  operand V^T comes from row-major V in LDS
-//                                  through the transposing ds_read_b64_tr_b16
-// K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging) into two stages, row-major under an XOR swizzle of the 16-byte
-// slots (conflict-free K and transposing V reads); one barrier per tile.
+//                                  lane (lane & 31) and 16 of the unit's 32
+//                                  keys in that lane's registers (the other
+//                                  16 sit in lane ^ 32)
+//   O^T (channels x queries) += V^T P^T   P^T goes from registers straight
+//                                  into the B operand (bf16, round to nearest
+//                                  even); the A operand V^T comes from
+//                                  row-major V in LDS through the transposing
+//                                  ds_read_b64_tr_b16
+// Per wave, a software pipeline with one step per unit u: the MFMAs of
+// S(u+1) and of O += V(u-1) P(u-1) interleaved with the vector work of the
+// softmax of S(u), which depends on neither.
+// K and V tiles move HBM -> LDS with buffer loads straight into LDS (no
+// register staging), loaded three (K) and two (V) tiles ahead into four K
+// and four V stages, row-major under an XOR swizzle of the 16-byte slots
+// (conflict-free K and transposing V reads); one barrier per tile.  The
+// loop body covers four tiles, so every LDS read address is a per-lane base
+// plus an immediate offset.
 // Logits are scaled in fp32 (never folded into bf16 Q); exponentials are
 // base 2 with the scale folded into one FMA: p = exp2(s * scale * log2(e) - m2),
-// m2 the running max in log2 units.  m2 is moved only when a tile's max
-// exceeds it by more than kLazyTau, so the rescale of O is rare; the result
-// does not depend on which max is used as long as o, l and m agree
-// (O = o / l, LSE = m + ln l), and p stays <= 2^kLazyTau.
+// m2 the running max in log2 units.  The softmax uses m2 as it stands and
+// skips the row max; a unit whose row sum exceeds kRedoSum = 2^8, or is not
+// finite, is redone against its exact row max, which becomes m2 (with O and
+// l rescaled).  The result does not depend on which max is used as long as
+// o, l and m agree (O = o / l, LSE = m + ln l), and p stays at most 2^8.
 //
 // fp32 path (attn_f32_kernel): one wave per 64 query rows, fp32 FMA
 // throughout, for the fp32 workloads.
@@ -75,8 +82,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-constexpr float kLazyTau = 8.0f;
-constexpr float kRedoSum = 256.0f;  // 2^kLazyTau
+constexpr float kRedoSum = 256.0f;  // redo a unit when a lane's sum of p exceeds this
 
 // Physical 16-byte slot of logical slot p in LDS row r: p ^ f(r), with
 // f(r) = 4 (r & 3) + ((r >> 2) & 3) (the two low 2-bit fields of r swapped),
@@ -270,9 +276,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // u = 2t + h (half h of tile t).  Every wave runs the same software
   // pipeline, one step per unit: step u issues the MFMAs of
   //   S(u+1) = K(u+1) Q^T   and   O^T += V(u-1)^T P(u-1)^T
-  // interleaved with the vector work of the softmax of S(u) (mask, row max,
-  // lazy max update, P(u) = exp2(S c - m), row sum), which depends on
-  // neither; the rescale of O after a max update follows the step.  Two waves
+  // interleaved with the vector work of the softmax of S(u) (P(u) =
+  // exp2(S c - m), row sum), which depends on neither; the mask of a tile
+  // that needs one precedes the step, a redo of the unit follows it.  Two waves
   // share each SIMD, so both the matrix cores and the vector ALUs are fed by
   // two instruction streams.  The K fragments of unit u+1 are read in the
   // second half of step u-1, the V^T fragments of unit u-1 in the first half
@@ -438,10 +444,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // the fp32 row sum (only the MFMA operand is rounded to bf16: rows with
     // few visible keys would otherwise carry the 2^-9 rounding of one term
     // into l and the LSE).  The row max is not computed on this path.  When a
-    // lane's sum of p exceeds 2^kLazyTau or is not finite (m2 still -inf, or
+    // lane's sum of p exceeds kRedoSum or is not finite (m2 still -inf, or
     // an overflow), the whole unit is redone after the step against its
     // exact row max, which becomes m2 (sm_fix).  So m2 moves only on a redo,
-    // every p stays below 2^kLazyTau, and o, l and m2 always agree: the
+    // every p stays at most kRedoSum, and o, l and m2 always agree: the
     // result does not depend on which max was used.  Each step pins its
     // results with an empty asm statement (the compiler would otherwise sink
     // the arithmetic towards its consumers, out of the region it is meant to

@@ -111,6 +111,55 @@ def cpu_baseline(w, x, O_gpu, lse_gpu, target_s: float):
     return base, parity
 
 
+def stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch, reps: int = 5):
+    """The same share as P ra_step calls (ring order, state in HBM) plus
+    ra_finalize, and ra_finalize alone (HBM-bound: rows x (6d + 12) bytes for
+    bf16 O: o_acc fp32, m and l read, O and LSE written).  Both timed with
+    HIP events on the launch stream; the median of `reps` runs."""
+    dev = qd.device
+    nkv = w.N // w.P
+    o_acc = torch.empty((w.B, w.nq, w.Hq, w.d), dtype=torch.float32, device=dev)
+    m = torch.empty((w.B, w.Hq, w.nq), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    odt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    O = torch.empty((w.B, w.nq, w.Hq, w.d), dtype=odt, device=dev)
+    lse = torch.empty_like(m)
+    blocks = [(ra.ra_ring_block(w.P, r, s), ) for s in range(w.P)]
+    kb = [kd[:, j * nkv:(j + 1) * nkv] for (j,) in blocks]
+    vb = [vd[:, j * nkv:(j + 1) * nkv] for (j,) in blocks]
+
+    def stepwise():
+        ra.ra_state_init(o_acc, m, l)
+        for (j,), kk, vv in zip(blocks, kb, vb):
+            ra.ra_step(qd, kk, vv, o_acc, m, l, r * nkv, j * nkv, w.causal)
+        ra.ra_finalize(o_acc, l, m=m, o_out=O, lse_out=lse)
+
+    def timed(fn):
+        stream = torch.cuda.current_stream()
+        fn()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
+        return sorted(per)[len(per) // 2]
+
+    st_ms = timed(stepwise)
+    fin_ms = timed(lambda: ra.ra_finalize(o_acc, l, m=m, o_out=O, lse_out=lse))
+    rows = w.B * w.Hq * w.nq
+    fin_bytes = rows * (6 * w.d + 12) if w.dtype == "bf16" else rows * (8 * w.d + 12)
+    log(f"stepwise {w.P} x ra_step + ra_finalize: {st_ms:.3f} ms -> {flop / st_ms / 1e9:.1f} TFLOP/s; "
+        f"ra_finalize alone {fin_ms * 1e3:.1f} us -> {fin_bytes / fin_ms / 1e6:.0f} GB/s")
+    return {"stepwise": {"ms": round(st_ms, 4), "tflops": round(flop / st_ms / 1e9, 3), "launches": w.P + 2},
+            "finalize": {"us": round(fin_ms * 1e3, 2), "bytes": fin_bytes,
+                         "GB/s": round(fin_bytes / fin_ms / 1e6, 1),
+                         "frac_of_hbm": round(fin_bytes / fin_ms / 1e6 / HBM_PEAK_GBS, 4)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +231,8 @@ def main() -> int:
     log(f"{w.name}: {ms_per_step:.3f} ms/step, kernel mean {mean_ms:.3f} ms "
         f"(median {per[len(per) // 2]:.3f}, min {per[0]:.3f}) -> {achieved:.1f} TFLOP/s")
 
+    side = stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch)
+
     out = {
         "metric": "rank-share ring-attention TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -198,6 +249,8 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name)},
         "inputs_sha256": {t: inputs.sha256(xq[t])[:16] for t in "qkv"},
+        "stepwise": side["stepwise"],
+        "finalize": side["finalize"],
     }
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, xq, O, lse, args.cpu_seconds)

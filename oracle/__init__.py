@@ -62,6 +62,10 @@ def _load(path: Optional[str] = None):
     lib.orc_rank_share.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                    ctypes.c_int, ctypes.c_double, _ip, _i64, _dp, _dp, ctypes.c_int]
     lib.orc_rank_share.restype = ctypes.c_int
+    lib.orc_rank_share_zigzag.argtypes = lib.orc_rank_share.argtypes
+    lib.orc_rank_share_zigzag.restype = ctypes.c_int
+    lib.orc_share_flops_zigzag.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.orc_share_flops_zigzag.restype = ctypes.c_double
     lib.orc_ring_block.argtypes = [_i64, _i64, _i64]
     lib.orc_ring_block.restype = _i64
     lib.orc_classify.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
@@ -202,6 +206,34 @@ def rank_share(q, k, v, P: int, rank: int, causal: bool, scale: Optional[float] 
     return out, lse
 
 
+def rank_share_zigzag(q, k, v, P: int, rank: int, causal: bool, scale: Optional[float] = None,
+                      rows=None, nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Load-balanced share: local Q [B, 2c, Hq, d] = [chunk rank | chunk 2P-1-rank]
+    (c = N/(2P)) against the P ring blocks of K, V [B, N, Hkv, d], block j being
+    key chunks j and 2P-1-j.  Returns O [n, d], LSE [n] for the listed rows."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, nq, hq, d = q.shape
+    N, hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    r = _rows(rows, B, hq, nq)
+    n = r.shape[0]
+    out = np.zeros((n, d)); lse = np.zeros(n)
+    e = lib.orc_rank_share_zigzag(_ptr(q), _ptr(k), _ptr(v), B, N, P, rank, hq, hkv, d, int(causal),
+                                  float(scale), r.ctypes.data_as(_ip), n, _ptr(out), _ptr(lse),
+                                  nthreads or default_threads())
+    if e:
+        raise ValueError(f"orc_rank_share_zigzag failed ({e})")
+    return out, lse
+
+
+def zigzag_positions(N: int, P: int, rank: int) -> np.ndarray:
+    """Global positions of the local rows of the load-balanced share."""
+    c = N // (2 * P)
+    return np.concatenate([rank * c + np.arange(c), (2 * P - 1 - rank) * c + np.arange(c)])
+
+
 def ring_block(P: int, rank: int, s: int) -> int:
     return int(_load().orc_ring_block(P, rank, s))
 
@@ -217,3 +249,7 @@ def visible_pairs(q_off: int, nq: int, kv_off: int, nkv: int, causal: bool) -> i
 
 def share_flops(B: int, N: int, P: int, rank: int, Hq: int, d: int, causal: bool) -> float:
     return float(_load().orc_share_flops(B, N, P, rank, Hq, d, int(causal)))
+
+
+def share_flops_zigzag(B: int, N: int, P: int, rank: int, Hq: int, d: int, causal: bool) -> float:
+    return float(_load().orc_share_flops_zigzag(B, N, P, rank, Hq, d, int(causal)))

@@ -269,6 +269,73 @@ done:
     return e;
 }
 
+/* Load-balanced ("zigzag") share, the reading of "Implementation
+ * Considerations / Load Balancing" used here: the sequence is cut into 2P
+ * chunks of c = N/(2P) tokens and rank r owns chunks r and 2P-1-r, so under
+ * causal masking every rank gets the same number of visible pairs.  The
+ * local query block is [chunk r | chunk 2P-1-r] (2c rows): local row i sits
+ * at global position r*c + i for i < c and (2P-1-r)*c + (i - c) otherwise.
+ * The ring is unchanged: at step s rank r holds the block of rank
+ * j = (r - s) mod P, i.e. key chunks j and 2P-1-j (k, v are the whole
+ * sequence, [B, N, Hkv, d]); every local query attends to both chunks and
+ * the partials are merged as in orc_rank_share.  Listed rows of the two
+ * query chunks are handled as two row lists, each with its own position of
+ * local row 0 (q_off = r*c, and (2P-1-r)*c - c for the second chunk). */
+int orc_rank_share_zigzag(const double *q, const double *k, const double *v,
+                          int64_t B, int64_t N, int64_t P, int64_t rank,
+                          int64_t hq, int64_t hkv, int64_t d, int causal, double scale,
+                          const int64_t *rows, int64_t nrows, double *out, double *lse, int nthreads)
+{
+    if (P <= 0 || N % (2 * P) != 0) return -3;
+    if (rank < 0 || rank >= P) return -5;
+    const int64_t c = N / (2 * P), nq = 2 * c;
+    const int64_t q_off[2] = {rank * c, (2 * P - 1 - rank) * c - c};
+    size_t n1 = (size_t)(nrows > 0 ? nrows : 1), nd = n1 * (size_t)d;
+    int64_t *sub = malloc(3 * n1 * sizeof(int64_t)), *idx = malloc(n1 * sizeof(int64_t));
+    double *m = malloc(n1 * sizeof(double)), *l = malloc(n1 * sizeof(double)), *o = malloc(nd * sizeof(double));
+    double *pm = malloc(n1 * sizeof(double)), *pl = malloc(n1 * sizeof(double)), *po = malloc(nd * sizeof(double));
+    double *so = malloc(nd * sizeof(double)), *sl = malloc(n1 * sizeof(double));
+    int e = 0;
+    if (!sub || !idx || !m || !l || !o || !pm || !pl || !po || !so || !sl) { e = -8; goto done; }
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[3 * r + 2] < 0 || rows[3 * r + 2] >= nq) { e = -5; goto done; }
+    for (int half = 0; half < 2; ++half) {
+        /* the listed rows of this query chunk */
+        int64_t n = 0;
+        for (int64_t r = 0; r < nrows; ++r) {
+            if ((rows[3 * r + 2] >= c) != half) continue;
+            sub[3 * n] = rows[3 * r]; sub[3 * n + 1] = rows[3 * r + 1]; sub[3 * n + 2] = rows[3 * r + 2];
+            idx[n++] = r;
+        }
+        if (n == 0) continue;
+        for (int64_t r = 0; r < n; ++r) {
+            m[r] = -INFINITY;
+            l[r] = 0.0;
+            for (int64_t x = 0; x < d; ++x) o[r * d + x] = 0.0;
+        }
+        for (int64_t s = 0; s < P; ++s) {
+            const int64_t j = orc_ring_block(P, rank, s);
+            const int64_t chunks[2] = {j, 2 * P - 1 - j};
+            for (int t = 0; t < 2; ++t) {
+                const int64_t kc = chunks[t];
+                e = orc_block_partial(q, k + kc * c * hkv * d, v + kc * c * hkv * d,
+                                      B, nq, N, nq, c, hq, hkv, d, q_off[half], kc * c,
+                                      causal, scale, sub, n, pm, pl, po, nthreads);
+                if (e) goto done;
+                orc_merge(n, d, m, l, o, pm, pl, po, m, l, o);
+            }
+        }
+        orc_finalize(n, d, m, l, o, so, sl);
+        for (int64_t r = 0; r < n; ++r) {
+            lse[idx[r]] = sl[r];
+            for (int64_t x = 0; x < d; ++x) out[idx[r] * d + x] = so[r * d + x];
+        }
+    }
+done:
+    free(sub); free(idx); free(m); free(l); free(o); free(pm); free(pl); free(po); free(so); free(sl);
+    return e;
+}
+
 /* Block class of (query positions [q_off, q_off+nq), key positions
  * [kv_off, kv_off+nkv)): 0 = no visible pair (SKIP), 1 = every pair visible
  * (FULL), 2 = some but not all (PARTIAL). */
@@ -306,6 +373,27 @@ double orc_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq
         int cls = orc_classify(rank * nb, nb, j * nb, nb, causal);
         double w = cls == 1 ? 1.0 : (cls == 2 ? 0.5 : 0.0);
         f += w * 4.0 * (double)d * (double)hq * (double)nb * (double)nb * (double)B;
+    }
+    return f;
+}
+
+/* The same FLOP rule for the load-balanced share: each (query chunk, key
+ * chunk) pair of c x c tokens counts 4 * d * Hq * c * c * B weighted by its
+ * class. */
+double orc_share_flops_zigzag(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d, int causal)
+{
+    const int64_t c = N / (2 * P);
+    const int64_t qpos[2] = {rank * c, (2 * P - 1 - rank) * c};
+    double f = 0.0;
+    for (int64_t s = 0; s < P; ++s) {
+        const int64_t j = orc_ring_block(P, rank, s);
+        const int64_t kpos[2] = {j * c, (2 * P - 1 - j) * c};
+        for (int a = 0; a < 2; ++a)
+            for (int t = 0; t < 2; ++t) {
+                const double weight[3] = {0.0, 1.0, 0.5};   /* SKIP, FULL, PARTIAL */
+                f += weight[orc_classify(qpos[a], c, kpos[t], c, causal)] * 4.0 * (double)d * (double)hq *
+                     (double)c * (double)c * (double)B;
+            }
     }
     return f;
 }

@@ -26,6 +26,11 @@ MUTANTS = {
     "max_not_subtracted_in_l": ("l += w;", "l += exp(s[j]);"),
     "classify_full_off_by_one": ("if (kv_off + nkv - 1 <= q_off) return 1;", "if (kv_off + nkv <= q_off) return 1;"),
     "flops_partial_weight": ("cls == 2 ? 0.5 : 0.0", "cls == 2 ? 1.0 : 0.0"),
+    "zigzag_second_chunk_position": ("const int64_t q_off[2] = {rank * c, (2 * P - 1 - rank) * c - c};",
+                                     "const int64_t q_off[2] = {rank * c, (2 * P - 1 - rank) * c};"),
+    "zigzag_key_chunk": ("const int64_t chunks[2] = {j, 2 * P - 1 - j};", "const int64_t chunks[2] = {j, 2 * P - 2 - j};"),
+    "zigzag_flops_key_chunk": ("const int64_t kpos[2] = {j * c, (2 * P - 1 - j) * c};",
+                               "const int64_t kpos[2] = {j * c, (2 * P - 2 - j) * c};"),
     "pairs_count_off_by_one": ("int64_t c = causal ? q_off + i - kv_off + 1 : nkv;", "int64_t c = causal ? q_off + i - kv_off : nkv;"),
 }
 
@@ -41,6 +46,8 @@ PINS = [
     lambda: pins.test_last_rank_skips_no_block(),
     lambda: pins.test_classify_and_pair_count_match_brute_force(),
     lambda: pins.test_share_flops_rule(),
+    lambda: pins.test_zigzag_share_is_full_attention_at_its_positions(1, 48, 3, 2, 1, 8, True),
+    lambda: pins.test_zigzag_flops_rule_and_balance(),
 ]
 
 

@@ -281,6 +281,60 @@ def test_share_flops_of_the_workloads():
     assert sum(oracle.share_flops(1, 512, 4, r, 2, 64, False) for r in range(4)) == 134217728
 
 
+# ----------------------------------------------------- load-balanced (zigzag)
+@pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal", [
+    (1, 48, 3, 2, 1, 8, True),      # GQA, c = 8
+    (2, 40, 2, 2, 2, 4, True),      # c = 10
+    (1, 36, 3, 1, 1, 8, False),     # c = 6, no mask
+])
+def test_zigzag_share_is_full_attention_at_its_positions(B, N, P, Hq, Hkv, d, causal):
+    """Rank r's load-balanced share holds chunks r and 2P-1-r of the queries:
+    row i of its output must be row pos(i) of full attention (torch fp64)."""
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=N + P)
+    O_t, L_t = _torch_attention(q, k, v, 0, 0, causal, 0.3)
+    seen = []
+    for r in range(P):
+        pos = oracle.zigzag_positions(N, P, r)
+        seen.extend(pos.tolist())
+        o, lse = oracle.rank_share_zigzag(q[:, pos], k, v, P, r, causal, 0.3)
+        np.testing.assert_allclose(_grid(o, B, Hq, len(pos)), O_t[:, pos].numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse.reshape(B, Hq, len(pos)), L_t[:, :, pos].numpy(), atol=TOL, rtol=0)
+    assert sorted(seen) == list(range(N))  # the shares cover the sequence once
+
+
+def test_zigzag_share_matches_brute_force():
+    """Pure-Python brute force of every rank's rows (N = 8, P = 2, c = 2)."""
+    B, N, P, H, d = 1, 8, 2, 1, 4
+    q, k, v = _rand(B, N, N, H, H, d, seed=3)
+    bo, bl = brute.attention(q, k, v, 0, 0, True, 0.5)
+    for r in range(P):
+        pos = oracle.zigzag_positions(N, P, r)
+        o, lse = oracle.rank_share_zigzag(q[:, pos], k, v, P, r, True, 0.5)
+        for n, p in enumerate(pos):
+            assert abs(lse[n] - bl[0][0][p]) < TOL
+            assert max(abs(x - y) for x, y in zip(o[n], bo[0][p][0])) < TOL
+
+
+def test_zigzag_flops_rule_and_balance():
+    """The FLOP rule on the load-balanced share: every pair of a FULL chunk
+    pair, half of a PARTIAL one; under causal masking all ranks are equal and
+    together equal the contiguous split."""
+    for (B, N, P, H, d) in ((1, 48, 3, 2, 8), (2, 128, 4, 3, 16)):
+        c = N // (2 * P)
+        per = []
+        for r in range(P):
+            f = oracle.share_flops_zigzag(B, N, P, r, H, d, True)
+            qpos = (r * c, (2 * P - 1 - r) * c)
+            pairs = sum(oracle.visible_pairs(a, c, t * c, c, True) for a in qpos for t in range(2 * P))
+            assert f == 4 * d * H * B * (pairs - c)  # the two diagonal chunks lose c/2 each
+            assert oracle.share_flops_zigzag(B, N, P, r, H, d, False) == 4 * d * H * B * (2 * c) * N
+            per.append(f)
+        assert len(set(per)) == 1
+        assert sum(per) == sum(oracle.share_flops(B, N, P, r, H, d, True) for r in range(P))
+    # rank-7-of-8 shape: every rank does 4 of the contiguous last rank's 7.5 block-equivalents
+    assert oracle.share_flops_zigzag(1, 32768, 8, 0, 32, 128, True) == 1099511627776
+
+
 # ------------------------------------------------------------ input generator
 def test_inputs_are_deterministic_and_seeded():
     a = inputs.draw_qkv(1, 64, 128, 4, 2, 16, seed=7)

@@ -160,6 +160,45 @@ def stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch, reps: int = 5):
                          "frac_of_hbm": round(fin_bytes / fin_ms / 1e6 / HBM_PEAK_GBS, 4)}}
 
 
+def load_balance(w, r, qd, kd, vd, mean_ms, ra, torch, reps: int = 5):
+    """Causal load balance across the ring: the contiguous share of rank 0
+    against the timed rank's, and the load-balanced (zigzag) share of the
+    first and last rank, same shapes (the local Q has N/P rows either way)."""
+    if not w.causal or w.P < 2 or w.N % (2 * w.P) != 0:
+        return None
+    O = torch.empty((w.B, w.nq, w.Hq, w.d), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                    device=qd.device)
+    lse = torch.empty((w.B, w.Hq, w.nq), dtype=torch.float32, device=qd.device)
+
+    def timed(fn):
+        stream = torch.cuda.current_stream()
+        fn()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
+        return sorted(per)[len(per) // 2]
+
+    c0 = timed(lambda: ra.ra_rank_share(qd, kd, vd, w.P, 0, True, O, lse))
+    zz = {}
+    for rr in (0, w.P - 1):
+        ms = timed(lambda: ra.ra_rank_share_zigzag(qd, kd, vd, w.P, rr, True, O, lse))
+        f = ra.ra_share_flops_zigzag(w.B, w.N, w.P, rr, w.Hq, w.d, True)
+        zz[f"rank{rr}"] = {"ms": round(ms, 4), "tflops": round(f / ms / 1e9, 3)}
+    slow_contig = max(c0, mean_ms)
+    slow_zz = max(v["ms"] for v in zz.values())
+    log(f"load balance: contiguous rank 0 {c0:.3f} ms, rank {r} {mean_ms:.3f} ms; zigzag "
+        + ", ".join(f"{k} {v['ms']:.3f} ms ({v['tflops']:.0f} TFLOP/s)" for k, v in zz.items())
+        + f"; slowest rank {slow_contig / slow_zz:.2f}x faster")
+    return {"contiguous_ms": {"rank0": round(c0, 4), f"rank{r}": round(mean_ms, 4)}, "zigzag": zz,
+            "slowest_rank_speedup": round(slow_contig / slow_zz, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +271,7 @@ def main() -> int:
         f"(median {per[len(per) // 2]:.3f}, min {per[0]:.3f}) -> {achieved:.1f} TFLOP/s")
 
     side = stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch)
+    balance = load_balance(w, r, qd, kd, vd, mean_ms, ra, torch)
 
     out = {
         "metric": "rank-share ring-attention TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
@@ -251,6 +291,7 @@ def main() -> int:
         "inputs_sha256": {t: inputs.sha256(xq[t])[:16] for t in "qkv"},
         "stepwise": side["stepwise"],
         "finalize": side["finalize"],
+        "load_balance": balance,
     }
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, xq, O, lse, args.cpu_seconds)

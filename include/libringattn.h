@@ -124,6 +124,24 @@ int ra_finalize(const ra_tensor *o_acc, const ra_tensor *l, const ra_opts *opts)
 int ra_rank_share(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                   int P, int rank, int causal, const ra_opts *opts);
 
+/* One rank's LOAD-BALANCED share in one launch (glossary page "sequence
+ * parallelism transformers", section "Implementation Considerations", item
+ * "Load Balancing": under causal masking contiguous shards leave rank 0 with
+ * half a block of work and rank P-1 with P - 1/2).  The sequence is cut into
+ * 2P chunks of c = N/(2P) tokens and rank r owns chunks r and 2P-1-r, so
+ * every rank gets the same number of visible pairs.
+ *   q:    [B, 2c, Hq, d] = [chunk r | chunk 2P-1-r]: local row i is global
+ *         position r*c + i for i < c and (2P-1-r)*c + (i - c) otherwise;
+ *   k, v: [B, N, Hkv, d], the whole sequence in natural order (the ring
+ *         block of rank j is key chunks j and 2P-1-j);
+ *   opts->o_out (required) [B, 2c, Hq, d] and opts->lse_out (optional)
+ *         [B, Hq, 2c] in the same local row order.
+ * Every key chunk is folded into both query chunks; the fold order differs
+ * from the ring's only in rounding.  N % (2P) != 0 or Nq != 2 N/(2P) is
+ * RA_E_SHAPE; other errors as for ra_rank_share. */
+int ra_rank_share_zigzag(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                         int P, int rank, int causal, const ra_opts *opts);
+
 /* ---- host-only queries (no GPU needed) --------------------------------- */
 
 /* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1. */
@@ -147,6 +165,12 @@ int ra_tile_shape(int32_t dtype, int64_t d, int64_t *bm, int64_t *bn);
  * weighted 1 for FULL, 1/2 for PARTIAL (the causal diagonal), 0 for SKIP. */
 double ra_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d,
                       int causal);
+
+/* The same FLOP rule for ra_rank_share_zigzag's share: each (query chunk,
+ * key chunk) pair of c x c tokens counts 4 * c * c * d * Hq * B, weighted by
+ * its class.  -1 if N % (2P) != 0 or rank is outside [0, P). */
+double ra_share_flops_zigzag(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d,
+                             int causal);
 
 /* Description of the last error on this thread ("" if none). */
 const char *ra_last_error(void);

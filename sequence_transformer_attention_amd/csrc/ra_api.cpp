@@ -189,6 +189,7 @@ int ra_step(const ra_tensor* q, const ra_tensor* k_blk, const ra_tensor* v_blk, 
   if (B == 0 || nq == 0 || ra_plan_class(q_off, nq, kv_off, nkv, causal) == RA_CLASS_SKIP) return ok();
 
   RaAttnArgs a{};
+  a.nsplit = 1;
   a.q = q->data; set_bshd(q, a.q_sb, a.q_ss, a.q_sh);
   a.k = k_blk->data; set_bshd(k_blk, a.k_sb, a.k_ss, a.k_sh);
   a.v = v_blk->data; set_bshd(v_blk, a.v_sb, a.v_ss, a.v_sh);
@@ -237,23 +238,33 @@ int ra_finalize(const ra_tensor* o_acc, const ra_tensor* l, const ra_opts* opts)
   return launched(ra_launch_finalize(a, stream_of(opts)), "ra_finalize launch");
 }
 
-int ra_rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
-                  const ra_opts* opts) {
+// One rank's share in one launch.  zigzag == 0: the local rows are block
+// `rank` of P contiguous blocks; zigzag == 1: they are chunks rank and
+// 2P-1-rank of 2P chunks (the load-balanced share), each chunk folding all 2P
+// key chunks in its own ring order.
+static int rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
+                      const ra_opts* opts, int zigzag) {
+  const char* fn = zigzag ? "ra_rank_share_zigzag" : "ra_rank_share";
   int e = check_qkv(q, k, v, "k", "v");
   if (e) return e;
-  if (!opts || !opts->o_out) return fail(RA_E_NULL, "ra_rank_share needs opts->o_out");
+  if (!opts || !opts->o_out) return fail(RA_E_NULL, "%s needs opts->o_out", fn);
   if (P < 1) return fail(RA_E_RANGE, "P must be >= 1 (got %d)", P);
   if (rank < 0 || rank >= P) return fail(RA_E_RANGE, "rank %d outside [0, %d)", rank, P);
   const int64_t B = q->shape[0], nq = q->shape[1], hq = q->shape[2], d = q->shape[3];
   const int64_t N = k->shape[1];
-  if (N % P != 0)
-    return fail(RA_E_SHAPE, "sequence length %lld is not divisible by P = %d (no implicit padding)", (long long)N, P);
-  const int64_t nb = N / P;
-  if (nq != nb) return fail(RA_E_SHAPE, "local query block has %lld rows, expected N/P = %lld", (long long)nq, (long long)nb);
+  const int64_t parts = zigzag ? 2 * (int64_t)P : P;
+  if (N % parts != 0)
+    return fail(RA_E_SHAPE, "sequence length %lld is not divisible by %s = %lld (no implicit padding)",
+                (long long)N, zigzag ? "2P" : "P", (long long)parts);
+  const int64_t nb = N / parts;  // block (contiguous) or chunk (zigzag) length
+  const int64_t rows = zigzag ? 2 * nb : nb;
+  if (nq != rows)
+    return fail(RA_E_SHAPE, "local query block has %lld rows, expected %s = %lld", (long long)nq,
+                zigzag ? "2 N/(2P)" : "N/P", (long long)rows);
   if ((e = check_out(opts->o_out, q, "o_out"))) return e;
   if (opts->lse_out && (e = check_rows(opts->lse_out, "lse_out", B, hq, nq))) return e;
   const int64_t bm = q->dtype == RA_BF16 ? RA_BF16_BM : RA_F32_BM;
-  if ((e = check_grid(nq, bm, hq, B))) return e;
+  if ((e = check_grid(zigzag ? 2 * ((nb + bm - 1) / bm) * bm : nq, bm, hq, B))) return e;
   if (B == 0 || nq == 0) return ok();
 
   RaAttnArgs a{};
@@ -262,14 +273,29 @@ int ra_rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, in
   a.v = v->data; set_bshd(v, a.v_sb, a.v_ss, a.v_sh);
   a.B = (int32_t)B; a.Hq = (int32_t)hq; a.Hkv = (int32_t)k->shape[2]; a.nq = (int32_t)nq;
   a.nkv = nb; a.q_off = (int64_t)rank * nb; a.kv_off = 0;
-  a.ring = 1; a.P = P; a.rank = rank; a.causal = causal ? 1 : 0;
+  a.ring = 1; a.P = (int32_t)parts; a.rank = rank; a.causal = causal ? 1 : 0;
+  a.nsplit = 1;
+  if (zigzag) {
+    a.nsplit = 2; a.qc = nb;
+    a.rank2 = (int32_t)(parts - 1 - rank); a.q_off2 = (parts - 1 - rank) * nb;
+  }
   a.c = resolve_scale(opts, d) * 1.4426950408889634f;
   a.state_in = 0; a.out_state = 0;
   a.o = opts->o_out->data; set_bshd(opts->o_out, a.o_sb, a.o_ss, a.o_sh); a.o_bf16 = opts->o_out->dtype == RA_BF16;
   if (opts->lse_out) { a.lse = (float*)opts->lse_out->data; set_rows(opts->lse_out, a.lse_sb, a.lse_sh, a.lse_ss); }
   hipStream_t st = stream_of(opts);
   return launched(q->dtype == RA_BF16 ? ra_launch_attn_bf16(a, (int)d, st) : ra_launch_attn_f32(a, (int)d, st),
-                  "ra_rank_share launch");
+                  zigzag ? "ra_rank_share_zigzag launch" : "ra_rank_share launch");
+}
+
+int ra_rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
+                  const ra_opts* opts) {
+  return rank_share(q, k, v, P, rank, causal, opts, 0);
+}
+
+int ra_rank_share_zigzag(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
+                         const ra_opts* opts) {
+  return rank_share(q, k, v, P, rank, causal, opts, 1);
 }
 
 int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s) {
@@ -314,6 +340,19 @@ double ra_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq,
     const int c = ra_plan_class(rank * nb, nb, ra_plan_ring_block(P, rank, s) * nb, nb, causal);
     f += c == RA_CLASS_FULL ? unit : (c == RA_CLASS_PARTIAL ? 0.5 * unit : 0.0);
   }
+  return f;
+}
+
+double ra_share_flops_zigzag(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d, int causal) {
+  if (P < 1 || N % (2 * P) != 0 || rank < 0 || rank >= P) return -1.0;
+  const int64_t c = N / (2 * P), chunks = 2 * P;
+  const double unit = 4.0 * (double)d * (double)hq * (double)c * (double)c * (double)B;
+  double f = 0.0;
+  for (const int64_t qa : {(int64_t)rank, chunks - 1 - rank})
+    for (int64_t t = 0; t < chunks; ++t) {
+      const int cl = ra_plan_class(qa * c, c, t * c, c, causal);
+      f += cl == RA_CLASS_FULL ? unit : (cl == RA_CLASS_PARTIAL ? 0.5 * unit : 0.0);
+    }
   return f;
 }
 

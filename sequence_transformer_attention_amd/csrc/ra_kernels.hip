@@ -129,18 +129,24 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep per-wave values in SGPRs
   const int lr = lane & 31, lg = lane >> 5;
 
-  const int nqt = (a.nq + BM - 1) / BM;
+  // query tiles: nqt_c per chunk of nqc rows (one chunk unless the share is split)
+  const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
+  const int nqt_c = (nqc + BM - 1) / BM;
+  const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   int qt = logical % nqt;
   const int hb = logical / nqt;
   const int h = hb % a.Hq, b = hb / a.Hq;
   if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
   const int hk = h / (a.Hq / a.Hkv);
+  const int chunk = qt / nqt_c;
+  const int64_t qpos0 = chunk ? a.q_off2 : a.q_off;  // global position of the chunk's first row
+  const int rank_e = chunk ? a.rank2 : a.rank;        // its ring order
 
-  const int qrow_wg = qt * BM;
+  const int qrow_wg = (qt - chunk * nqt_c) * BM;      // rows within the chunk
   const int qrow_w = qrow_wg + wave * 32;
-  const int my_q = qrow_w + lr;
-  const bool q_ok = my_q < a.nq;
+  const int my_q = chunk * nqc + qrow_w + lr;         // local row (q, o, lse, state)
+  const bool q_ok = qrow_w + lr < nqc;
 
   // Q fragment (B operand of S^T = K Q^T): lane holds Q[my_q][16c + 8lg .. +7].
   bf16x8 qf[KC];
@@ -177,8 +183,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     lsum = lg == 0 ? lv : 0.f;
   }
 
-  const int64_t q0_wg = a.q_off + qrow_wg;
-  const int nq_wg = min(BM, a.nq - qrow_wg);
+  const int64_t q0_wg = qpos0 + qrow_wg;
+  const int nq_wg = min(BM, nqc - qrow_wg);
   const int nsteps = a.ring ? a.P : 1;
   // Key position (ring mode: also first row in k/v) of the block folded at
   // loop step s.  The blocks arrive in ring order (block (rank - s) mod P at
@@ -188,7 +194,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // per query tile and would spread them apart), which keeps the K/V stream
   // they share in L2.  The merge is order-independent: only rounding changes.
   auto step_kv_off = [&](int s) -> int64_t {
-    return a.ring ? (int64_t)ra_plan_ring_block32(a.P, a.rank, (s + 1) % a.P) * a.nkv : a.kv_off;
+    return a.ring ? (int64_t)ra_plan_ring_block32(a.P, rank_e, (s + 1) % a.P) * a.nkv : a.kv_off;
   };
   auto step_tiles = [&](int s) -> int {
     return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
@@ -292,7 +298,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
 
   if (n > 0) {  // workgroup-uniform
     const int64_t roff = a.ring ? 0 : a.kv_off;  // key position - row in k/v
-    const int64_t q0w = a.q_off + qrow_w;        // the wave's first query position
+    const int64_t q0w = qpos0 + qrow_w;          // the wave's first query position
     const int64_t kstep = (int64_t)BN * a.k_ss * 2, vstep = (int64_t)BN * a.v_ss * 2;
     // Cursor over the tiles: loop step cs, tile cu of its cnt tiles, the
     // tile's key position relative to the wave's first query (saturated at
@@ -421,7 +427,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // cut at the query's own position under causal masking, 0 for SKIP (no
     // visible key for these rows: p = 0).  The key index of register r is
     // 8 (r / 4) + (r % 4) + 4 lg.
-    const int nqw = min(32, a.nq - qrow_w);
+    const int nqw = min(32, nqc - qrow_w);
     auto sm_mask = [&](int x, int64_t k0, int nvalid) __attribute__((always_inline)) {
       // every key valid and, under causal masking, at or before the wave's
       // first query: nothing to mask (rows past nq are never stored)
@@ -720,13 +726,19 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int tid = threadIdx.x;
-  const int nqt = (a.nq + BM - 1) / BM;
-  int qt = blockIdx.x % nqt;
+  const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;  // rows per chunk
+  const int nqt_c = (nqc + BM - 1) / BM;
+  const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
+  const int qt = blockIdx.x % nqt;
   const int hb = blockIdx.x / nqt;
   const int h = hb % a.Hq, b = hb / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
-  const int my_q = qt * BM + tid;
-  const bool q_ok = my_q < a.nq;
+  const int chunk = qt / nqt_c;
+  const int64_t qpos0 = chunk ? a.q_off2 : a.q_off;
+  const int rank_e = chunk ? a.rank2 : a.rank;
+  const int qrow = (qt - chunk * nqt_c) * BM + tid;  // row within the chunk
+  const int my_q = chunk * nqc + qrow;
+  const bool q_ok = qrow < nqc;
 
   float q[D], o[D];
   {
@@ -752,11 +764,11 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
     lsum = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q * a.l_ss];
   }
 
-  const int64_t q0_wg = a.q_off + (int64_t)qt * BM;
-  const int nq_wg = min(BM, a.nq - qt * BM);
+  const int64_t q0_wg = qpos0 + (qrow - tid);
+  const int nq_wg = min(BM, nqc - (qrow - tid));
   const int nsteps = a.ring ? a.P : 1;
   for (int s = 0; s < nsteps; ++s) {
-    const int64_t jb = a.ring ? ra_plan_ring_block(a.P, a.rank, s) : 0;
+    const int64_t jb = a.ring ? ra_plan_ring_block(a.P, rank_e, s) : 0;
     const int64_t kv_off = a.ring ? jb * a.nkv : a.kv_off;
     const int64_t row0 = a.ring ? jb * a.nkv : 0;
     const int nt = (int)ra_plan_key_tiles(q0_wg, nq_wg, kv_off, a.nkv, a.causal, BN);
@@ -778,7 +790,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
       }
       __syncthreads();
       const int64_t k0 = kv_off + (int64_t)u * BN;
-      const int64_t qpos = a.q_off + my_q;
+      const int64_t qpos = qpos0 + qrow;
       float sc[BN];
       float mx = -INFINITY;
       for (int j = 0; j < BN; ++j) {
@@ -881,16 +893,14 @@ __global__ void __launch_bounds__(256) init_kernel(RaInitArgs a) {
 }  // namespace
 
 hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t st) {
-  const int nqt = (a.nq + RA_BF16_BM - 1) / RA_BF16_BM;
-  const dim3 grid((unsigned)((int64_t)nqt * a.Hq * a.B)), block(512);
+  const dim3 grid((unsigned)(ra_query_tiles(a, RA_BF16_BM) * a.Hq * a.B)), block(512);
   if (d == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t ra_launch_attn_f32(const RaAttnArgs& a, int d, hipStream_t st) {
-  const int nqt = (a.nq + RA_F32_BM - 1) / RA_F32_BM;
-  const dim3 grid((unsigned)((int64_t)nqt * a.Hq * a.B)), block(64);
+  const dim3 grid((unsigned)(ra_query_tiles(a, RA_F32_BM) * a.Hq * a.B)), block(64);
   if (d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, block, 0, st, a);
   return hipGetLastError();

@@ -7,6 +7,11 @@
 //   ring == 0: one step, keys at global kv_off.., k/v point at the block.
 //   ring == 1: P steps in ring order from `rank`; k/v point at the whole
 //              sequence [B, P*nkv, Hkv, d]; q_off = rank * nkv.
+//   nsplit:    2 = the local rows are two chunks of qc rows: rows [0, qc)
+//              at global positions q_off.. (ring order from rank), rows
+//              [qc, 2 qc) at q_off2.. (ring order from rank2); otherwise one
+//              block of nq rows at q_off.. .  Query tiles never straddle the
+//              chunks.
 //   state_in:  1 = start from (oacc, m, l); 0 = start from the empty state.
 //   out_state: 1 = write (oacc, m, l) back; 0 = write normalised o (+ lse).
 struct RaAttnArgs {
@@ -24,6 +29,7 @@ struct RaAttnArgs {
   float* l; int64_t l_sb, l_sh, l_ss;
   void* o; int64_t o_sb, o_ss, o_sh; int32_t o_bf16;
   float* lse; int64_t lse_sb, lse_sh, lse_ss;
+  int32_t nsplit, rank2; int64_t qc, q_off2;
 };
 
 // O = oacc / l (to o, bf16 or fp32, or in place), LSE = m + ln l (optional).
@@ -47,6 +53,12 @@ struct RaInitArgs {
 // Tile shape of the attention kernels (query rows per workgroup, keys per tile).
 constexpr int RA_BF16_BM = 256, RA_BF16_BN = 64;
 constexpr int RA_F32_BM = 64, RA_F32_BN = 64;
+
+// Query tiles of a launch: per chunk ceil(rows / BM), times the chunk count.
+inline int64_t ra_query_tiles(const RaAttnArgs& a, int bm) {
+  const int64_t rows = a.nsplit == 2 ? a.qc : a.nq;
+  return (a.nsplit == 2 ? 2 : 1) * ((rows + bm - 1) / bm);
+}
 
 hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t s);
 hipError_t ra_launch_attn_f32(const RaAttnArgs& a, int d, hipStream_t s);

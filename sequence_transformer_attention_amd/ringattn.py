@@ -67,7 +67,8 @@ def lib() -> ctypes.CDLL:
     L.ra_step.argtypes = [T, T, T, T, T, T, i64, i64, ctypes.c_int, O]
     L.ra_finalize.argtypes = [T, T, O]
     L.ra_rank_share.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
-    for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share):
+    L.ra_rank_share_zigzag.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
+    for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share, L.ra_rank_share_zigzag):
         f.restype = ctypes.c_int
     L.ra_ring_block.argtypes = [i64, i64, i64]
     L.ra_ring_block.restype = i64
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.ra_tile_shape.restype = ctypes.c_int
     L.ra_share_flops.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.ra_share_flops.restype = ctypes.c_double
+    L.ra_share_flops_zigzag.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    L.ra_share_flops_zigzag.restype = ctypes.c_double
     L.ra_last_error.argtypes = []
     L.ra_last_error.restype = ctypes.c_char_p
     L.ra_version.argtypes = []
@@ -169,6 +172,15 @@ def ra_rank_share(q, k, v, P: int, rank: int, causal: bool, o_out, lse_out=None,
                                ctypes.byref(opts)))
 
 
+def ra_rank_share_zigzag(q, k, v, P: int, rank: int, causal: bool, o_out, lse_out=None,
+                         scale: Optional[float] = None, stream=None) -> None:
+    """One rank's load-balanced share (local rows = chunks rank and 2P-1-rank of
+    2P) in one launch: O -> o_out, LSE -> lse_out."""
+    opts, keep = _opts(stream, scale, o_out=o_out, lse_out=lse_out)
+    _check(lib().ra_rank_share_zigzag(_desc(q), _desc(k), _desc(v), int(P), int(rank), int(bool(causal)),
+                                      ctypes.byref(opts)))
+
+
 def ra_ring_block(P: int, rank: int, s: int) -> int:
     return int(lib().ra_ring_block(P, rank, s))
 
@@ -194,6 +206,10 @@ def ra_tile_shape(dtype: torch.dtype, d: int):
 
 def ra_share_flops(B: int, N: int, P: int, rank: int, Hq: int, d: int, causal: bool) -> float:
     return float(lib().ra_share_flops(B, N, P, rank, Hq, d, int(bool(causal))))
+
+
+def ra_share_flops_zigzag(B: int, N: int, P: int, rank: int, Hq: int, d: int, causal: bool) -> float:
+    return float(lib().ra_share_flops_zigzag(B, N, P, rank, Hq, d, int(bool(causal))))
 
 
 def ra_last_error() -> str:

@@ -75,3 +75,20 @@ def stepwise_gpu(q, k, v, P, rank, causal, o_dtype=torch.float32, scale=None, or
     lse = torch.full((B, hq, nq), float("nan"), dtype=torch.float32, device=dev)
     ra.ra_finalize(oacc, l, m=m, o_out=O, lse_out=lse)
     return O, lse
+
+
+def zigzag_rows(N: int, P: int, rank: int) -> torch.Tensor:
+    """Sequence rows of rank `rank`'s load-balanced share: chunks rank and
+    2P-1-rank of 2P (written out here, independently of both sides)."""
+    c = N // (2 * P)
+    return torch.cat([torch.arange(rank * c, (rank + 1) * c), torch.arange((2 * P - 1 - rank) * c, (2 * P - rank) * c)])
+
+
+def zigzag_gpu(q, k, v, P, rank, causal, o_dtype=torch.float32, scale=None):
+    """q = the rank's local rows (both chunks) on the device; returns (O, lse)."""
+    B, nq, hq, d = q.shape
+    O = torch.full((B, nq, hq, d), float("nan"), dtype=o_dtype, device=q.device)
+    lse = torch.full((B, hq, nq), float("nan"), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share_zigzag(q, k, v, P, rank, causal, O, lse, scale=scale)
+    return O, lse
+

@@ -147,6 +147,27 @@ def test_ra_rank_share_validation():
     assert share(T([1, 0, 4, 128]), T([1, 0, 1, 128]), T([1, 0, 1, 128]), 8, 7, o_out=T([1, 0, 4, 128])) == ra.RA_OK
 
 
+def test_ra_rank_share_zigzag_validation():
+    def zz(q, k, v, Pn, rank, o_out=None, lse=None):
+        opts = ra.RaOpts()
+        if o_out is not None:
+            opts.o_out = ctypes.pointer(o_out)
+        if lse is not None:
+            opts.lse_out = ctypes.pointer(lse)
+        return ra.lib().ra_rank_share_zigzag(P(q), P(k), P(v), Pn, rank, 1, ctypes.byref(opts))
+    q, k, v = T([1, 512, 4, 128]), T([1, 4096, 1, 128]), T([1, 4096, 1, 128])
+    o = T([1, 512, 4, 128])
+    assert zz(q, k, v, 8, 7) == ra.RA_E_NULL                      # no o_out
+    assert zz(q, k, v, 0, 0, o_out=o) == ra.RA_E_RANGE            # P < 1
+    assert zz(q, k, v, 8, 8, o_out=o) == ra.RA_E_RANGE            # rank outside [0, P)
+    k3, v3 = T([1, 4104, 1, 128]), T([1, 4104, 1, 128])         # divisible by P = 8, not by 2P
+    assert zz(T([1, 513, 4, 128]), k3, v3, 8, 7, o_out=T([1, 513, 4, 128])) == ra.RA_E_SHAPE
+    assert "2P" in ra.ra_last_error()
+    assert zz(q, k, v, 4, 3, o_out=o) == ra.RA_E_SHAPE            # Nq != 2 N/(2P)
+    assert zz(q, k, v, 8, 7, o_out=o, lse=rows(1, 4, 511)) == ra.RA_E_SHAPE
+    assert zz(T([1, 0, 4, 128]), T([1, 0, 1, 128]), T([1, 0, 1, 128]), 8, 7, o_out=T([1, 0, 4, 128])) == ra.RA_OK
+
+
 def test_ra_finalize_validation():
     L = ra.lib()
     oacc, l = T([1, 64, 2, 64], ra.RA_F32), rows(1, 2, 64)
@@ -210,6 +231,15 @@ def test_share_flops_match_oracle():
         for r in range(w.P):
             assert ra.ra_share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal) == \
                 oracle.share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal)
+
+
+def test_zigzag_share_flops_match_oracle():
+    for (B, N, P, H, d) in ((1, 32768, 8, 32, 128), (1, 131072, 16, 32, 128), (2, 1200, 3, 2, 64)):
+        for r in range(P):
+            for causal in (False, True):
+                assert ra.ra_share_flops_zigzag(B, N, P, r, H, d, causal) == \
+                    oracle.share_flops_zigzag(B, N, P, r, H, d, causal)
+    assert ra.ra_share_flops_zigzag(1, 100, 8, 0, 1, 64, True) == -1.0   # N % 2P != 0
 
 
 def test_tile_shape():

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
-from tests.gpu_util import assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu
+from tests.gpu_util import (assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu, zigzag_gpu,
+                            zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,3 +37,24 @@ def test_full_size_sampled_rows(w):
     assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"{w.name} fused bf16 O", out_bf16=True)
     assert_close(*gather(O32, lse32, rows), o_ref, l_ref, "bf16", f"{w.name} fused fp32 O")
     assert_close(*gather(Os, lses, rows), o_ref, l_ref, "bf16", f"{w.name} stepwise")
+
+
+def test_full_size_zigzag_sampled_rows():
+    """Load-balanced shares of the rank-7-of-8 shape (N 32768, 32 heads, d 128),
+    first and last rank, bf16 O as timed."""
+    w = workloads.RANK7_BF16
+    say("zigzag full size: drawing inputs (whole-sequence Q)")
+    x = inputs.draw_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.d, w.seed + 100, w.dtype, w.dist)
+    k, v = x["k"].to("cuda"), x["v"].to("cuda")
+    for r in (0, w.P - 1):
+        pos = zigzag_rows(w.N, w.P, r)
+        ql = x["q"][:, pos].contiguous()
+        say(f"zigzag full size rank {r}")
+        O, lse = zigzag_gpu(ql.to("cuda"), k, v, w.P, r, w.causal, torch.bfloat16)
+        torch.cuda.synchronize()
+        rows = inputs.sample_rows(w.B, w.Hq, len(pos), w.seed + r).numpy()
+        say(f"zigzag full size rank {r}: oracle on {len(rows)} rows")
+        o_ref, l_ref = oracle.rank_share_zigzag(ql, x["k"], x["v"], w.P, r, w.causal, rows=rows,
+                                                nthreads=oracle_threads())
+        assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"zigzag rank {r} bf16 O", out_bf16=True)
+

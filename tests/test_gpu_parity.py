@@ -12,7 +12,8 @@ import torch
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from sequence_transformer_attention_amd import ringattn as ra
-from tests.gpu_util import assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu
+from tests.gpu_util import (assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu, zigzag_gpu,
+                            zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +101,47 @@ def test_shrunken_bf16_workloads_all_rows(w):
     Os, lses = stepwise_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal)
     torch.cuda.synchronize()
     assert_close(*gather(Os, lses, rows), o_ref, l_ref, "bf16", f"{w.name} stepwise")
+
+
+# -------------------------------------------------- load-balanced (zigzag) share
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal,ranks", [
+    (1, 4096, 4, 2, 1, 128, True, (0, 3)),     # chunks of 512 rows: two full bf16 query tiles each
+    (2, 1200, 3, 2, 2, 64, True, (0, 1, 2)),   # chunks of 200: ragged query and key tiles, B = 2
+    (1, 2048, 2, 4, 2, 128, False, (1,)),      # no mask, GQA
+    (1, 192, 3, 1, 1, 64, True, (2,)),         # chunks of 32 rows
+])
+def test_zigzag_share(dt, B, N, P, Hq, Hkv, d, causal, ranks):
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=N + P, dtype=dt)
+    dv = _dev(x)
+    for r in ranks:
+        pos = zigzag_rows(N, P, r)
+        ql = x["q"][:, pos].contiguous()
+        say(f"zigzag {dt} B{B} N{N} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+        O, lse = zigzag_gpu(ql.to(DEV), dv["k"], dv["v"], P, r, causal)
+        torch.cuda.synchronize()
+        rows = oracle.all_rows(B, Hq, len(pos))
+        o_ref, l_ref = oracle.rank_share_zigzag(ql, x["k"], x["v"], P, r, causal, rows=rows,
+                                                nthreads=oracle_threads())
+        assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"zigzag rank {r}")
+
+
+def test_zigzag_shares_reassemble_full_attention():
+    """All ranks' load-balanced shares, put back in sequence order, give the
+    same result as the one-rank share over the whole sequence (P = 1)."""
+    B, N, P, H, d = 1, 2048, 4, 2, 128
+    x = _dev(inputs.draw_qkv(B, N, N, H, H, d, seed=77))
+    full, full_lse = rank_share_gpu(x["q"], x["k"], x["v"], 1, 0, True)
+    got = torch.empty_like(full)
+    got_lse = torch.empty_like(full_lse)
+    for r in range(P):
+        pos = zigzag_rows(N, P, r).to(DEV)
+        O, lse = zigzag_gpu(x["q"][:, pos].contiguous(), x["k"], x["v"], P, r, True)
+        got[:, pos] = O
+        got_lse[:, :, pos] = lse
+    torch.cuda.synchronize()
+    say(f"zigzag reassembled: max|dO| {float((got - full).abs().max()):.3e}")
+    assert float((got - full).abs().max()) <= 1e-2 and float((got_lse - full_lse).abs().max()) <= 1e-3
 
 
 # ------------------------------------------------------------------ edge cases

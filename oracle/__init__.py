@@ -66,6 +66,10 @@ def _load(path: Optional[str] = None):
     lib.orc_rank_share_zigzag.restype = ctypes.c_int
     lib.orc_share_flops_zigzag.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
     lib.orc_share_flops_zigzag.restype = ctypes.c_double
+    lib.orc_rank_share_bwd.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       ctypes.c_int, ctypes.c_double, _ip, _i64, _ip, _i64, _dp, _dp, _dp,
+                                       ctypes.c_int]
+    lib.orc_rank_share_bwd.restype = ctypes.c_int
     lib.orc_ring_block.argtypes = [_i64, _i64, _i64]
     lib.orc_ring_block.restype = _i64
     lib.orc_classify.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
@@ -232,6 +236,29 @@ def zigzag_positions(N: int, P: int, rank: int) -> np.ndarray:
     """Global positions of the local rows of the load-balanced share."""
     c = N // (2 * P)
     return np.concatenate([rank * c + np.arange(c), (2 * P - 1 - rank) * c + np.arange(c)])
+
+
+def rank_share_bwd(q, k, v, dout, P: int, rank: int, causal: bool, scale: Optional[float] = None,
+                   qrows=None, krows=None, nthreads: Optional[int] = None):
+    """Gradients of one rank's share for the upstream gradient dout [B, N/P, Hq, d]:
+    dQ of the listed (b, h, i) local rows [n, d] (default all), and this rank's
+    contribution dK, dV to the listed (b, g, j) key rows [m, d] (default all)."""
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, nq, hq, d = q.shape
+    N, hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    qr = _rows(qrows, B, hq, nq)
+    kr = np.ascontiguousarray(all_rows(B, hkv, N) if krows is None else np.asarray(krows, dtype=np.int64))
+    nq_r, nk_r = qr.shape[0], kr.shape[0]
+    dq = np.zeros((max(nq_r, 1), d)); dk = np.zeros((max(nk_r, 1), d)); dv = np.zeros((max(nk_r, 1), d))
+    e = lib.orc_rank_share_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, P, rank, hq, hkv, d, int(causal),
+                               float(scale), qr.ctypes.data_as(_ip), nq_r, kr.ctypes.data_as(_ip), nk_r,
+                               _ptr(dq), _ptr(dk), _ptr(dv), nthreads or default_threads())
+    if e:
+        raise ValueError(f"orc_rank_share_bwd failed ({e})")
+    return dq[:nq_r], dk[:nk_r], dv[:nk_r]
 
 
 def ring_block(P: int, rank: int, s: int) -> int:

@@ -397,3 +397,222 @@ double orc_share_flops_zigzag(int64_t B, int64_t N, int64_t P, int64_t rank, int
     }
     return f;
 }
+
+/* ---------------------------------------------------------------- backward
+ *
+ * Gradients of one rank's share ("Implementation Considerations / Gradient
+ * Synchronization": the backward pass uses the same communication pattern as
+ * the forward pass, so the ring visits the same blocks).  With the share's
+ * forward P_ij = exp(s_ij - LSE_i) over the visible keys, s_ij = scale
+ * <q_i, k_j>, O_i = sum_j P_ij v_j and an upstream gradient dO_i, the chain
+ * rule through the softmax gives (the plain definition, written out):
+ *   D_i   = <dO_i, O_i>
+ *   dP_ij = <dO_i, v_j>,   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i
+ * dQ rows sum over every visible key, block by block in ring order; dK and
+ * dV rows are this rank's contribution (its local queries, all query heads
+ * of the kv head) to key j, which the ring would carry back to its owner.
+ *
+ * Layout: q, dout [B, N/P, Hq, d]; k, v [B, N, Hkv, d]; contiguous fp64.
+ * qrows: (b, h, i) triples of dQ rows, dq[r*d + c]; krows: (b, g, j)
+ * triples (j a row of k/v, g a kv head) of dK/dV rows, dk/dv[r*d + c]. */
+
+typedef struct {
+    const double *q, *k, *v, *dout;
+    int64_t B, N, P, rank, nb, hq, hkv, d;
+    int causal;
+    double scale;
+} orc_bwd;
+
+static int bwd_visible(const orc_bwd *w, int64_t i, int64_t j)
+{
+    return !w->causal || j <= w->rank * w->nb + i;
+}
+
+static double bwd_dot(const double *a, const double *b, int64_t d)
+{
+    double s = 0.0;
+    for (int64_t c = 0; c < d; ++c) s += a[c] * b[c];
+    return s;
+}
+
+/* LSE_i and D_i of local query row (b, h, i): the forward by definition over
+ * all visible keys (block by block in ring order), then D = <dO, O>.
+ * o is scratch of d doubles, s of N doubles. */
+static void bwd_row_stats(const orc_bwd *w, int64_t b, int64_t h, int64_t i, double *s, double *o,
+                          double *lse_out, double *D_out)
+{
+    const int64_t d = w->d, g = h / (w->hq / w->hkv);
+    const double *qi = w->q + ((b * w->nb + i) * w->hq + h) * d;
+    double m = -INFINITY;
+    for (int64_t st = 0; st < w->P; ++st) {
+        const int64_t blk = orc_ring_block(w->P, w->rank, st);
+        for (int64_t j = blk * w->nb; j < (blk + 1) * w->nb; ++j) {
+            if (!bwd_visible(w, i, j)) continue;
+            s[j] = w->scale * bwd_dot(qi, w->k + ((b * w->N + j) * w->hkv + g) * d, d);
+            if (s[j] > m) m = s[j];
+        }
+    }
+    double l = 0.0;
+    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < w->N; ++j) {
+        if (!bwd_visible(w, i, j)) continue;
+        const double e = exp(s[j] - m);
+        const double *vj = w->v + ((b * w->N + j) * w->hkv + g) * d;
+        l += e;
+        for (int64_t c = 0; c < d; ++c) o[c] += e * vj[c];
+    }
+    const double lse = m + log(l);
+    for (int64_t c = 0; c < d; ++c) o[c] /= l;
+    *lse_out = lse;
+    *D_out = bwd_dot(w->dout + ((b * w->nb + i) * w->hq + h) * d, o, d);
+}
+
+typedef struct {
+    const orc_bwd *w;
+    int kind;                 /* 0: stats of all rows of listed heads; 1: dQ rows; 2: dK/dV rows */
+    const int64_t *rows;
+    int64_t r0, r1;
+    const double *lse, *D;    /* kind 2: per (head slot, i) */
+    const int64_t *slot;      /* kind 2: head slot of (b, h), or -1 */
+    double *out0, *out1;
+    int err;
+} orc_bwd_job;
+
+static void *bwd_run(void *arg)
+{
+    orc_bwd_job *J = (orc_bwd_job *)arg;
+    const orc_bwd *w = J->w;
+    const int64_t d = w->d, G = w->hq / w->hkv;
+    double *s = malloc(sizeof(double) * (size_t)(w->N > 0 ? w->N : 1));
+    double *o = malloc(sizeof(double) * (size_t)d);
+    if (!s || !o) { J->err = 1; free(s); free(o); return NULL; }
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        if (J->kind == 0) {            /* rows = (b, h) heads: all local rows of each */
+            const int64_t b = J->rows[2 * (r / w->nb)], h = J->rows[2 * (r / w->nb) + 1], i = r % w->nb;
+            bwd_row_stats(w, b, h, i, s, o, &J->out0[r], &J->out1[r]);
+        } else if (J->kind == 1) {     /* dQ row (b, h, i) */
+            const int64_t b = J->rows[3 * r], h = J->rows[3 * r + 1], i = J->rows[3 * r + 2];
+            const int64_t g = h / G;
+            double lse, D;
+            bwd_row_stats(w, b, h, i, s, o, &lse, &D);
+            const double *doi = w->dout + ((b * w->nb + i) * w->hq + h) * d;
+            double *dq = J->out0 + r * d;
+            for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
+            for (int64_t st = 0; st < w->P; ++st) {
+                const int64_t blk = orc_ring_block(w->P, w->rank, st);
+                for (int64_t j = blk * w->nb; j < (blk + 1) * w->nb; ++j) {
+                    if (!bwd_visible(w, i, j)) continue;
+                    const double *kj = w->k + ((b * w->N + j) * w->hkv + g) * d;
+                    const double p = exp(s[j] - lse);
+                    const double dp = bwd_dot(doi, w->v + ((b * w->N + j) * w->hkv + g) * d, d);
+                    const double ds = p * (dp - D);
+                    for (int64_t c = 0; c < d; ++c) dq[c] += w->scale * ds * kj[c];
+                }
+            }
+        } else {                       /* dK, dV row (b, g, j) */
+            const int64_t b = J->rows[3 * r], g = J->rows[3 * r + 1], j = J->rows[3 * r + 2];
+            const double *kj = w->k + ((b * w->N + j) * w->hkv + g) * d;
+            const double *vj = w->v + ((b * w->N + j) * w->hkv + g) * d;
+            double *dk = J->out0 + r * d, *dv = J->out1 + r * d;
+            for (int64_t c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+            for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                const int64_t sl = J->slot[b * w->hq + h];
+                for (int64_t i = 0; i < w->nb; ++i) {
+                    if (!bwd_visible(w, i, j)) continue;
+                    const double *qi = w->q + ((b * w->nb + i) * w->hq + h) * d;
+                    const double *doi = w->dout + ((b * w->nb + i) * w->hq + h) * d;
+                    const double p = exp(w->scale * bwd_dot(qi, kj, d) - J->lse[sl * w->nb + i]);
+                    const double ds = p * (bwd_dot(doi, vj, d) - J->D[sl * w->nb + i]);
+                    for (int64_t c = 0; c < d; ++c) {
+                        dk[c] += w->scale * ds * qi[c];
+                        dv[c] += p * doi[c];
+                    }
+                }
+            }
+        }
+    }
+    free(s); free(o);
+    return NULL;
+}
+
+static int bwd_threads(orc_bwd_job proto, int64_t n, int nthreads)
+{
+    if (n <= 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > n) nthreads = (int)n;
+    orc_bwd_job *jobs = calloc((size_t)nthreads, sizeof(orc_bwd_job));
+    pthread_t *tid = calloc((size_t)nthreads, sizeof(pthread_t));
+    int *joined = calloc((size_t)nthreads, sizeof(int));
+    if (!jobs || !tid || !joined) { free(jobs); free(tid); free(joined); return -8; }
+    const int64_t per = (n + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = proto;
+        jobs[t].r0 = t * per;
+        jobs[t].r1 = (t + 1) * per < n ? (t + 1) * per : n;
+        if (jobs[t].r0 >= jobs[t].r1) continue;
+        if (pthread_create(&tid[t], NULL, bwd_run, &jobs[t]) == 0) joined[t] = 1;
+        else bwd_run(&jobs[t]);
+    }
+    int err = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (joined[t]) pthread_join(tid[t], NULL);
+        if (jobs[t].err) err = -8;
+    }
+    free(jobs); free(tid); free(joined);
+    return err;
+}
+
+int orc_rank_share_bwd(const double *q, const double *k, const double *v, const double *dout,
+                       int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
+                       int causal, double scale,
+                       const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
+                       double *dq, double *dk, double *dv, int nthreads)
+{
+    if (P <= 0 || N % P != 0 || hkv <= 0 || hq % hkv != 0 || d <= 0) return -3;
+    if (rank < 0 || rank >= P) return -5;
+    const orc_bwd w = {q, k, v, dout, B, N, P, rank, N / P, hq, hkv, d, causal, scale};
+    const int64_t G = hq / hkv;
+    for (int64_t r = 0; r < nqrows; ++r)
+        if (qrows[3 * r] < 0 || qrows[3 * r] >= B || qrows[3 * r + 1] < 0 || qrows[3 * r + 1] >= hq ||
+            qrows[3 * r + 2] < 0 || qrows[3 * r + 2] >= w.nb) return -5;
+    for (int64_t r = 0; r < nkrows; ++r)
+        if (krows[3 * r] < 0 || krows[3 * r] >= B || krows[3 * r + 1] < 0 || krows[3 * r + 1] >= hkv ||
+            krows[3 * r + 2] < 0 || krows[3 * r + 2] >= N) return -5;
+    orc_bwd_job proto;
+    memset(&proto, 0, sizeof proto);
+    proto.w = &w;
+    int e = 0;
+    if (nqrows > 0) {
+        proto.kind = 1; proto.rows = qrows; proto.out0 = dq;
+        if ((e = bwd_threads(proto, nqrows, nthreads))) return e;
+    }
+    if (nkrows <= 0) return 0;
+    /* LSE and D of every local row of the query heads the listed kv rows need */
+    int64_t *slot = malloc(sizeof(int64_t) * (size_t)(B * hq));
+    int64_t *heads = malloc(sizeof(int64_t) * (size_t)(2 * B * hq));
+    if (!slot || !heads) { free(slot); free(heads); return -8; }
+    for (int64_t x = 0; x < B * hq; ++x) slot[x] = -1;
+    int64_t nh = 0;
+    for (int64_t r = 0; r < nkrows; ++r) {
+        const int64_t b = krows[3 * r], g = krows[3 * r + 1];
+        for (int64_t h = g * G; h < (g + 1) * G; ++h)
+            if (slot[b * hq + h] < 0) {
+                slot[b * hq + h] = nh;
+                heads[2 * nh] = b; heads[2 * nh + 1] = h;
+                ++nh;
+            }
+    }
+    double *lse = malloc(sizeof(double) * (size_t)(nh * w.nb + 1));
+    double *D = malloc(sizeof(double) * (size_t)(nh * w.nb + 1));
+    if (!lse || !D) { e = -8; goto done; }
+    proto.kind = 0; proto.rows = heads; proto.out0 = lse; proto.out1 = D;
+    if ((e = bwd_threads(proto, nh * w.nb, nthreads))) goto done;
+    proto.kind = 2; proto.rows = krows; proto.lse = lse; proto.D = D; proto.slot = slot;
+    proto.out0 = dk; proto.out1 = dv;
+    e = bwd_threads(proto, nkrows, nthreads);
+done:
+    free(slot); free(heads); free(lse); free(D);
+    return e;
+}

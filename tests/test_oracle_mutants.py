@@ -31,6 +31,11 @@ MUTANTS = {
     "zigzag_key_chunk": ("const int64_t chunks[2] = {j, 2 * P - 1 - j};", "const int64_t chunks[2] = {j, 2 * P - 2 - j};"),
     "zigzag_flops_key_chunk": ("const int64_t kpos[2] = {j * c, (2 * P - 1 - j) * c};",
                                "const int64_t kpos[2] = {j * c, (2 * P - 2 - j) * c};"),
+    "bwd_ds_sign": ("const double ds = p * (dp - D);", "const double ds = p * (D - dp);"),
+    "bwd_dk_scale_dropped": ("dk[c] += w->scale * ds * qi[c];", "dk[c] += ds * qi[c];"),
+    "bwd_dv_uses_ds": ("dv[c] += p * doi[c];", "dv[c] += ds * doi[c];"),
+    "bwd_D_from_q": ("*D_out = bwd_dot(w->dout + ((b * w->nb + i) * w->hq + h) * d, o, d);",
+                     "*D_out = bwd_dot(w->dout + ((b * w->nb + i) * w->hq + h) * d, qi, d);"),
     "pairs_count_off_by_one": ("int64_t c = causal ? q_off + i - kv_off + 1 : nkv;", "int64_t c = causal ? q_off + i - kv_off : nkv;"),
 }
 
@@ -48,6 +53,7 @@ PINS = [
     lambda: pins.test_share_flops_rule(),
     lambda: pins.test_zigzag_share_is_full_attention_at_its_positions(1, 48, 3, 2, 1, 8, True),
     lambda: pins.test_zigzag_flops_rule_and_balance(),
+    lambda: pins.test_backward_matches_torch_autograd(1, 24, 3, 2, 1, 8, True),
 ]
 
 

@@ -335,6 +335,82 @@ def test_zigzag_flops_rule_and_balance():
     assert oracle.share_flops_zigzag(1, 32768, 8, 0, 32, 128, True) == 1099511627776
 
 
+# ------------------------------------------------------------------ backward
+def _share_loss_autograd(q, k, v, dout, P, r, causal, scale):
+    """torch fp64 autograd through the share's forward (the local queries of
+    rank r against the whole sequence); returns dQ, dK, dV as [B, S, H, d]."""
+    B, N, Hq, d = q.shape[0], k.shape[1], q.shape[2], q.shape[3]
+    nb = N // P
+    ql = q[:, r * nb:(r + 1) * nb].clone().requires_grad_(True)
+    kk = k.clone().requires_grad_(True)
+    vv = v.clone().requires_grad_(True)
+    O, _ = _torch_attention(ql, kk, vv, r * nb, 0, causal, scale)
+    (O * dout).sum().backward()
+    return ql.grad, kk.grad, vv.grad
+
+
+@pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal", [
+    (1, 24, 3, 2, 1, 8, True),     # GQA
+    (2, 16, 2, 2, 2, 4, True),
+    (1, 18, 3, 1, 1, 8, False),
+])
+def test_backward_matches_torch_autograd(B, N, P, Hq, Hkv, d, causal):
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=N * P)
+    nb = N // P
+    g = torch.Generator().manual_seed(9)
+    for r in range(P):
+        dout = torch.randn(B, nb, Hq, d, generator=g, dtype=torch.float64)
+        dq_t, dk_t, dv_t = _share_loss_autograd(q, k, v, dout, P, r, causal, 0.4)
+        dq, dk, dv = oracle.rank_share_bwd(q[:, r * nb:(r + 1) * nb], k, v, dout, P, r, causal, 0.4)
+        np.testing.assert_allclose(_grid(dq, B, Hq, nb), dq_t.numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(_grid(dk, B, Hkv, N), dk_t.numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(_grid(dv, B, Hkv, N), dv_t.numpy(), atol=TOL, rtol=0)
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of L = <O, dO> computed with the (pinned) forward oracle."""
+    B, N, P, H, d, r, scale = 1, 6, 2, 1, 4, 1, 0.7
+    q, k, v = _rand(B, N, N, H, H, d, seed=21)
+    nb = N // P
+    dout = torch.randn(B, nb, H, d, generator=torch.Generator().manual_seed(4), dtype=torch.float64)
+    ql = q[:, r * nb:(r + 1) * nb].clone()
+
+    def loss(qx, kx, vx):
+        o, _ = oracle.rank_share(qx, kx, vx, P, r, True, scale)
+        return float((_grid(o, B, H, nb) * dout.numpy()).sum())
+
+    dq, dk, dv = oracle.rank_share_bwd(ql, k, v, dout, P, r, True, scale)
+    eps = 1e-5
+    for name, t, grad, rows in (("q", ql, dq, nb), ("k", k, dk, N), ("v", v, dv, N)):
+        gg = _grid(grad, B, H, rows)
+        for idx in itertools.product(range(B), range(rows), range(H), range(d)):
+            tp, tm = t.clone(), t.clone()
+            tp[idx] += eps
+            tm[idx] -= eps
+            args_p = {"q": (tp, k, v), "k": (ql, tp, v), "v": (ql, k, tp)}[name]
+            args_m = {"q": (tm, k, v), "k": (ql, tm, v), "v": (ql, k, tm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - gg[idx]) < 1e-8, (name, idx, fd, gg[idx])
+
+
+def test_backward_contributions_of_all_ranks_sum_to_full_attention():
+    """Each rank's dK, dV is its queries' contribution: summed over the ring
+    they equal the gradients of full attention over the whole sequence (P = 1)."""
+    B, N, P, Hq, Hkv, d = 1, 24, 4, 4, 2, 8
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=8)
+    dout = torch.randn(B, N, Hq, d, generator=torch.Generator().manual_seed(2), dtype=torch.float64)
+    nb = N // P
+    dk_sum = np.zeros((B * Hkv * N, d)); dv_sum = np.zeros_like(dk_sum)
+    for r in range(P):
+        _, dk, dv = oracle.rank_share_bwd(q[:, r * nb:(r + 1) * nb], k, v, dout[:, r * nb:(r + 1) * nb], P, r,
+                                          True, 0.3)
+        dk_sum += dk
+        dv_sum += dv
+    dq1, dk1, dv1 = oracle.rank_share_bwd(q, k, v, dout, 1, 0, True, 0.3)
+    np.testing.assert_allclose(dk_sum, dk1, atol=TOL, rtol=0)
+    np.testing.assert_allclose(dv_sum, dv1, atol=TOL, rtol=0)
+
+
 # ------------------------------------------------------------ input generator
 def test_inputs_are_deterministic_and_seeded():
     a = inputs.draw_qkv(1, 64, 128, 4, 2, 16, seed=7)

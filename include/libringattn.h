@@ -142,6 +142,29 @@ int ra_rank_share(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
 int ra_rank_share_zigzag(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                          int P, int rank, int causal, const ra_opts *opts);
 
+/* Backward of one rank's (contiguous) share (glossary page "sequence
+ * parallelism transformers", section "Implementation Considerations", item
+ * "Gradient Synchronization": the backward pass runs the same ring).  With
+ * the forward's P_ij = exp(s_ij - LSE_i) and dO the gradient arriving at O:
+ * D_i = <dO_i, O_i>, dS_ij = P_ij (<dO_i, v_j> - D_i), dQ_i = scale *
+ * sum_j dS_ij k_j, dK_j = scale * sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i.
+ *   q, o, dout: [B, N/P, Hq, d] bf16 (o and lse as ra_rank_share returned
+ *               them; dout the upstream gradient);
+ *   k, v:       [B, N, Hkv, d] bf16, the whole sequence;
+ *   lse:        [B, Hq, N/P] fp32;
+ *   dq:         [B, N/P, Hq, d] fp32, written;
+ *   dk, dv:     [B, N, Hkv, d] fp32, written: this rank's contribution for
+ *               every key (zero for keys none of its queries sees), which
+ *               the ring would carry back to the key's owner;
+ *   delta:      [B, Hq, N/P] fp32 workspace owned by the caller (D_i).
+ * bf16 q/k/v only (RA_E_UNSUPPORTED otherwise); shapes and strides as for
+ * ra_rank_share.  Four launches on opts->stream. */
+int ra_rank_share_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                      const ra_tensor *o, const ra_tensor *lse, const ra_tensor *dout,
+                      int P, int rank, int causal,
+                      const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
+                      const ra_tensor *delta, const ra_opts *opts);
+
 /* ---- host-only queries (no GPU needed) --------------------------------- */
 
 /* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1. */

@@ -15,6 +15,7 @@
 
 #include <limits>
 
+#include "ra_bwd.h"
 #include "ra_launch.h"
 #include "ra_plan.h"
 
@@ -296,6 +297,49 @@ int ra_rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, in
 int ra_rank_share_zigzag(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
                          const ra_opts* opts) {
   return rank_share(q, k, v, P, rank, causal, opts, 1);
+}
+
+int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
+                      const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal, const ra_tensor* dq,
+                      const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta, const ra_opts* opts) {
+  int e = check_qkv(q, k, v, "k", "v");
+  if (e) return e;
+  if (q->dtype != RA_BF16) return fail(RA_E_UNSUPPORTED, "ra_rank_share_bwd takes bf16 q, k, v");
+  if (P < 1) return fail(RA_E_RANGE, "P must be >= 1 (got %d)", P);
+  if (rank < 0 || rank >= P) return fail(RA_E_RANGE, "rank %d outside [0, %d)", rank, P);
+  const int64_t B = q->shape[0], nq = q->shape[1], hq = q->shape[2], d = q->shape[3];
+  const int64_t N = k->shape[1];
+  if (N % P != 0)
+    return fail(RA_E_SHAPE, "sequence length %lld is not divisible by P = %d (no implicit padding)", (long long)N, P);
+  const int64_t nb = N / P;
+  if (nq != nb) return fail(RA_E_SHAPE, "local query block has %lld rows, expected N/P = %lld", (long long)nq, (long long)nb);
+  if ((e = check_out(o, q, "o")) || (e = check_out(dout, q, "dout")) || (e = check_out(dq, q, "dq"))) return e;
+  if (o->dtype != RA_BF16 || dout->dtype != RA_BF16) return fail(RA_E_DTYPE, "o and dout must be bf16");
+  if (dq->dtype != RA_F32) return fail(RA_E_DTYPE, "dq must be fp32");
+  if ((e = check_bshd(dk, "dk")) || (e = check_bshd(dv, "dv"))) return e;
+  if (!same_shape(dk, k) || !same_shape(dv, k)) return fail(RA_E_SHAPE, "dk and dv must have the shape of k");
+  if (dk->dtype != RA_F32 || dv->dtype != RA_F32) return fail(RA_E_DTYPE, "dk and dv must be fp32");
+  if ((e = check_rows(lse, "lse", B, hq, nq)) || (e = check_rows(delta, "delta", B, hq, nq))) return e;
+  if ((e = check_grid(nq, RA_BWD_BM, hq, B)) || (e = check_grid(N, RA_BWD_BM, k->shape[2], B))) return e;
+  if (B == 0 || nq == 0) return ok();
+
+  RaBwdArgs a{};
+  a.q = q->data; set_bshd(q, a.q_sb, a.q_ss, a.q_sh);
+  a.k = k->data; set_bshd(k, a.k_sb, a.k_ss, a.k_sh);
+  a.v = v->data; set_bshd(v, a.v_sb, a.v_ss, a.v_sh);
+  a.o = o->data; set_bshd(o, a.o_sb, a.o_ss, a.o_sh);
+  a.dout = dout->data; set_bshd(dout, a.do_sb, a.do_ss, a.do_sh);
+  a.lse = (const float*)lse->data; set_rows(lse, a.lse_sb, a.lse_sh, a.lse_ss);
+  a.delta = (float*)delta->data; set_rows(delta, a.de_sb, a.de_sh, a.de_ss);
+  a.dq = (float*)dq->data; set_bshd(dq, a.dq_sb, a.dq_ss, a.dq_sh);
+  a.dk = (float*)dk->data; set_bshd(dk, a.dk_sb, a.dk_ss, a.dk_sh);
+  a.dv = (float*)dv->data; set_bshd(dv, a.dv_sb, a.dv_ss, a.dv_sh);
+  a.B = (int32_t)B; a.Hq = (int32_t)hq; a.Hkv = (int32_t)k->shape[2]; a.nq = (int32_t)nq;
+  a.N = N; a.nb = nb; a.q_off = (int64_t)rank * nb;
+  a.P = P; a.rank = rank; a.causal = causal ? 1 : 0;
+  a.scale = resolve_scale(opts, d);
+  a.c = a.scale * 1.4426950408889634f;
+  return launched(ra_launch_bwd(a, (int)d, stream_of(opts)), "ra_rank_share_bwd launch");
 }
 
 int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s) {

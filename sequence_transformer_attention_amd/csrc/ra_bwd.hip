@@ -1,0 +1,385 @@
+// ra_bwd.hip -- gfx950 kernels of the backward of one rank's share.
+//
+// What is computed (glossary page "sequence parallelism transformers",
+// section "Implementation Considerations", item "Gradient Synchronization":
+// the backward pass needs the same communication as the forward pass): the
+// gradients of the share's outputs O with respect to its local queries and,
+// for every key of the sequence, this rank's contribution to dK and dV (the
+// part the ring would carry back to the key's owner).  With the forward's
+// P_ij = exp(s_ij - LSE_i), s_ij = scale <q_i, k_j>, and dO the gradient
+// arriving at O:
+//   D_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - D_i)
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+//   dV_j = sum_i P_ij dO_i
+// P is recomputed from the saved LSE (no softmax state is kept).
+//
+// Kernels (bf16 inputs, fp32 accumulation, v_mfma_f32_32x32x16_bf16):
+//   bwd_prep_kernel   D_i, one thread per row.
+//   bwd_dq_kernel     4 waves x 32 query rows (Q and dO fragments stay in
+//                     registers as B operands); per 32-key unit of a
+//                     64-key K/V tile staged in LDS:
+//                       S^T = K Q^T, dP^T = V dO^T (A operands from LDS),
+//                       dS^T = P^T (dP^T - D) in fp32, then
+//                       dQ^T += K^T dS^T with K^T from the transposing
+//                       ds_read_b64_tr_b16 and dS^T from registers.
+//   bwd_dkdv_kernel   4 waves x 32 keys (K and V fragments stay in
+//                     registers as B operands); per 32-query unit of a
+//                     64-row Q/dO tile staged in LDS, for every query head
+//                     of the kv head:
+//                       S = Q K^T, dP = dO V^T (A operands from LDS),
+//                       P and dS in fp32 with LSE and D per query row, then
+//                       dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T
+//                       from transposing reads and P, dS from registers.
+// Both attention kernels use the forward's LDS layout (rows of 2d bytes,
+// 16-byte slots XOR-swizzled) and one-stage synchronous tile loads.
+#include "ra_bwd.h"
+#include "ra_plan.h"
+
+#include <type_traits>
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Physical 16-byte slot of logical slot p in LDS row r (the forward's swizzle:
+// conflict-free 128-bit reads of 16 rows at one slot and transposing reads).
+template <int SLOTS>
+__device__ __forceinline__ int swz(int r, int p) {
+  return p ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (SLOTS - 1));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Per-lane LDS addresses inside a 64-row tile (rows of 2D bytes):
+//   rd[c]:        128-bit read of row lr, logical slot 2c + lg (A operand of
+//                 a 32x32x16 MFMA: row lr, elements 16c + 8lg .. +7);
+//   tr[half][db]: transposing read, as the forward's V^T reads (A operand
+//                 of channel block db over 16 rows; + 2D * 16 hh per group).
+template <int D>
+struct TileAddr {
+  static constexpr int SLOTS = D / 8, KC = D / 16, DB = D / 32;
+  unsigned rd[KC], tr[2][DB];
+  __device__ __forceinline__ void init(unsigned base, int lane) {
+    const int lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) rd[c] = base + lr * 2 * D + 16 * swz<SLOTS>(lr, 2 * c + lg);
+    const int vj = lane & 15, ve = vj >> 2, vc = vj & 3, vgrp = lane >> 4;
+    const int vx = 2 * (vgrp & 1) + (vc >> 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int r = 4 * lg + ve + 8 * half;
+        tr[half][db] = base + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
+      }
+  }
+};
+
+// 128-bit A-operand reads of the 32-row unit at byte offset OFF, then a wait
+// that carries the registers (so no consumer is placed before it).
+template <int KC>
+__device__ __forceinline__ void read_rows(bf16x8 (&f)[KC], const unsigned (&rd)[KC], unsigned off) {
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    const unsigned ad = rd[c] + off;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(f[c]) : "v"(ad));
+  }
+  if constexpr (KC == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                 "+v"(f[6]), "+v"(f[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+}
+
+// Transposing A operand of channel block db, 16-row group at byte offset OFF.
+__device__ __forceinline__ bf16x8 read_tr(unsigned lo_addr, unsigned hi_addr, unsigned off) {
+  u32x2 lo, hi;
+  const unsigned a0 = lo_addr + off, a1 = hi_addr + off;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi));
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Load a 64-row tile (rows row0 .. row0 + nvalid - 1 of a [*, D] bf16 matrix
+// with row stride `stride` elements; rows past nvalid re-read the last one)
+// into LDS at dst, swizzled.  All NW waves take a share of 1 KiB chunks.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(const __bf16* row0, int64_t stride, int nvalid, char* dst, int wave,
+                                          int lane) {
+  constexpr int SLOTS = D / 8, TILE = 64 * D * 2, NL = TILE / 1024 / NW;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)row0, (short)0, (int)(unsigned)(64 * stride * 2), 0x00020000);
+  const int last = nvalid - 1;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int ls = (wave * NL + i) * 64 + lane;
+    const int r = ls / SLOTS;
+    const unsigned off = (unsigned)(r < last ? r : last) * (unsigned)stride * 2u + 16u * (unsigned)swz<SLOTS>(r, ls % SLOTS);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (wave * NL + i) * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// D_i = <dO_i, O_i> for every local row.
+__global__ void __launch_bounds__(256) bwd_prep_kernel(RaBwdArgs a, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.B * a.Hq * a.nq) return;
+  const int i = (int)(idx % a.nq);
+  const int64_t t = idx / a.nq;
+  const int h = (int)(t % a.Hq), b = (int)(t / a.Hq);
+  const __bf16* op = (const __bf16*)a.o + (int64_t)b * a.o_sb + (int64_t)i * a.o_ss + (int64_t)h * a.o_sh;
+  const __bf16* dp = (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)i * a.do_ss + (int64_t)h * a.do_sh;
+  float s = 0.f;
+  for (int c = 0; c < d; c += 8) {
+    const bf16x8 x = *(const bf16x8*)(op + c), y = *(const bf16x8*)(dp + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
+  }
+  a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)i * a.de_ss] = s;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
+  constexpr int NW = 4, BM = NW * 32, BN = RA_BWD_BN, KC = D / 16, DB = D / 32, TILE = BN * D * 2;
+  static_assert(BM == RA_BWD_BM, "query rows per workgroup");
+  __shared__ __attribute__((aligned(1024))) char smem[2][TILE];  // K tile, V tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int nqt = (a.nq + BM - 1) / BM;
+  const int qt = blockIdx.x % nqt, hb = blockIdx.x / nqt;
+  const int h = hb % a.Hq, b = hb / a.Hq, hk = h / (a.Hq / a.Hkv);
+  const int qrow_wg = qt * BM, qrow_w = qrow_wg + wave * 32, my_q = qrow_w + lr;
+  const bool q_ok = my_q < a.nq;
+
+  bf16x8 qf[KC], dof[KC];  // lane: row my_q, elements 16c + 8lg .. +7
+  {
+    const int row = q_ok ? my_q : 0;
+    const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)row * a.q_ss + (int64_t)h * a.q_sh + 8 * lg;
+    const __bf16* dp =
+        (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)row * a.do_ss + (int64_t)h * a.do_sh + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      qf[c] = q_ok ? *(const bf16x8*)(qp + 16 * c) : bf16x8{};
+      dof[c] = q_ok ? *(const bf16x8*)(dp + 16 * c) : bf16x8{};
+    }
+  }
+  // rows past nq: LSE = +inf gives P = 0
+  const float lse2 = q_ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)my_q * a.lse_ss] * kLog2e
+                          : INFINITY;
+  const float dlt = q_ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)my_q * a.de_ss] : 0.f;
+
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+  TileAddr<D> ta;
+  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]), lane);
+
+  const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
+  const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
+  const int64_t q0_wg = a.q_off + qrow_wg, q0w = a.q_off + qrow_w;
+  const int nq_wg = min(BM, a.nq - qrow_wg);
+  for (int s = 0; s < a.P; ++s) {
+    const int64_t kv0 = ra_plan_ring_block(a.P, a.rank, s) * a.nb;  // position = row
+    const int nt = (int)ra_plan_key_tiles(q0_wg, nq_wg, kv0, a.nb, a.causal, BN);
+    for (int u = 0; u < nt; ++u) {
+      const int64_t k0 = kv0 + (int64_t)u * BN;
+      const int64_t left = a.nb - (int64_t)u * BN;
+      const int nvalid = left < BN ? (int)left : BN;
+      __syncthreads();  // every wave is done with the previous tile
+      load_tile<D, NW>(kb + k0 * a.k_ss, a.k_ss, nvalid, &smem[0][0], wave, lane);
+      load_tile<D, NW>(vb + k0 * a.v_ss, a.v_ss, nvalid, &smem[1][0], wave, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      static_for<0, 2>([&](auto HF) {
+        constexpr int hf = decltype(HF)::value;
+        constexpr unsigned uo = (unsigned)hf * 64 * D;  // 32-row unit
+        // S^T = K Q^T (keys x queries)
+        bf16x8 fr[KC];
+        read_rows<KC>(fr, ta.rd, uo);
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], qf[c], sacc, 0, 0, 0);
+        // dP^T = V dO^T
+        read_rows<KC>(fr, ta.rd, TILE + uo);
+        f32x16 dpa = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], dof[c], dpa, 0, 0, 0);
+        // P^T and dS^T; key index of register r: 8 (r / 4) + (r % 4) + 4 lg
+        const int nv = min(max(nvalid - 32 * hf, 0), 32);
+        const int64_t vis = a.causal ? q0w + lr - (k0 + 32 * hf) + 1 : nv;  // keys below this index are visible
+        const int lim = (int)(vis < nv ? (vis > 0 ? vis : 0) : nv);
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + (r & 3) + 4 * lg;
+          const float p = kk < lim ? __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2) : 0.f;
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 kt = read_tr(ta.tr[0][db], ta.tr[1][db], uo + (unsigned)hh * 32 * D);
+            dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[hh], dqa[db], 0, 0, 0);
+          }
+      });
+    }
+  }
+  if (!q_ok) return;
+  float* dp = a.dq + (int64_t)b * a.dq_sb + (int64_t)my_q * a.dq_ss + (int64_t)h * a.dq_sh;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = {dqa[db][4 * j] * a.scale, dqa[db][4 * j + 1] * a.scale, dqa[db][4 * j + 2] * a.scale,
+                       dqa[db][4 * j + 3] * a.scale};
+      *(f32x4*)(dp + 32 * db + 8 * j + 4 * lg) = x;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
+  constexpr int NW = 4, BK = NW * 32, BN = RA_BWD_BN, KC = D / 16, DB = D / 32, TILE = BN * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2][TILE];  // Q tile, dO tile
+  __shared__ __attribute__((aligned(16))) float lsd[2][BN];      // LSE * log2(e), D of the tile's rows
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int nkt = (int)((a.N + BK - 1) / BK);
+  const int kt = blockIdx.x % nkt, hb = blockIdx.x / nkt;
+  const int g = hb % a.Hkv, b = hb / a.Hkv, G = a.Hq / a.Hkv;
+  const int64_t my_k = (int64_t)kt * BK + wave * 32 + lr;
+  const bool k_ok = my_k < a.N;
+
+  bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7
+  {
+    const int64_t row = k_ok ? my_k : 0;
+    const __bf16* kp = (const __bf16*)a.k + (int64_t)b * a.k_sb + row * a.k_ss + (int64_t)g * a.k_sh + 8 * lg;
+    const __bf16* vp = (const __bf16*)a.v + (int64_t)b * a.v_sb + row * a.v_ss + (int64_t)g * a.v_sh + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      kf[c] = k_ok ? *(const bf16x8*)(kp + 16 * c) : bf16x8{};
+      vf[c] = k_ok ? *(const bf16x8*)(vp + 16 * c) : bf16x8{};
+    }
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16{};
+  TileAddr<D> ta;
+  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]), lane);
+
+  // Local query rows that see any key of the workgroup: under causal
+  // masking those at positions >= the first key's.
+  const int64_t kfirst = (int64_t)kt * BK;
+  int64_t qlo = a.causal ? kfirst - a.q_off : 0;
+  qlo = qlo < 0 ? 0 : qlo;
+  const int t0 = qlo >= a.nq ? a.nq : (int)(qlo / BN);
+  const int ntq = (a.nq + BN - 1) / BN;
+  for (int hh_ = 0; hh_ < G; ++hh_) {
+    const int h = g * G + hh_;
+    const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+    const __bf16* db_ = (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh;
+    for (int t = t0; t < ntq; ++t) {
+      const int r0 = t * BN;
+      const int nvalid = min(BN, a.nq - r0);
+      __syncthreads();
+      load_tile<D, NW>(qb + (int64_t)r0 * a.q_ss, a.q_ss, nvalid, &smem[0][0], wave, lane);
+      load_tile<D, NW>(db_ + (int64_t)r0 * a.do_ss, a.do_ss, nvalid, &smem[1][0], wave, lane);
+      if (tid < BN) {
+        const int row = r0 + tid;
+        const bool ok = row < a.nq;
+        lsd[0][tid] = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e
+                         : INFINITY;
+        lsd[1][tid] = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      static_for<0, 2>([&](auto HF) {
+        constexpr int hf = decltype(HF)::value;
+        constexpr unsigned uo = (unsigned)hf * 64 * D;
+        // S = Q K^T (queries x keys); query row of register r: 8 (r / 4) + 4 lg + (r % 4)
+        bf16x8 fr[KC];
+        read_rows<KC>(fr, ta.rd, uo);
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], kf[c], sacc, 0, 0, 0);
+        read_rows<KC>(fr, ta.rd, TILE + uo);
+        f32x16 dpa = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], vf[c], dpa, 0, 0, 0);
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qr = 32 * hf + 8 * j + 4 * lg;  // first of 4 consecutive rows
+          const f32x4 l4 = *(const f32x4*)&lsd[0][qr];
+          const f32x4 d4 = *(const f32x4*)&lsd[1][qr];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            const int64_t qpos = a.q_off + r0 + qr + i;
+            const bool vis = k_ok && r0 + qr + i < a.nq && (!a.causal || my_k <= qpos);
+            const float p = vis ? __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[i]) : 0.f;
+            pf[r >> 3][r & 7] = (__bf16)p;
+            dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - d4[i]));
+          }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int d_ = 0; d_ < DB; ++d_) {
+            const bf16x8 dot = read_tr(ta.tr[0][d_], ta.tr[1][d_], TILE + uo + (unsigned)hh * 32 * D);
+            dva[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pf[hh], dva[d_], 0, 0, 0);
+            const bf16x8 qtr = read_tr(ta.tr[0][d_], ta.tr[1][d_], uo + (unsigned)hh * 32 * D);
+            dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr, dsf[hh], dka[d_], 0, 0, 0);
+          }
+      });
+    }
+  }
+  if (!k_ok) return;
+  float* kp = a.dk + (int64_t)b * a.dk_sb + my_k * a.dk_ss + (int64_t)g * a.dk_sh;
+  float* vp = a.dv + (int64_t)b * a.dv_sb + my_k * a.dv_ss + (int64_t)g * a.dv_sh;
+#pragma unroll
+  for (int d_ = 0; d_ < DB; ++d_)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 xk = {dka[d_][4 * j] * a.scale, dka[d_][4 * j + 1] * a.scale, dka[d_][4 * j + 2] * a.scale,
+                        dka[d_][4 * j + 3] * a.scale};
+      const f32x4 xv = {dva[d_][4 * j], dva[d_][4 * j + 1], dva[d_][4 * j + 2], dva[d_][4 * j + 3]};
+      *(f32x4*)(kp + 32 * d_ + 8 * j + 4 * lg) = xk;
+      *(f32x4*)(vp + 32 * d_ + 8 * j + 4 * lg) = xv;
+    }
+}
+
+}  // namespace
+
+hipError_t ra_launch_bwd(const RaBwdArgs& a, int d, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a, d);
+  const dim3 gq((unsigned)((int64_t)((a.nq + RA_BWD_BM - 1) / RA_BWD_BM) * a.Hq * a.B)), block(256);
+  const dim3 gk((unsigned)(((a.N + RA_BWD_BM - 1) / RA_BWD_BM) * a.Hkv * a.B));
+  if (d == 128) {
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, gq, block, 0, st, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gk, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, gq, block, 0, st, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gk, block, 0, st, a);
+  }
+  return hipGetLastError();
+}

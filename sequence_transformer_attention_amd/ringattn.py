@@ -68,7 +68,9 @@ def lib() -> ctypes.CDLL:
     L.ra_finalize.argtypes = [T, T, O]
     L.ra_rank_share.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
     L.ra_rank_share_zigzag.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
-    for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share, L.ra_rank_share_zigzag):
+    L.ra_rank_share_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, T, T, T, O]
+    for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share, L.ra_rank_share_zigzag,
+              L.ra_rank_share_bwd):
         f.restype = ctypes.c_int
     L.ra_ring_block.argtypes = [i64, i64, i64]
     L.ra_ring_block.restype = i64
@@ -179,6 +181,16 @@ def ra_rank_share_zigzag(q, k, v, P: int, rank: int, causal: bool, o_out, lse_ou
     opts, keep = _opts(stream, scale, o_out=o_out, lse_out=lse_out)
     _check(lib().ra_rank_share_zigzag(_desc(q), _desc(k), _desc(v), int(P), int(rank), int(bool(causal)),
                                       ctypes.byref(opts)))
+
+
+def ra_rank_share_bwd(q, k, v, o, lse, dout, P: int, rank: int, causal: bool, dq, dk, dv, delta,
+                      scale: Optional[float] = None, stream=None) -> None:
+    """Backward of one rank's share: dq [B, N/P, Hq, d], this rank's dk, dv
+    [B, N, Hkv, d] (all fp32, written); delta [B, Hq, N/P] fp32 workspace."""
+    opts, keep = _opts(stream, scale)
+    _check(lib().ra_rank_share_bwd(_desc(q), _desc(k), _desc(v), _desc(o), _desc(lse, True), _desc(dout),
+                                   int(P), int(rank), int(bool(causal)), _desc(dq), _desc(dk), _desc(dv),
+                                   _desc(delta, True), ctypes.byref(opts)))
 
 
 def ra_ring_block(P: int, rank: int, s: int) -> int:

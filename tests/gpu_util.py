@@ -92,3 +92,33 @@ def zigzag_gpu(q, k, v, P, rank, causal, o_dtype=torch.float32, scale=None):
     ra.ra_rank_share_zigzag(q, k, v, P, rank, causal, O, lse, scale=scale)
     return O, lse
 
+
+def backward_gpu(q, k, v, P, rank, causal, dout, scale=None):
+    """Forward (bf16 O, LSE) then backward on the device; returns (dq, dk, dv) fp32."""
+    B, nq, hq, d = q.shape
+    O = torch.empty((B, nq, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share(q, k, v, P, rank, causal, O, lse, scale=scale)
+    dq = torch.full((B, nq, hq, d), float("nan"), dtype=torch.float32, device=q.device)
+    dk = torch.full(k.shape, float("nan"), dtype=torch.float32, device=q.device)
+    dv = torch.full(k.shape, float("nan"), dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share_bwd(q, k, v, O, lse, dout, P, rank, causal, dq, dk, dv, delta, scale=scale)
+    return dq, dk, dv
+
+
+# Gradients: bf16 operands (q, k, v, dO, the forward's bf16 O, and P and dS
+# rounded to bf16 for the MFMAs) against the exact fp64 chain rule.  Each
+# rounding is at most 2^-9 relative; the gradients are sums of such terms, so
+# the error is bounded relative to the gradient's own scale.
+GRAD_TOL = 1e-2
+
+
+def assert_grad_close(g, g_ref, what: str):
+    """max |g - g_ref| <= GRAD_TOL * max(1, max |g_ref|) (fp64 numpy arrays)."""
+    assert np.isfinite(g).all(), f"{what}: non-finite gradient"
+    scale = max(1.0, float(np.abs(g_ref).max()) if g_ref.size else 1.0)
+    err = float(np.abs(g - g_ref).max()) if g.size else 0.0
+    say(f"{what}: max|d| = {err:.3e}, max|ref| = {scale:.3e} (tol {GRAD_TOL} x {scale:.3g})")
+    assert err <= GRAD_TOL * scale, f"{what}: max |g - g_ref| = {err} > {GRAD_TOL * scale}"
+

@@ -168,6 +168,29 @@ def test_ra_rank_share_zigzag_validation():
     assert zz(T([1, 0, 4, 128]), T([1, 0, 1, 128]), T([1, 0, 1, 128]), 8, 7, o_out=T([1, 0, 4, 128])) == ra.RA_OK
 
 
+def test_ra_rank_share_bwd_validation():
+    def bwd(q, k, v, o, lse, dout, Pn, rank, dq, dk, dv, delta):
+        return ra.lib().ra_rank_share_bwd(P(q), P(k), P(v), P(o), P(lse), P(dout), Pn, rank, 1, P(dq), P(dk),
+                                          P(dv), P(delta), None)
+    q, k, v = T([1, 512, 4, 128]), T([1, 4096, 1, 128]), T([1, 4096, 1, 128])
+    o, do = T([1, 512, 4, 128]), T([1, 512, 4, 128])
+    dq = T([1, 512, 4, 128], ra.RA_F32)
+    dk, dv = T([1, 4096, 1, 128], ra.RA_F32), T([1, 4096, 1, 128], ra.RA_F32)
+    st = rows(1, 4, 512)
+    good = dict(q=q, k=k, v=v, o=o, lse=st, dout=do, Pn=8, rank=7, dq=dq, dk=dk, dv=dv, delta=rows(1, 4, 512))
+    for key, bad, status in (("q", None, ra.RA_E_NULL), ("dq", T([1, 512, 4, 128]), ra.RA_E_DTYPE),
+                             ("dk", T([1, 4096, 1, 64], ra.RA_F32), ra.RA_E_SHAPE),
+                             ("o", T([1, 512, 4, 128], ra.RA_F32), ra.RA_E_DTYPE),
+                             ("delta", rows(1, 4, 511), ra.RA_E_SHAPE), ("rank", 8, ra.RA_E_RANGE)):
+        args = dict(good)
+        args[key] = bad
+        assert bwd(**args) == status, key
+    assert bwd(**dict(good, Pn=4, rank=3)) == ra.RA_E_SHAPE        # Nq != N / P
+    f32 = dict(good, q=T([1, 512, 4, 128], ra.RA_F32), k=T([1, 4096, 1, 128], ra.RA_F32),
+               v=T([1, 4096, 1, 128], ra.RA_F32))
+    assert bwd(**f32) == ra.RA_E_UNSUPPORTED
+
+
 def test_ra_finalize_validation():
     L = ra.lib()
     oacc, l = T([1, 64, 2, 64], ra.RA_F32), rows(1, 2, 64)

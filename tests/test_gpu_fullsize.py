@@ -10,8 +10,8 @@ import torch
 
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
-from tests.gpu_util import (assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu, zigzag_gpu,
-                            zigzag_rows)
+from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
+                            say, stepwise_gpu, zigzag_gpu, zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,4 +57,31 @@ def test_full_size_zigzag_sampled_rows():
         o_ref, l_ref = oracle.rank_share_zigzag(ql, x["k"], x["v"], w.P, r, w.causal, rows=rows,
                                                 nthreads=oracle_threads())
         assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"zigzag rank {r} bf16 O", out_bf16=True)
+
+
+
+
+def test_full_size_backward_sampled_rows():
+    """Backward of the rank-7-of-8 share (N 32768, 32 heads, d 128): sampled dQ
+    rows, and dK/dV rows of kv head 0 sampled over the whole sequence."""
+    w = workloads.RANK7_BF16
+    x = inputs.workload_inputs(w)
+    d = {k: t.to("cuda") for k, t in x.items()}
+    r = w.ranks[0]
+    dout = torch.randn(w.B, w.nq, w.Hq, w.d, generator=torch.Generator().manual_seed(w.seed)).to(torch.bfloat16)
+    say("backward full size: forward + backward on the GPU")
+    dq, dk, dv = backward_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, dout.to("cuda"))
+    torch.cuda.synchronize()
+    qrows = inputs.sample_rows(w.B, w.Hq, w.nq, w.seed).numpy()[:512]
+    g = torch.Generator().manual_seed(w.seed + 1)
+    krows = torch.stack([torch.zeros(256, dtype=torch.long), torch.zeros(256, dtype=torch.long),
+                         torch.randint(0, w.N, (256,), generator=g)], 1).numpy()
+    say(f"backward full size: oracle on {len(qrows)} dQ rows and {len(krows)} dK/dV rows")
+    dq_r, dk_r, dv_r = oracle.rank_share_bwd(x["q"], x["k"], x["v"], dout, w.P, r, w.causal, qrows=qrows,
+                                             krows=krows, nthreads=oracle_threads())
+    qi = torch.as_tensor(qrows)
+    ki = torch.as_tensor(krows)
+    assert_grad_close(dq[qi[:, 0], qi[:, 2], qi[:, 1]].double().cpu().numpy(), dq_r, "dQ full size")
+    assert_grad_close(dk[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dk_r, "dK full size")
+    assert_grad_close(dv[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dv_r, "dV full size")
 

@@ -12,8 +12,8 @@ import torch
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from sequence_transformer_attention_amd import ringattn as ra
-from tests.gpu_util import (assert_close, gather, oracle_threads, rank_share_gpu, say, stepwise_gpu, zigzag_gpu,
-                            zigzag_rows)
+from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
+                            say, stepwise_gpu, zigzag_gpu, zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +142,30 @@ def test_zigzag_shares_reassemble_full_attention():
     torch.cuda.synchronize()
     say(f"zigzag reassembled: max|dO| {float((got - full).abs().max()):.3e}")
     assert float((got - full).abs().max()) <= 1e-2 and float((got_lse - full_lse).abs().max()) <= 1e-3
+
+
+# ---------------------------------------------------------------- backward
+@pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal,ranks", [
+    (1, 1024, 4, 2, 1, 128, True, (0, 3)),     # GQA; the first rank's keys past its queries get zero
+    (2, 600, 3, 2, 2, 64, True, (1,)),         # blocks of 200: ragged query and key tiles, B = 2
+    (1, 512, 2, 4, 2, 128, False, (1,)),       # no mask
+])
+def test_backward_share(B, N, P, Hq, Hkv, d, causal, ranks):
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=N + 3 * P)
+    dv_ = _dev(x)
+    nb = N // P
+    g = torch.Generator().manual_seed(N)
+    for r in ranks:
+        ql = x["q"][:, r * nb:(r + 1) * nb].contiguous()
+        dout = torch.randn(B, nb, Hq, d, generator=g).to(torch.bfloat16)
+        say(f"backward B{B} N{N} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+        dq, dk, dv = backward_gpu(ql.to(DEV), dv_["k"], dv_["v"], P, r, causal, dout.to(DEV))
+        torch.cuda.synchronize()
+        dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, P, r, causal, nthreads=oracle_threads())
+        grid = lambda a, H, S: a.reshape(B, H, S, d).transpose(0, 2, 1, 3)
+        assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nb), f"dQ rank {r}")
+        assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"dK rank {r}")
+        assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"dV rank {r}")
 
 
 # ------------------------------------------------------------------ edge cases

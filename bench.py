@@ -199,6 +199,45 @@ def load_balance(w, r, qd, kd, vd, mean_ms, ra, torch, reps: int = 5):
             "slowest_rank_speedup": round(slow_contig / slow_zz, 3)}
 
 
+def backward(w, r, qd, kd, vd, flop, ra, torch, reps: int = 5):
+    """ra_rank_share_bwd on the same share (bf16 only): the algorithmic FLOP
+    of the backward is 2.5x the forward's (five products per visible pair:
+    S, dP, dV, dQ, dK, against two)."""
+    if w.dtype != "bf16":
+        return None
+    dev = qd.device
+    O = torch.empty((w.B, w.nq, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.nq), dtype=torch.float32, device=dev)
+    ra.ra_rank_share(qd, kd, vd, w.P, r, w.causal, O, lse)
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    dout = torch.randn((w.B, w.nq, w.Hq, w.d), generator=g, device=dev).to(torch.bfloat16)
+    dq = torch.empty((w.B, w.nq, w.Hq, w.d), dtype=torch.float32, device=dev)
+    dk = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    delta = torch.empty((w.B, w.Hq, w.nq), dtype=torch.float32, device=dev)
+
+    def run():
+        ra.ra_rank_share_bwd(qd, kd, vd, O, lse, dout, w.P, r, w.causal, dq, dk, dv, delta)
+
+    stream = torch.cuda.current_stream()
+    run()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    ms = sorted(per)[len(per) // 2]
+    bf = 2.5 * flop
+    log(f"backward (prep + dQ + dK/dV): {ms:.3f} ms -> {bf / ms / 1e9:.1f} TFLOP/s "
+        f"({100 * bf / ms / 1e9 / PEAK_BF16_TFLOPS:.1f} % of peak)")
+    return {"ms": round(ms, 4), "flop": bf, "tflops": round(bf / ms / 1e9, 3),
+            "frac_of_peak": round(bf / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +311,7 @@ def main() -> int:
 
     side = stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch)
     balance = load_balance(w, r, qd, kd, vd, mean_ms, ra, torch)
+    bwd = backward(w, r, qd, kd, vd, flop, ra, torch)
 
     out = {
         "metric": "rank-share ring-attention TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
@@ -292,6 +332,7 @@ def main() -> int:
         "stepwise": side["stepwise"],
         "finalize": side["finalize"],
         "load_balance": balance,
+        "backward": bwd,
     }
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, xq, O, lse, args.cpu_seconds)

@@ -256,8 +256,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
 template <int D>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   constexpr int NW = 4, BK = NW * 32, BN = RA_BWD_BN, KC = D / 16, DB = D / 32, TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[2][TILE];  // Q tile, dO tile
-  __shared__ __attribute__((aligned(16))) float lsd[2][BN];      // LSE * log2(e), D of the tile's rows
+  // two stages of (Q tile, dO tile) and of their rows' (LSE log2(e), D)
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][BN];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -282,75 +283,120 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16{};
   TileAddr<D> ta;
-  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]), lane);
+  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0][0]), lane);
+  const unsigned lsd_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) float*)&lsd[0][0][0]);
 
   // Local query rows that see any key of the workgroup: under causal
-  // masking those at positions >= the first key's.
+  // masking those at positions >= the first key's.  The work is the list of
+  // (query head of the kv head, 64-row tile) pairs, walked with the loads of
+  // the next pair in flight during the current one.
   const int64_t kfirst = (int64_t)kt * BK;
   int64_t qlo = a.causal ? kfirst - a.q_off : 0;
   qlo = qlo < 0 ? 0 : qlo;
-  const int t0 = qlo >= a.nq ? a.nq : (int)(qlo / BN);
   const int ntq = (a.nq + BN - 1) / BN;
-  for (int hh_ = 0; hh_ < G; ++hh_) {
-    const int h = g * G + hh_;
-    const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
-    const __bf16* db_ = (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh;
-    for (int t = t0; t < ntq; ++t) {
-      const int r0 = t * BN;
-      const int nvalid = min(BN, a.nq - r0);
-      __syncthreads();
-      load_tile<D, NW>(qb + (int64_t)r0 * a.q_ss, a.q_ss, nvalid, &smem[0][0], wave, lane);
-      load_tile<D, NW>(db_ + (int64_t)r0 * a.do_ss, a.do_ss, nvalid, &smem[1][0], wave, lane);
-      if (tid < BN) {
-        const int row = r0 + tid;
-        const bool ok = row < a.nq;
-        lsd[0][tid] = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e
-                         : INFINITY;
-        lsd[1][tid] = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
+  const int t0 = qlo >= a.nq ? ntq : (int)(qlo / BN);
+  const int nt = ntq - t0, total = G * nt;
+  float lsv = 0.f, dlv = 0.f;  // threads 0..63: LSE log2(e) and D of row tid of the tile in flight
+  auto issue = [&](int it, int st) __attribute__((always_inline)) {
+    const int h = g * G + it / nt, r0 = (t0 + it % nt) * BN;
+    const int nvalid = min(BN, a.nq - r0);
+    load_tile<D, NW>((const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss, a.q_ss,
+                     nvalid, &smem[st][0][0], wave, lane);
+    load_tile<D, NW>((const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)r0 * a.do_ss,
+                     a.do_ss, nvalid, &smem[st][1][0], wave, lane);
+    if (tid < BN) {
+      const int row = r0 + tid;
+      const bool ok = row < a.nq;
+      lsv = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e : INFINITY;
+      dlv = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
+    }
+  };
+  if (total > 0) issue(0, 0);
+  for (int it = 0; it < total; ++it) {
+    const int st = it & 1;
+    const int r0 = (t0 + it % nt) * BN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid < BN) {
+      lsd[st][0][tid] = lsv;
+      lsd[st][1][tid] = dlv;
+    }
+    __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
+    if (it + 1 < total) issue(it + 1, st ^ 1);
+    const unsigned sb = (unsigned)st * 2 * TILE;
+    static_for<0, 2>([&](auto HF) {
+      constexpr int hf = decltype(HF)::value;
+      constexpr unsigned uo = (unsigned)hf * 64 * D;
+      // S = Q K^T and dP = dO V^T (queries x keys); query row of register r:
+      // 8 (r / 4) + 4 lg + (r % 4)
+      bf16x8 fq[KC], fd[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const unsigned a0 = ta.rd[c] + sb + uo, a1 = ta.rd[c] + sb + TILE + uo;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(fq[c]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(fd[c]) : "v"(a1));
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      static_for<0, 2>([&](auto HF) {
-        constexpr int hf = decltype(HF)::value;
-        constexpr unsigned uo = (unsigned)hf * 64 * D;
-        // S = Q K^T (queries x keys); query row of register r: 8 (r / 4) + 4 lg + (r % 4)
-        bf16x8 fr[KC];
-        read_rows<KC>(fr, ta.rd, uo);
-        f32x16 sacc = f32x16{};
+      // LSE log2(e) and D of the lane's 16 query rows (4 runs of 4)
+      f32x4 l4[4], d4[4];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], kf[c], sacc, 0, 0, 0);
-        read_rows<KC>(fr, ta.rd, TILE + uo);
-        f32x16 dpa = f32x16{};
+      for (int j = 0; j < 4; ++j) {
+        const unsigned o4 = (unsigned)(32 * hf + 8 * j + 4 * lg) * 4u;
+        const unsigned al = lsd_base + (unsigned)st * 2 * BN * 4 + o4, ad = al + BN * 4;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(l4[j]) : "v"(al));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(d4[j]) : "v"(ad));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]), "+v"(d4[0]),
+                   "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
+      if constexpr (KC == 8)
+        asm volatile("" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fq[4]), "+v"(fq[5]), "+v"(fq[6]),
+                     "+v"(fq[7]), "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(fd[4]), "+v"(fd[5]),
+                     "+v"(fd[6]), "+v"(fd[7]));
+      else
+        asm volatile("" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]),
+                     "+v"(fd[3]));
+      f32x16 sacc = f32x16{}, dpa = f32x16{};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], vf[c], dpa, 0, 0, 0);
-        bf16x8 pf[2], dsf[2];
+      for (int c = 0; c < KC; ++c) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sacc, 0, 0, 0);
+        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], vf[c], dpa, 0, 0, 0);
+      }
+      // transposing reads of dO^T and Q^T for the dV and dK products, in
+      // flight while P and dS are formed
+      u32x2 tlo[2][2][DB], thi[2][2][DB];  // [dO / Q][16-row group][channel block]
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qr = 32 * hf + 8 * j + 4 * lg;  // first of 4 consecutive rows
-          const f32x4 l4 = *(const f32x4*)&lsd[0][qr];
-          const f32x4 d4 = *(const f32x4*)&lsd[1][qr];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * j + i;
-            const int64_t qpos = a.q_off + r0 + qr + i;
-            const bool vis = k_ok && r0 + qr + i < a.nq && (!a.causal || my_k <= qpos);
-            const float p = vis ? __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[i]) : 0.f;
-            pf[r >> 3][r & 7] = (__bf16)p;
-            dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - d4[i]));
-          }
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS
+      for (int w = 0; w < 2; ++w)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int d_ = 0; d_ < DB; ++d_) {
-            const bf16x8 dot = read_tr(ta.tr[0][d_], ta.tr[1][d_], TILE + uo + (unsigned)hh * 32 * D);
-            dva[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pf[hh], dva[d_], 0, 0, 0);
-            const bf16x8 qtr = read_tr(ta.tr[0][d_], ta.tr[1][d_], uo + (unsigned)hh * 32 * D);
-            dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr, dsf[hh], dka[d_], 0, 0, 0);
+            const unsigned off = sb + (w ? 0u : (unsigned)TILE) + uo + (unsigned)hh * 32 * D;
+            const unsigned a0 = ta.tr[0][d_] + off, a1 = ta.tr[1][d_] + off;
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(tlo[w][hh][d_]) : "v"(a0));
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(thi[w][hh][d_]) : "v"(a1));
           }
-      });
-    }
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          const int qrow = r0 + 32 * hf + 8 * j + 4 * lg + i;
+          const bool vis = k_ok && qrow < a.nq && (!a.causal || my_k <= a.q_off + qrow);
+          const float p = vis ? __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]) : 0.f;
+          pf[r >> 3][r & 7] = (__bf16)p;
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - d4[j][i]));
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int d_ = 0; d_ < DB; ++d_) {
+          u32x2 l0 = tlo[0][hh][d_], h0 = thi[0][hh][d_], l1 = tlo[1][hh][d_], h1 = thi[1][hh][d_];
+          asm volatile("" : "+v"(l0), "+v"(h0), "+v"(l1), "+v"(h1));
+          const u32x4 wd = {l0[0], l0[1], h0[0], h0[1]}, wq = {l1[0], l1[1], h1[0], h1[1]};
+          dva[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wd), pf[hh], dva[d_], 0, 0, 0);
+          dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), dsf[hh], dka[d_], 0, 0, 0);
+        }
+    });
   }
   if (!k_ok) return;
   float* kp = a.dk + (int64_t)b * a.dk_sb + my_k * a.dk_ss + (int64_t)g * a.dk_sh;

@@ -104,6 +104,16 @@ __device__ __forceinline__ void read_rows(bf16x8 (&f)[KC], const unsigned (&rd)[
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
 }
 
+// LDS reads with an immediate byte offset.
+template <unsigned OFF, typename T>
+__device__ __forceinline__ void ds_rd128(T& r, unsigned addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+template <unsigned OFF>
+__device__ __forceinline__ void ds_rdtr(u32x2& r, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+
 // Transposing A operand of channel block db, 16-row group at byte offset OFF.
 __device__ __forceinline__ bf16x8 read_tr(unsigned lo_addr, unsigned hi_addr, unsigned off) {
   u32x2 lo, hi;
@@ -156,7 +166,7 @@ template <int D>
 __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
   constexpr int NW = 4, BM = NW * 32, BN = RA_BWD_BN, KC = D / 16, DB = D / 32, TILE = BN * D * 2;
   static_assert(BM == RA_BWD_BM, "query rows per workgroup");
-  __shared__ __attribute__((aligned(1024))) char smem[2][TILE];  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // two stages of (K tile, V tile)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -187,59 +197,111 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
   TileAddr<D> ta;
-  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]), lane);
+  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0][0]), lane);
 
   const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
   const int64_t q0_wg = a.q_off + qrow_wg, q0w = a.q_off + qrow_w;
   const int nq_wg = min(BM, a.nq - qrow_wg);
-  for (int s = 0; s < a.P; ++s) {
-    const int64_t kv0 = ra_plan_ring_block(a.P, a.rank, s) * a.nb;  // position = row
-    const int nt = (int)ra_plan_key_tiles(q0_wg, nq_wg, kv0, a.nb, a.causal, BN);
-    for (int u = 0; u < nt; ++u) {
-      const int64_t k0 = kv0 + (int64_t)u * BN;
-      const int64_t left = a.nb - (int64_t)u * BN;
-      const int nvalid = left < BN ? (int)left : BN;
-      __syncthreads();  // every wave is done with the previous tile
-      load_tile<D, NW>(kb + k0 * a.k_ss, a.k_ss, nvalid, &smem[0][0], wave, lane);
-      load_tile<D, NW>(vb + k0 * a.v_ss, a.v_ss, nvalid, &smem[1][0], wave, lane);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      static_for<0, 2>([&](auto HF) {
-        constexpr int hf = decltype(HF)::value;
-        constexpr unsigned uo = (unsigned)hf * 64 * D;  // 32-row unit
-        // S^T = K Q^T (keys x queries)
-        bf16x8 fr[KC];
-        read_rows<KC>(fr, ta.rd, uo);
-        f32x16 sacc = f32x16{};
+  auto tiles = [&](int s) -> int {
+    return (int)ra_plan_key_tiles(q0_wg, nq_wg, ra_plan_ring_block(a.P, a.rank, s) * a.nb, a.nb, a.causal, BN);
+  };
+  // The workgroup's key tiles in ring order; the loads of the next tile are
+  // in flight while the current one is computed (two LDS stages).
+  struct Cur {
+    int s, u, nt;
+    int64_t k0;
+  };
+  auto cur_fix = [&](Cur& c) {  // move to the first tile of the first non-empty step from c.s on
+    while (c.s < a.P && (c.nt = tiles(c.s)) == 0) ++c.s;
+    c.u = 0;
+    c.k0 = c.s < a.P ? ra_plan_ring_block(a.P, a.rank, c.s) * a.nb : 0;
+  };
+  auto cur_next = [&](Cur& c) {
+    if (++c.u < c.nt) return;
+    ++c.s;
+    cur_fix(c);
+  };
+  int total = 0;
+  for (int s = 0; s < a.P; ++s) total += tiles(s);
+  Cur cc{0, 0, 0, 0}, cl{0, 0, 0, 0};  // compute cursor, load cursor
+  cur_fix(cc);
+  cur_fix(cl);
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const int64_t k0 = cl.k0 + (int64_t)cl.u * BN, left = a.nb - (int64_t)cl.u * BN;
+    const int nvalid = left < BN ? (int)left : BN;
+    load_tile<D, NW>(kb + k0 * a.k_ss, a.k_ss, nvalid, &smem[st][0][0], wave, lane);
+    load_tile<D, NW>(vb + k0 * a.v_ss, a.v_ss, nvalid, &smem[st][1][0], wave, lane);
+    cur_next(cl);
+  };
+  auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    const int64_t k0 = cc.k0 + (int64_t)cc.u * BN, left = a.nb - (int64_t)cc.u * BN;
+    const int nvalid = left < BN ? (int)left : BN;
+    cur_next(cc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
+    if (it + 1 < total) issue(st ^ 1);
+    static_for<0, 2>([&](auto HF) {
+      constexpr int hf = decltype(HF)::value;
+      constexpr unsigned ko = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // K unit; V unit at + TILE
+      // S^T = K Q^T and dP^T = V dO^T (keys x queries)
+      bf16x8 fk[KC], fv[KC];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], qf[c], sacc, 0, 0, 0);
-        // dP^T = V dO^T
-        read_rows<KC>(fr, ta.rd, TILE + uo);
-        f32x16 dpa = f32x16{};
+      for (int c = 0; c < KC; ++c) {
+        ds_rd128<ko>(fk[c], ta.rd[c]);
+        ds_rd128<ko + TILE>(fv[c], ta.rd[c]);
+      }
+      if constexpr (KC == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]), "+v"(fk[4]),
+                     "+v"(fk[5]), "+v"(fk[6]), "+v"(fk[7]), "+v"(fv[0]), "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]),
+                     "+v"(fv[4]), "+v"(fv[5]), "+v"(fv[6]), "+v"(fv[7]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]), "+v"(fv[0]),
+                     "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]));
+      f32x16 sacc = f32x16{}, dpa = f32x16{};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c], dof[c], dpa, 0, 0, 0);
-        // P^T and dS^T; key index of register r: 8 (r / 4) + (r % 4) + 4 lg
-        const int nv = min(max(nvalid - 32 * hf, 0), 32);
-        const int64_t vis = a.causal ? q0w + lr - (k0 + 32 * hf) + 1 : nv;  // keys below this index are visible
-        const int lim = (int)(vis < nv ? (vis > 0 ? vis : 0) : nv);
-        bf16x8 dsf[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + (r & 3) + 4 * lg;
-          const float p = kk < lim ? __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2) : 0.f;
-          dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
-        }
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 kt = read_tr(ta.tr[0][db], ta.tr[1][db], uo + (unsigned)hh * 32 * D);
-            dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[hh], dqa[db], 0, 0, 0);
-          }
+      for (int c = 0; c < KC; ++c) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], qf[c], sacc, 0, 0, 0);
+        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c], dof[c], dpa, 0, 0, 0);
+      }
+      // K^T for the dQ product, in flight while P^T and dS^T are formed
+      u32x2 tlo[2][DB], thi[2][DB];
+      static_for<0, 2 * DB>([&](auto X) {
+        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
+        constexpr unsigned off = ko + (unsigned)hh * 32 * D;
+        ds_rdtr<off>(tlo[hh][d_], ta.tr[0][d_]);
+        ds_rdtr<off>(thi[hh][d_], ta.tr[1][d_]);
       });
-    }
+      // key index of register r: 8 (r / 4) + (r % 4) + 4 lg; keys below lim are visible
+      const int nv = min(max(nvalid - 32 * hf, 0), 32);
+      const int64_t vis = a.causal ? q0w + lr - (k0 + 32 * hf) + 1 : nv;
+      const int lim = (int)(vis < nv ? (vis > 0 ? vis : 0) : nv);
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + (r & 3) + 4 * lg;
+        float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2);
+        asm volatile("" : "+v"(t));  // computed for every lane: no branch
+        const float p = kk < lim ? t : 0.f;
+        dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int d_ = 0; d_ < DB; ++d_) {
+          u32x2 l0 = tlo[hh][d_], h0 = thi[hh][d_];
+          asm volatile("" : "+v"(l0), "+v"(h0));
+          const u32x4 w = {l0[0], l0[1], h0[0], h0[1]};
+          dqa[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), dsf[hh], dqa[d_], 0, 0, 0);
+        }
+    });
+  };
+  if (total > 0) issue(0);
+  for (int it = 0; it < total; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < total) tile(it + 1, std::integral_constant<int, 1>{});
   }
   if (!q_ok) return;
   float* dp = a.dq + (int64_t)b * a.dq_sb + (int64_t)my_q * a.dq_ss + (int64_t)h * a.dq_sh;
@@ -311,9 +373,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       dlv = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
     }
   };
-  if (total > 0) issue(0, 0);
-  for (int it = 0; it < total; ++it) {
-    const int st = it & 1;
+  const unsigned lsd_lane = lsd_base + 16u * (unsigned)lg;  // + 4 floats per lane group
+  // One tile: stage ST (compile time, so every LDS offset is an immediate).
+  auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
     const int r0 = (t0 + it % nt) * BN;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (tid < BN) {
@@ -322,28 +385,25 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     }
     __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
     if (it + 1 < total) issue(it + 1, st ^ 1);
-    const unsigned sb = (unsigned)st * 2 * TILE;
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
-      constexpr unsigned uo = (unsigned)hf * 64 * D;
+      constexpr unsigned qo = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // Q unit; dO unit at + TILE
       // S = Q K^T and dP = dO V^T (queries x keys); query row of register r:
       // 8 (r / 4) + 4 lg + (r % 4)
       bf16x8 fq[KC], fd[KC];
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const unsigned a0 = ta.rd[c] + sb + uo, a1 = ta.rd[c] + sb + TILE + uo;
-        asm volatile("ds_read_b128 %0, %1" : "=v"(fq[c]) : "v"(a0));
-        asm volatile("ds_read_b128 %0, %1" : "=v"(fd[c]) : "v"(a1));
+        ds_rd128<qo>(fq[c], ta.rd[c]);
+        ds_rd128<qo + TILE>(fd[c], ta.rd[c]);
       }
       // LSE log2(e) and D of the lane's 16 query rows (4 runs of 4)
       f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned o4 = (unsigned)(32 * hf + 8 * j + 4 * lg) * 4u;
-        const unsigned al = lsd_base + (unsigned)st * 2 * BN * 4 + o4, ad = al + BN * 4;
-        asm volatile("ds_read_b128 %0, %1" : "=v"(l4[j]) : "v"(al));
-        asm volatile("ds_read_b128 %0, %1" : "=v"(d4[j]) : "v"(ad));
-      }
+      static_for<0, 4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr unsigned o4 = ((unsigned)st * 2 * BN + 32u * hf + 8u * j) * 4u;
+        ds_rd128<o4>(l4[j], lsd_lane);
+        ds_rd128<o4 + BN * 4>(d4[j], lsd_lane);
+      });
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]), "+v"(d4[0]),
                    "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
       if constexpr (KC == 8)
@@ -362,26 +422,26 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       // transposing reads of dO^T and Q^T for the dV and dK products, in
       // flight while P and dS are formed
       u32x2 tlo[2][2][DB], thi[2][2][DB];  // [dO / Q][16-row group][channel block]
-#pragma unroll
-      for (int w = 0; w < 2; ++w)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int d_ = 0; d_ < DB; ++d_) {
-            const unsigned off = sb + (w ? 0u : (unsigned)TILE) + uo + (unsigned)hh * 32 * D;
-            const unsigned a0 = ta.tr[0][d_] + off, a1 = ta.tr[1][d_] + off;
-            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(tlo[w][hh][d_]) : "v"(a0));
-            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(thi[w][hh][d_]) : "v"(a1));
-          }
+      static_for<0, 2 * 2 * DB>([&](auto X) {
+        constexpr int x = decltype(X)::value, w = x / (2 * DB), hh = (x / DB) % 2, d_ = x % DB;
+        constexpr unsigned off = qo + (w ? 0u : (unsigned)TILE) + (unsigned)hh * 32 * D;
+        ds_rdtr<off>(tlo[w][hh][d_], ta.tr[0][d_]);
+        ds_rdtr<off>(thi[w][hh][d_], ta.tr[1][d_]);
+      });
+      // visible: query row rb + e (e = 8 (r / 4) + (r % 4)) exists and, under
+      // causal masking, is at or after this lane's key: lo <= e < hi
+      const int rb = r0 + 32 * hf + 4 * lg;
+      const int lo = a.causal ? (int)(my_k - a.q_off) - rb : -(1 << 30);
+      const int hi = k_ok ? a.nq - rb : -(1 << 30);
       bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const int qrow = r0 + 32 * hf + 8 * j + 4 * lg + i;
-          const bool vis = k_ok && qrow < a.nq && (!a.causal || my_k <= a.q_off + qrow);
-          const float p = vis ? __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]) : 0.f;
+          const int r = 4 * j + i, e = 8 * j + i;
+          float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]);
+          asm volatile("" : "+v"(t));  // computed for every lane: no branch
+          const float p = (e >= lo && e < hi) ? t : 0.f;
           pf[r >> 3][r & 7] = (__bf16)p;
           dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - d4[j][i]));
         }
@@ -397,6 +457,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
           dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), dsf[hh], dka[d_], 0, 0, 0);
         }
     });
+  };
+  if (total > 0) issue(0, 0);
+  for (int it = 0; it < total; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < total) tile(it + 1, std::integral_constant<int, 1>{});
   }
   if (!k_ok) return;
   float* kp = a.dk + (int64_t)b * a.dk_sb + my_k * a.dk_ss + (int64_t)g * a.dk_sh;

@@ -62,6 +62,9 @@ def _load(path: Optional[str] = None):
     lib.orc_rank_share.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                    ctypes.c_int, ctypes.c_double, _ip, _i64, _dp, _dp, ctypes.c_int]
     lib.orc_rank_share.restype = ctypes.c_int
+    lib.orc_rank_share_padded.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                          ctypes.c_int, ctypes.c_double, _i64, _ip, _i64, _dp, _dp, ctypes.c_int]
+    lib.orc_rank_share_padded.restype = ctypes.c_int
     lib.orc_rank_share_zigzag.argtypes = lib.orc_rank_share.argtypes
     lib.orc_rank_share_zigzag.restype = ctypes.c_int
     lib.orc_share_flops_zigzag.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
@@ -207,6 +210,27 @@ def rank_share(q, k, v, P: int, rank: int, causal: bool, scale: Optional[float] 
                            nthreads or default_threads())
     if e:
         raise ValueError(f"orc_rank_share failed ({e})")
+    return out, lse
+
+
+def rank_share_padded(q, k, v, P: int, rank: int, causal: bool, n_valid: int, scale: Optional[float] = None,
+                      rows=None, nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Share of a padded sequence: K, V [B, N, Hkv, d] with the first n_valid
+    rows real; keys at positions >= n_valid are masked out.  O [n, d], LSE [n]."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, nq, hq, d = q.shape
+    N, hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    r = _rows(rows, B, hq, nq)
+    n = r.shape[0]
+    out = np.zeros((n, d)); lse = np.zeros(n)
+    e = lib.orc_rank_share_padded(_ptr(q), _ptr(k), _ptr(v), B, N, P, rank, hq, hkv, d, int(causal), float(scale),
+                                  int(n_valid), r.ctypes.data_as(_ip), n, _ptr(out), _ptr(lse),
+                                  nthreads or default_threads())
+    if e:
+        raise ValueError(f"orc_rank_share_padded failed ({e})")
     return out, lse
 
 

@@ -269,6 +269,50 @@ done:
     return e;
 }
 
+/* Share of an explicitly padded sequence (mvp-engine skill page
+ * "sequence-parallel": pad and mask explicitly when the length is not a
+ * multiple of the shard count): k, v hold N rows of which the first n_valid
+ * are real; a key at position >= n_valid is visible to no query.  The ring
+ * is unchanged; block j contributes its keys before n_valid (none: the merge
+ * identity). */
+int orc_rank_share_padded(const double *q, const double *k, const double *v,
+                          int64_t B, int64_t N, int64_t P, int64_t rank,
+                          int64_t hq, int64_t hkv, int64_t d, int causal, double scale, int64_t n_valid,
+                          const int64_t *rows, int64_t nrows, double *out, double *lse, int nthreads)
+{
+    if (P <= 0 || N % P != 0) return -3;
+    if (rank < 0 || rank >= P || n_valid < 1 || n_valid > N) return -5;
+    const int64_t nb = N / P;
+    size_t nd = (size_t)(nrows > 0 ? nrows : 1) * (size_t)d;
+    size_t n1 = (size_t)(nrows > 0 ? nrows : 1);
+    double *m = malloc(n1 * sizeof(double)), *l = malloc(n1 * sizeof(double));
+    double *o = malloc(nd * sizeof(double));
+    double *pm = malloc(n1 * sizeof(double)), *pl = malloc(n1 * sizeof(double));
+    double *po = malloc(nd * sizeof(double));
+    int e = 0;
+    if (!m || !l || !o || !pm || !pl || !po) { e = -8; goto done; }
+    for (int64_t r = 0; r < nrows; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.0;
+        for (int64_t c = 0; c < d; ++c) o[r * d + c] = 0.0;
+    }
+    for (int64_t s = 0; s < P; ++s) {
+        const int64_t j = orc_ring_block(P, rank, s);
+        const int64_t real = n_valid - j * nb;         /* real keys of block j */
+        const int64_t nk = real < 0 ? 0 : (real > nb ? nb : real);
+        if (nk == 0) continue;
+        e = orc_block_partial(q, k + j * nb * hkv * d, v + j * nb * hkv * d,
+                              B, nb, N, nb, nk, hq, hkv, d, rank * nb, j * nb,
+                              causal, scale, rows, nrows, pm, pl, po, nthreads);
+        if (e) goto done;
+        orc_merge(nrows, d, m, l, o, pm, pl, po, m, l, o);
+    }
+    orc_finalize(nrows, d, m, l, o, out, lse);
+done:
+    free(m); free(l); free(o); free(pm); free(pl); free(po);
+    return e;
+}
+
 /* Load-balanced ("zigzag") share, the reading of "Implementation
  * Considerations / Load Balancing" used here: the sequence is cut into 2P
  * chunks of c = N/(2P) tokens and rank r owns chunks r and 2P-1-r, so under

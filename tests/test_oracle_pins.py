@@ -281,6 +281,36 @@ def test_share_flops_of_the_workloads():
     assert sum(oracle.share_flops(1, 512, 4, r, 2, 64, False) for r in range(4)) == 134217728
 
 
+# ------------------------------------------------------ padded (uneven) length
+@pytest.mark.parametrize("B,n_valid,P,Hq,Hkv,d,causal", [
+    (1, 22, 4, 2, 1, 8, True),     # N = 24: the last block holds 4 real keys of 6
+    (2, 13, 3, 2, 2, 4, True),     # N = 15: the last block holds 3 of 5
+    (1, 17, 2, 1, 1, 8, False),    # N = 18, no causal mask
+    (1, 9, 4, 1, 1, 4, True),      # N = 12: the last block holds no real key
+])
+def test_padded_share_is_attention_over_the_real_keys(B, n_valid, P, Hq, Hkv, d, causal):
+    """Every row of every rank (padding rows included) equals torch fp64
+    attention of that query over the first n_valid keys only."""
+    N = P * (-(-n_valid // P))
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=n_valid * P)
+    O_t, L_t = _torch_attention(q, k[:, :n_valid], v[:, :n_valid], 0, 0, causal, 0.35)
+    nb = N // P
+    for r in range(P):
+        o, lse = oracle.rank_share_padded(q[:, r * nb:(r + 1) * nb], k, v, P, r, causal, n_valid, 0.35)
+        np.testing.assert_allclose(_grid(o, B, Hq, nb), O_t[:, r * nb:(r + 1) * nb].numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse.reshape(B, Hq, nb), L_t[:, :, r * nb:(r + 1) * nb].numpy(), atol=TOL, rtol=0)
+
+
+def test_padded_share_with_no_padding_is_the_share():
+    B, N, P, H, d = 1, 24, 3, 2, 8
+    q, k, v = _rand(B, N, N, H, H, d, seed=1)
+    for r in range(P):
+        a = oracle.rank_share(q[:, r * 8:(r + 1) * 8], k, v, P, r, True, 0.3)
+        b = oracle.rank_share_padded(q[:, r * 8:(r + 1) * 8], k, v, P, r, True, N, 0.3)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
 # ----------------------------------------------------- load-balanced (zigzag)
 @pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal", [
     (1, 48, 3, 2, 1, 8, True),      # GQA, c = 8

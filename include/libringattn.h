@@ -124,6 +124,17 @@ int ra_finalize(const ra_tensor *o_acc, const ra_tensor *l, const ra_opts *opts)
 int ra_rank_share(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                   int P, int rank, int causal, const ra_opts *opts);
 
+/* One rank's share of an explicitly PADDED sequence (mvp-engine skill page
+ * "sequence-parallel": when the sequence length is not a multiple of the
+ * shard count, pad and mask explicitly).  k, v hold N = P * ceil(n_valid/P)
+ * rows, the first n_valid real and the rest padding; keys at positions
+ * >= n_valid are masked out for every query.  Query rows at positions
+ * >= n_valid (padding) are computed like the others, against the real keys,
+ * and are the caller's to ignore.  Shapes, outputs and errors as for
+ * ra_rank_share; n_valid outside [1, N] is RA_E_RANGE. */
+int ra_rank_share_padded(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                         int P, int rank, int causal, int64_t n_valid, const ra_opts *opts);
+
 /* One rank's LOAD-BALANCED share in one launch (glossary page "sequence
  * parallelism transformers", section "Implementation Considerations", item
  * "Load Balancing": under causal masking contiguous shards leave rank 0 with

@@ -191,6 +191,7 @@ int ra_step(const ra_tensor* q, const ra_tensor* k_blk, const ra_tensor* v_blk, 
 
   RaAttnArgs a{};
   a.nsplit = 1;
+  a.kv_end = kv_off + nkv;
   a.q = q->data; set_bshd(q, a.q_sb, a.q_ss, a.q_sh);
   a.k = k_blk->data; set_bshd(k_blk, a.k_sb, a.k_ss, a.k_sh);
   a.v = v_blk->data; set_bshd(v_blk, a.v_sb, a.v_ss, a.v_sh);
@@ -244,8 +245,8 @@ int ra_finalize(const ra_tensor* o_acc, const ra_tensor* l, const ra_opts* opts)
 // 2P-1-rank of 2P chunks (the load-balanced share), each chunk folding all 2P
 // key chunks in its own ring order.
 static int rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
-                      const ra_opts* opts, int zigzag) {
-  const char* fn = zigzag ? "ra_rank_share_zigzag" : "ra_rank_share";
+                      const ra_opts* opts, int zigzag, int64_t n_valid) {
+  const char* fn = zigzag ? "ra_rank_share_zigzag" : (n_valid >= 0 ? "ra_rank_share_padded" : "ra_rank_share");
   int e = check_qkv(q, k, v, "k", "v");
   if (e) return e;
   if (!opts || !opts->o_out) return fail(RA_E_NULL, "%s needs opts->o_out", fn);
@@ -257,6 +258,8 @@ static int rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
   if (N % parts != 0)
     return fail(RA_E_SHAPE, "sequence length %lld is not divisible by %s = %lld (no implicit padding)",
                 (long long)N, zigzag ? "2P" : "P", (long long)parts);
+  if (n_valid > N) return fail(RA_E_RANGE, "n_valid %lld exceeds the padded length %lld", (long long)n_valid, (long long)N);
+  if (n_valid == 0 && N > 0) return fail(RA_E_RANGE, "n_valid must be >= 1");
   const int64_t nb = N / parts;  // block (contiguous) or chunk (zigzag) length
   const int64_t rows = zigzag ? 2 * nb : nb;
   if (nq != rows)
@@ -276,6 +279,7 @@ static int rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
   a.nkv = nb; a.q_off = (int64_t)rank * nb; a.kv_off = 0;
   a.ring = 1; a.P = (int32_t)parts; a.rank = rank; a.causal = causal ? 1 : 0;
   a.nsplit = 1;
+  a.kv_end = n_valid >= 0 ? n_valid : N;
   if (zigzag) {
     a.nsplit = 2; a.qc = nb;
     a.rank2 = (int32_t)(parts - 1 - rank); a.q_off2 = (parts - 1 - rank) * nb;
@@ -291,12 +295,18 @@ static int rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
 
 int ra_rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
                   const ra_opts* opts) {
-  return rank_share(q, k, v, P, rank, causal, opts, 0);
+  return rank_share(q, k, v, P, rank, causal, opts, 0, -1);
+}
+
+int ra_rank_share_padded(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
+                         int64_t n_valid, const ra_opts* opts) {
+  if (n_valid < 0) return fail(RA_E_RANGE, "n_valid must be >= 1");
+  return rank_share(q, k, v, P, rank, causal, opts, 0, n_valid);
 }
 
 int ra_rank_share_zigzag(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, int P, int rank, int causal,
                          const ra_opts* opts) {
-  return rank_share(q, k, v, P, rank, causal, opts, 1);
+  return rank_share(q, k, v, P, rank, causal, opts, 1, -1);
 }
 
 int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,

@@ -196,8 +196,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   auto step_kv_off = [&](int s) -> int64_t {
     return a.ring ? (int64_t)ra_plan_ring_block32(a.P, rank_e, (s + 1) % a.P) * a.nkv : a.kv_off;
   };
+  // keys of the block at loop step s before the end of the valid keys
+  auto step_keys = [&](int s) -> int64_t {
+    const int64_t n = a.kv_end - step_kv_off(s);
+    return n < 0 ? 0 : (n < a.nkv ? n : a.nkv);
+  };
   auto step_tiles = [&](int s) -> int {
-    return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), a.nkv, a.causal, BN);
+    return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), step_keys(s), a.causal, BN);
   };
 
   // Direct loads.  All eight waves load a share (NL KiB) of each K and V
@@ -316,7 +321,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       cnt = step_tiles(cs);
       const int64_t kv = step_kv_off(cs), rel = kv - q0w;
       crel = rel < -kRelSat ? -kRelSat : (rel > kRelSat ? kRelSat : (int)rel);
-      cleft = (int)a.nkv;
+      cleft = (int)step_keys(cs);
       cka = kbase + (kv - roff) * a.k_ss * 2;
       cva = vbase + (kv - roff) * a.v_ss * 2;
     };
@@ -771,9 +776,10 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
     const int64_t jb = a.ring ? ra_plan_ring_block(a.P, rank_e, s) : 0;
     const int64_t kv_off = a.ring ? jb * a.nkv : a.kv_off;
     const int64_t row0 = a.ring ? jb * a.nkv : 0;
-    const int nt = (int)ra_plan_key_tiles(q0_wg, nq_wg, kv_off, a.nkv, a.causal, BN);
+    const int64_t nkeys = a.kv_end - kv_off < 0 ? 0 : (a.kv_end - kv_off < a.nkv ? a.kv_end - kv_off : a.nkv);
+    const int nt = (int)ra_plan_key_tiles(q0_wg, nq_wg, kv_off, nkeys, a.causal, BN);
     for (int u = 0; u < nt; ++u) {
-      const int64_t left = a.nkv - (int64_t)u * BN;
+      const int64_t left = nkeys - (int64_t)u * BN;
       const int nvalid = left < BN ? (int)left : BN;
       const float* kb = (const float*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + (row0 + (int64_t)u * BN) * a.k_ss;
       const float* vb = (const float*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + (row0 + (int64_t)u * BN) * a.v_ss;

@@ -12,6 +12,9 @@
 //              [qc, 2 qc) at q_off2.. (ring order from rank2); otherwise one
 //              block of nq rows at q_off.. .  Query tiles never straddle the
 //              chunks.
+//   kv_end:    keys at global positions >= kv_end are not visible (the
+//              valid length of an explicitly padded sequence; the end of the
+//              block or sequence otherwise).
 //   state_in:  1 = start from (oacc, m, l); 0 = start from the empty state.
 //   out_state: 1 = write (oacc, m, l) back; 0 = write normalised o (+ lse).
 struct RaAttnArgs {
@@ -30,6 +33,7 @@ struct RaAttnArgs {
   void* o; int64_t o_sb, o_ss, o_sh; int32_t o_bf16;
   float* lse; int64_t lse_sb, lse_sh, lse_ss;
   int32_t nsplit, rank2; int64_t qc, q_off2;
+  int64_t kv_end;
 };
 
 // O = oacc / l (to o, bf16 or fp32, or in place), LSE = m + ln l (optional).

@@ -68,9 +68,10 @@ def lib() -> ctypes.CDLL:
     L.ra_finalize.argtypes = [T, T, O]
     L.ra_rank_share.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
     L.ra_rank_share_zigzag.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
+    L.ra_rank_share_padded.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, O]
     L.ra_rank_share_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, T, T, T, O]
     for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share, L.ra_rank_share_zigzag,
-              L.ra_rank_share_bwd):
+              L.ra_rank_share_bwd, L.ra_rank_share_padded):
         f.restype = ctypes.c_int
     L.ra_ring_block.argtypes = [i64, i64, i64]
     L.ra_ring_block.restype = i64
@@ -172,6 +173,15 @@ def ra_rank_share(q, k, v, P: int, rank: int, causal: bool, o_out, lse_out=None,
     opts, keep = _opts(stream, scale, o_out=o_out, lse_out=lse_out)
     _check(lib().ra_rank_share(_desc(q), _desc(k), _desc(v), int(P), int(rank), int(bool(causal)),
                                ctypes.byref(opts)))
+
+
+def ra_rank_share_padded(q, k, v, P: int, rank: int, causal: bool, n_valid: int, o_out, lse_out=None,
+                         scale: Optional[float] = None, stream=None) -> None:
+    """One rank's share of a sequence padded to N = P * ceil(n_valid / P) rows:
+    keys at positions >= n_valid are masked out."""
+    opts, keep = _opts(stream, scale, o_out=o_out, lse_out=lse_out)
+    _check(lib().ra_rank_share_padded(_desc(q), _desc(k), _desc(v), int(P), int(rank), int(bool(causal)),
+                                      int(n_valid), ctypes.byref(opts)))
 
 
 def ra_rank_share_zigzag(q, k, v, P: int, rank: int, causal: bool, o_out, lse_out=None,

@@ -93,6 +93,15 @@ def zigzag_gpu(q, k, v, P, rank, causal, o_dtype=torch.float32, scale=None):
     return O, lse
 
 
+def padded_gpu(q, k, v, P, rank, causal, n_valid, o_dtype=torch.float32, scale=None):
+    """Share of a sequence padded to k.shape[1] rows, the first n_valid real."""
+    B, nq, hq, d = q.shape
+    O = torch.full((B, nq, hq, d), float("nan"), dtype=o_dtype, device=q.device)
+    lse = torch.full((B, hq, nq), float("nan"), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share_padded(q, k, v, P, rank, causal, n_valid, O, lse, scale=scale)
+    return O, lse
+
+
 def backward_gpu(q, k, v, P, rank, causal, dout, scale=None):
     """Forward (bf16 O, LSE) then backward on the device; returns (dq, dk, dv) fp32."""
     B, nq, hq, d = q.shape

@@ -168,6 +168,22 @@ def test_ra_rank_share_zigzag_validation():
     assert zz(T([1, 0, 4, 128]), T([1, 0, 1, 128]), T([1, 0, 1, 128]), 8, 7, o_out=T([1, 0, 4, 128])) == ra.RA_OK
 
 
+def test_ra_rank_share_padded_validation():
+    def pad(q, k, v, Pn, rank, n_valid, o_out=None):
+        opts = ra.RaOpts()
+        if o_out is not None:
+            opts.o_out = ctypes.pointer(o_out)
+        return ra.lib().ra_rank_share_padded(P(q), P(k), P(v), Pn, rank, 1, n_valid, ctypes.byref(opts))
+    q, k, v = T([1, 512, 4, 128]), T([1, 4096, 1, 128]), T([1, 4096, 1, 128])
+    o = T([1, 512, 4, 128])
+    assert pad(q, k, v, 8, 7, 4000) == ra.RA_E_NULL               # no o_out
+    for bad in (0, -1, 4097):                                     # n_valid outside [1, N]
+        assert pad(q, k, v, 8, 7, bad, o_out=o) == ra.RA_E_RANGE, bad
+        assert "n_valid" in ra.ra_last_error()
+    assert pad(q, k, v, 8, 8, 4000, o_out=o) == ra.RA_E_RANGE     # rank outside [0, P)
+    assert pad(q, k, v, 4, 3, 4000, o_out=o) == ra.RA_E_SHAPE     # Nq != N / P
+
+
 def test_ra_rank_share_bwd_validation():
     def bwd(q, k, v, o, lse, dout, Pn, rank, dq, dk, dv, delta):
         return ra.lib().ra_rank_share_bwd(P(q), P(k), P(v), P(o), P(lse), P(dout), Pn, rank, 1, P(dq), P(dk),

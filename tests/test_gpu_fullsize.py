@@ -11,7 +11,7 @@ import torch
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
-                            say, stepwise_gpu, zigzag_gpu, zigzag_rows)
+                            padded_gpu, say, stepwise_gpu, zigzag_gpu, zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,26 @@ def test_full_size_zigzag_sampled_rows():
         assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"zigzag rank {r} bf16 O", out_bf16=True)
 
 
+
+
+def test_full_size_padded_sampled_rows():
+    """Rank-7-of-8 shape (N 32768, 32 heads, d 128) holding 32768 - 777 real
+    tokens: the last rank's block ends in 777 NaN padding keys."""
+    w = workloads.RANK7_BF16
+    n_valid = w.N - 777
+    say("padded full size: drawing inputs")
+    x = inputs.workload_inputs(w)
+    x["k"][:, n_valid:] = float("nan")
+    x["v"][:, n_valid:] = float("nan")
+    d = {k: t.to("cuda") for k, t in x.items()}
+    r = w.ranks[0]
+    O, lse = padded_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, n_valid, torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(w.B, w.Hq, w.nq, w.seed + 7).numpy()
+    say(f"padded full size rank {r}: oracle on {len(rows)} rows")
+    o_ref, l_ref = oracle.rank_share_padded(x["q"], x["k"], x["v"], w.P, r, w.causal, n_valid, rows=rows,
+                                            nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"padded rank {r} bf16 O", out_bf16=True)
 
 
 def test_full_size_backward_sampled_rows():

@@ -13,7 +13,7 @@ import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from sequence_transformer_attention_amd import ringattn as ra
 from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
-                            say, stepwise_gpu, zigzag_gpu, zigzag_rows)
+                            padded_gpu, say, stepwise_gpu, zigzag_gpu, zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +124,36 @@ def test_zigzag_share(dt, B, N, P, Hq, Hkv, d, causal, ranks):
         o_ref, l_ref = oracle.rank_share_zigzag(ql, x["k"], x["v"], P, r, causal, rows=rows,
                                                 nthreads=oracle_threads())
         assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"zigzag rank {r}")
+
+
+# ------------------------------------------------ padded (uneven length) share
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,n_valid,P,Hq,Hkv,d,causal,ranks", [
+    (1, 4000, 4, 2, 1, 128, True, (0, 3)),     # N 4000 = 4 x 1000: last block 1000 rows, 0 padding
+    (1, 3990, 4, 2, 1, 128, True, (1, 3)),     # N 3992: last block holds 990 real keys of 998
+    (2, 1133, 3, 2, 2, 64, False, (0, 2)),     # N 1134, no mask, B 2
+    (1, 700, 4, 4, 2, 128, True, (2, 3)),      # N 700: nb 175, ragged key tiles everywhere
+    (1, 1500, 4, 2, 1, 128, True, (3, 0)),     # N 1500 + padding block: n_valid < 3 nb + 1 for N 2000
+])
+def test_padded_share(dt, B, n_valid, P, Hq, Hkv, d, causal, ranks):
+    """Keys past n_valid hold NaN: a kernel that lets any of them into a sum fails."""
+    N = P * (-(-n_valid // P))
+    if n_valid == 1500:
+        N = 2000                               # the whole last block is padding
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=n_valid + P, dtype=dt)
+    x["k"][:, n_valid:] = float("nan")
+    x["v"][:, n_valid:] = float("nan")
+    dv = _dev(x)
+    nb = N // P
+    for r in ranks:
+        ql = x["q"][:, r * nb:(r + 1) * nb].contiguous()
+        say(f"padded {dt} B{B} N{N} n_valid{n_valid} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+        O, lse = padded_gpu(ql.to(DEV), dv["k"], dv["v"], P, r, causal, n_valid)
+        torch.cuda.synchronize()
+        rows = oracle.all_rows(B, Hq, nb)
+        o_ref, l_ref = oracle.rank_share_padded(ql, x["k"], x["v"], P, r, causal, n_valid, rows=rows,
+                                                nthreads=oracle_threads())
+        assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"padded rank {r}")
 
 
 def test_zigzag_shares_reassemble_full_attention():

@@ -246,6 +246,9 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the rank share only (no stepwise, load-balance or backward measurements), "
+                         "so that a profiler's per-kernel summary covers the timed launches alone")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -309,9 +312,12 @@ def main() -> int:
     log(f"{w.name}: {ms_per_step:.3f} ms/step, kernel mean {mean_ms:.3f} ms "
         f"(median {per[len(per) // 2]:.3f}, min {per[0]:.3f}) -> {achieved:.1f} TFLOP/s")
 
-    side = stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch)
-    balance = load_balance(w, r, qd, kd, vd, mean_ms, ra, torch)
-    bwd = backward(w, r, qd, kd, vd, flop, ra, torch)
+    if args.no_extras:
+        side, balance, bwd = {"stepwise": None, "finalize": None}, None, None
+    else:
+        side = stepwise_and_finalize(w, r, qd, kd, vd, flop, ra, torch)
+        balance = load_balance(w, r, qd, kd, vd, mean_ms, ra, torch)
+        bwd = backward(w, r, qd, kd, vd, flop, ra, torch)
 
     out = {
         "metric": "rank-share ring-attention TFLOP/s (bf16, causal) and % of MFMA bf16 peak",

@@ -171,7 +171,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
   const int nqt = (a.nq + BM - 1) / BM;
-  const int qt = blockIdx.x % nqt, hb = blockIdx.x / nqt;
+  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x);
+  int qt = logical % nqt;
+  const int hb = logical / nqt;
+  if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
   const int h = hb % a.Hq, b = hb / a.Hq, hk = h / (a.Hq / a.Hkv);
   const int qrow_wg = qt * BM, qrow_w = qrow_wg + wave * 32, my_q = qrow_w + lr;
   const bool q_ok = my_q < a.nq;
@@ -203,10 +206,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
   const int64_t q0_wg = a.q_off + qrow_wg, q0w = a.q_off + qrow_w;
   const int nq_wg = min(BM, a.nq - qrow_wg);
+  // Key block of loop step s: ring order with the rank's own block (ring
+  // step 0) last, so that all query tiles of a head walk the other blocks in
+  // lockstep and share the K/V stream in L2 (the own block's causal tile
+  // count differs per query tile).
+  auto blk = [&](int s) -> int64_t { return ra_plan_ring_block(a.P, a.rank, (s + 1) % a.P); };
   auto tiles = [&](int s) -> int {
-    return (int)ra_plan_key_tiles(q0_wg, nq_wg, ra_plan_ring_block(a.P, a.rank, s) * a.nb, a.nb, a.causal, BN);
+    return (int)ra_plan_key_tiles(q0_wg, nq_wg, blk(s) * a.nb, a.nb, a.causal, BN);
   };
-  // The workgroup's key tiles in ring order; the loads of the next tile are
+  // The workgroup's key tiles in that order; the loads of the next tile are
   // in flight while the current one is computed (two LDS stages).
   struct Cur {
     int s, u, nt;
@@ -215,7 +223,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
   auto cur_fix = [&](Cur& c) {  // move to the first tile of the first non-empty step from c.s on
     while (c.s < a.P && (c.nt = tiles(c.s)) == 0) ++c.s;
     c.u = 0;
-    c.k0 = c.s < a.P ? ra_plan_ring_block(a.P, a.rank, c.s) * a.nb : 0;
+    c.k0 = c.s < a.P ? blk(c.s) * a.nb : 0;
   };
   auto cur_next = [&](Cur& c) {
     if (++c.u < c.nt) return;
@@ -325,7 +333,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
   const int nkt = (int)((a.N + BK - 1) / BK);
-  const int kt = blockIdx.x % nkt, hb = blockIdx.x / nkt;
+  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % nkt, hb = logical / nkt;
   const int g = hb % a.Hkv, b = hb / a.Hkv, G = a.Hq / a.Hkv;
   const int64_t my_k = (int64_t)kt * BK + wave * 32 + lr;
   const bool k_ok = my_k < a.N;

@@ -69,14 +69,6 @@ __device__ __forceinline__ float vmax3(float x, float y, float z) {
   return r;
 }
 
-// Workgroups are handed to the 8 XCDs round-robin.  Give XCD x the contiguous
-// logical range [x * n/8, (x+1) * n/8) so that all query tiles of a head (and
-// the heads sharing a kv head) run on one XCD and share its L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
-  if (nwg % 8 != 0) return bid;
-  return (bid % 8) * (nwg / 8) + bid / 8;
-}
-
 // ---------------------------------------------------------------------------
 // bf16 path.
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -133,7 +125,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
   const int nqt_c = (nqc + BM - 1) / BM;
   const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x);
   int qt = logical % nqt;
   const int hb = logical / nqt;
   const int h = hb % a.Hq, b = hb / a.Hq;

@@ -29,6 +29,15 @@ RA_HD int ra_plan_ring_block32(int P, int rank, int s) {
   return j < 0 ? j + P : j;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin.  Logical workgroup of
+// hardware workgroup bid out of nwg: XCD x gets the contiguous logical range
+// [x * nwg/8, (x+1) * nwg/8), so that the tiles of one head (which stream the
+// same K/V or Q/dO tiles) run on one XCD and share its L2.
+RA_HD int ra_plan_xcd_remap(int bid, int nwg) {
+  if (nwg % 8 != 0) return bid;
+  return (bid % 8) * (nwg / 8) + bid / 8;
+}
+
 RA_HD int ra_plan_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, int causal) {
   if (nq <= 0 || nk <= 0) return RA_CLASS_SKIP;
   if (!causal) return RA_CLASS_FULL;

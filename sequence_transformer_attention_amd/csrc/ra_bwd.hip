@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
   const int nqt = (a.nq + BM - 1) / BM;
-  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x, nqt);
   int qt = logical % nqt;
   const int hb = logical / nqt;
   if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
   const int nkt = (int)((a.N + BK - 1) / BK);
-  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x, nkt);
   const int kt = logical % nkt, hb = logical / nkt;
   const int g = hb % a.Hkv, b = hb / a.Hkv, G = a.Hq / a.Hkv;
   const int64_t my_k = (int64_t)kt * BK + wave * 32 + lr;

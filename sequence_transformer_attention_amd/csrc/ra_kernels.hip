@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
   const int nqt_c = (nqc + BM - 1) / BM;
   const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
-  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x, nqt);
   int qt = logical % nqt;
   const int hb = logical / nqt;
   const int h = hb % a.Hq, b = hb / a.Hq;

@@ -29,13 +29,22 @@ RA_HD int ra_plan_ring_block32(int P, int rank, int s) {
   return j < 0 ? j + P : j;
 }
 
-// Workgroups are handed to the 8 XCDs round-robin.  Logical workgroup of
-// hardware workgroup bid out of nwg: XCD x gets the contiguous logical range
-// [x * nwg/8, (x+1) * nwg/8), so that the tiles of one head (which stream the
-// same K/V or Q/dO tiles) run on one XCD and share its L2.
-RA_HD int ra_plan_xcd_remap(int bid, int nwg) {
+// Workgroups are handed to the 8 XCDs round-robin (hardware workgroup bid
+// runs on XCD bid % 8, the (bid / 8)-th there).  Logical workgroup of bid,
+// for a grid of nwg whose logical order runs through one head's tiles (which
+// stream the same K/V or Q/dO tiles) in runs of `run`: XCD x gets
+// per = nwg / 8 logical workgroups, so that a head's tiles stay on as few
+// XCDs as possible and share their L2.  When a run spans k > 1 XCDs (k the
+// least power of two with k * per >= run), the k XCDs of a group take its
+// logical range [g k per, (g+1) k per) interleaved (member m gets i k + m),
+// so that heavy and light tiles (causal masking) are shared evenly instead of
+// one XCD getting all the late tiles.  A bijection on [0, nwg).
+RA_HD int ra_plan_xcd_remap(int bid, int nwg, int run) {
   if (nwg % 8 != 0) return bid;
-  return (bid % 8) * (nwg / 8) + bid / 8;
+  const int per = nwg / 8, x = bid % 8, i = bid / 8;
+  int k = 1;
+  while (k < 8 && k * per < run) k *= 2;
+  return (x / k) * k * per + i * k + (x % k);
 }
 
 RA_HD int ra_plan_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, int causal) {

@@ -1,0 +1,52 @@
+// Host checks of the workgroup-to-XCD order in csrc/ra_plan.h (built and run
+// by tests/test_plan_native.py with the host compiler).
+#include "ra_plan.h"
+
+#include <cstdio>
+#include <vector>
+
+int main() {
+  // a bijection on [0, nwg) for every grid and run length
+  for (int nwg : {1, 7, 8, 16, 24, 64, 256, 512, 1000, 1024, 2048, 8192})
+    for (int run : {1, 3, 16, 32, 64, 96, 128, 256, 1024, 4096}) {
+      std::vector<int> seen(nwg, 0);
+      for (int b = 0; b < nwg; ++b) {
+        const int l = ra_plan_xcd_remap(b, nwg, run);
+        if (l < 0 || l >= nwg) { std::printf("out of range: nwg %d run %d\n", nwg, run); return 1; }
+        ++seen[l];
+      }
+      for (int v : seen)
+        if (v != 1) { std::printf("not a bijection: nwg %d run %d\n", nwg, run); return 1; }
+    }
+  // causal work per XCD (query tile t of a head has t + 1 units, later tiles
+  // first) within 2 % of the mean, and each XCD holds tiles of as few heads
+  // as the grid allows
+  struct Case { int nqt, heads; };
+  for (Case c : {Case{256, 4}, Case{16, 32}, Case{32, 8}, Case{512, 2}, Case{1024, 1}}) {
+    const int nwg = c.nqt * c.heads;
+    double w[8] = {0};
+    std::vector<std::vector<int>> heads(8);
+    for (int b = 0; b < nwg; ++b) {
+      const int l = ra_plan_xcd_remap(b, nwg, c.nqt), qt = c.nqt - 1 - l % c.nqt, h = l / c.nqt;
+      w[b % 8] += qt + 1;
+      bool have = false;
+      for (int x : heads[b % 8]) have |= x == h;
+      if (!have) heads[b % 8].push_back(h);
+    }
+    double mean = 0;
+    for (double x : w) mean += x / 8;
+    const int want = c.heads >= 8 ? c.heads / 8 : 1;
+    for (int x = 0; x < 8; ++x) {
+      if (w[x] > 1.02 * mean || w[x] < 0.98 * mean) {
+        std::printf("unbalanced: nqt %d heads %d xcd %d work %g mean %g\n", c.nqt, c.heads, x, w[x], mean);
+        return 1;
+      }
+      if ((int)heads[x].size() != want) {
+        std::printf("xcd %d holds %zu heads (nqt %d heads %d)\n", x, heads[x].size(), c.nqt, c.heads);
+        return 1;
+      }
+    }
+  }
+  std::printf("ok\n");
+  return 0;
+}

@@ -18,20 +18,27 @@
 //   bwd_dq_kernel     4 waves x 32 query rows (Q and dO fragments stay in
 //                     registers as B operands); per 32-key unit of a
 //                     64-key K/V tile staged in LDS:
-//                       S^T = K Q^T, dP^T = V dO^T (A operands from LDS),
-//                       dS^T = P^T (dP^T - D) in fp32, then
+//                       S^T = K Q^T, then dP^T = V dO^T (A operands from
+//                       LDS, the V rows read into the registers the K rows
+//                       free), dS^T = P^T (dP^T - D) in fp32, then
 //                       dQ^T += K^T dS^T with K^T from the transposing
 //                       ds_read_b64_tr_b16 and dS^T from registers.
+//                     252 VGPRs: two workgroups (two waves per SIMD) per CU.
 //   bwd_dkdv_kernel   4 waves x 32 keys (K and V fragments stay in
 //                     registers as B operands); per 32-query unit of a
 //                     64-row Q/dO tile staged in LDS, for every query head
-//                     of the kv head:
-//                       S = Q K^T, dP = dO V^T (A operands from LDS),
-//                       P and dS in fp32 with LSE and D per query row, then
-//                       dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T
-//                       from transposing reads and P, dS from registers.
+//                     of the kv head, stage by stage:
+//                       S = Q K^T, then dP = dO V^T (A operands from LDS),
+//                       P (while the dP products run), dV^T += dO^T P with
+//                       dO^T from transposing reads, dS (while the dV
+//                       products run), dK^T += Q^T dS.
+//                     The dK, dV accumulators stay in AGPRs for the whole
+//                     walk (inline-asm MFMAs; the compiler otherwise copies
+//                     them between register files every iteration); one
+//                     wave per SIMD.
 // Both attention kernels use the forward's LDS layout (rows of 2d bytes,
-// 16-byte slots XOR-swizzled) and one-stage synchronous tile loads.
+// 16-byte slots XOR-swizzled), two LDS stages with the next tile's loads in
+// flight, and inline-asm LDS reads whose waits carry their registers.
 #include "ra_bwd.h"
 #include "ra_plan.h"
 
@@ -125,6 +132,36 @@ __device__ __forceinline__ bf16x8 read_tr(unsigned lo_addr, unsigned hi_addr, un
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// acc[i] += A_i * B (v_mfma_f32_32x32x16_bf16, i = 0..3) with the
+// accumulators pinned to AGPRs.  Inline asm, so the compiler cannot insert
+// the wait states an MFMA needs after a vector write of its operands: the
+// leading s_nop gives them (A and B may have just been formed by VALU
+// instructions).  Only other MFMAs of this form touch the accumulators until
+// mfma_acc_drain.
+__device__ __forceinline__ void mfma_acc4(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3, const u32x4& a0,
+                                          const u32x4& a1, const u32x4& a2, const u32x4& a3, const bf16x8& b) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3"
+      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b));
+}
+// Zero an accumulator with an MFMA (zero operands, inline-constant C), so
+// that it is born in AGPRs.
+__device__ __forceinline__ void mfma_acc_zero(f32x16& c) {
+  const bf16x8 z = bf16x8{};
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(c) : "v"(z));
+}
+// Wait until the MFMAs writing the accumulators are done before anything
+// else reads them (an 8-pass MFMA's result is read safely 11 wait states
+// later; 40 are given).
+__device__ __forceinline__ void mfma_acc_drain(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
+}
+
 // Load a 64-row tile (rows row0 .. row0 + nvalid - 1 of a [*, D] bf16 matrix
 // with row stride `stride` elements; rows past nvalid re-read the last one)
 // into LDS at dst, swizzled.  All NW waves take a share of 1 KiB chunks.
@@ -163,7 +200,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(RaBwdArgs a, int d) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
   constexpr int NW = 4, BM = NW * 32, BN = RA_BWD_BN, KC = D / 16, DB = D / 32, TILE = BN * D * 2;
   static_assert(BM == RA_BWD_BM, "query rows per workgroup");
   __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // two stages of (K tile, V tile)
@@ -253,26 +290,29 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(RaBwdArgs a) {
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
       constexpr unsigned ko = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // K unit; V unit at + TILE
-      // S^T = K Q^T and dP^T = V dO^T (keys x queries)
-      bf16x8 fk[KC], fv[KC];
+      // S^T = K Q^T, then dP^T = V dO^T (keys x queries): the V rows are read
+      // while the S^T products run, into the registers the K rows free
+      bf16x8 fk[KC];
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        ds_rd128<ko>(fk[c], ta.rd[c]);
-        ds_rd128<ko + TILE>(fv[c], ta.rd[c]);
-      }
+      for (int c = 0; c < KC; ++c) ds_rd128<ko>(fk[c], ta.rd[c]);
       if constexpr (KC == 8)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]), "+v"(fk[4]),
-                     "+v"(fk[5]), "+v"(fk[6]), "+v"(fk[7]), "+v"(fv[0]), "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]),
-                     "+v"(fv[4]), "+v"(fv[5]), "+v"(fv[6]), "+v"(fv[7]));
+                     "+v"(fk[5]), "+v"(fk[6]), "+v"(fk[7]));
       else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]), "+v"(fv[0]),
-                     "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]));
       f32x16 sacc = f32x16{}, dpa = f32x16{};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], qf[c], sacc, 0, 0, 0);
-        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c], dof[c], dpa, 0, 0, 0);
-      }
+      for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], qf[c], sacc, 0, 0, 0);
+      bf16x8 fv[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) ds_rd128<ko + TILE>(fv[c], ta.rd[c]);
+      if constexpr (KC == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fv[0]), "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]), "+v"(fv[4]),
+                     "+v"(fv[5]), "+v"(fv[6]), "+v"(fv[7]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fv[0]), "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c], dof[c], dpa, 0, 0, 0);
       // K^T for the dQ product, in flight while P^T and dS^T are formed
       u32x2 tlo[2][DB], thi[2][DB];
       static_for<0, 2 * DB>([&](auto X) {
@@ -352,7 +392,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   }
   f32x16 dka[DB], dva[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16{};
+  for (int db = 0; db < DB; ++db) {
+    mfma_acc_zero(dka[db]);
+    mfma_acc_zero(dva[db]);
+  }
   TileAddr<D> ta;
   ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0][0]), lane);
   const unsigned lsd_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) float*)&lsd[0][0][0]);
@@ -397,14 +440,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
       constexpr unsigned qo = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // Q unit; dO unit at + TILE
-      // S = Q K^T and dP = dO V^T (queries x keys); query row of register r:
-      // 8 (r / 4) + 4 lg + (r % 4)
-      bf16x8 fq[KC], fd[KC];
+      // Stage by stage, so that each operand set is live only as long as its
+      // products need it and the vector work of one product overlaps the
+      // MFMAs of the next: S (Q rows), dP (dO rows) with P formed meanwhile,
+      // dV (dO^T) with dS formed meanwhile, dK (Q^T).
+      // S = Q K^T (queries x keys); query row of register r: 8 (r / 4) + 4 lg + (r % 4)
+      bf16x8 fq[KC];
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        ds_rd128<qo>(fq[c], ta.rd[c]);
-        ds_rd128<qo + TILE>(fd[c], ta.rd[c]);
-      }
+      for (int c = 0; c < KC; ++c) ds_rd128<qo>(fq[c], ta.rd[c]);
       // LSE log2(e) and D of the lane's 16 query rows (4 runs of 4)
       f32x4 l4[4], d4[4];
       static_for<0, 4>([&](auto J) {
@@ -413,36 +456,43 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         ds_rd128<o4>(l4[j], lsd_lane);
         ds_rd128<o4 + BN * 4>(d4[j], lsd_lane);
       });
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]), "+v"(d4[0]),
-                   "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
       if constexpr (KC == 8)
-        asm volatile("" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fq[4]), "+v"(fq[5]), "+v"(fq[6]),
-                     "+v"(fq[7]), "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(fd[4]), "+v"(fd[5]),
-                     "+v"(fd[6]), "+v"(fd[7]));
+        asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fq[4]),
+                     "+v"(fq[5]), "+v"(fq[6]), "+v"(fq[7]));
       else
-        asm volatile("" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]),
-                     "+v"(fd[3]));
-      f32x16 sacc = f32x16{}, dpa = f32x16{};
+        asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]));
+      f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sacc, 0, 0, 0);
-        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], vf[c], dpa, 0, 0, 0);
-      }
-      // transposing reads of dO^T and Q^T for the dV and dK products, in
-      // flight while P and dS are formed
-      u32x2 tlo[2][2][DB], thi[2][2][DB];  // [dO / Q][16-row group][channel block]
-      static_for<0, 2 * 2 * DB>([&](auto X) {
-        constexpr int x = decltype(X)::value, w = x / (2 * DB), hh = (x / DB) % 2, d_ = x % DB;
-        constexpr unsigned off = qo + (w ? 0u : (unsigned)TILE) + (unsigned)hh * 32 * D;
-        ds_rdtr<off>(tlo[w][hh][d_], ta.tr[0][d_]);
-        ds_rdtr<off>(thi[w][hh][d_], ta.tr[1][d_]);
+      for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sacc, 0, 0, 0);
+      // dP = dO V^T
+      bf16x8 fd[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) ds_rd128<qo + TILE>(fd[c], ta.rd[c]);
+      if constexpr (KC == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(fd[4]),
+                     "+v"(fd[5]), "+v"(fd[6]), "+v"(fd[7]), "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]),
+                     "+v"(d4[0]), "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(l4[0]),
+                     "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]), "+v"(d4[0]), "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
+      f32x16 dpa = f32x16{};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], vf[c], dpa, 0, 0, 0);
+      // dO^T for the dV product, in flight while P is formed
+      u32x2 olo[2][DB], ohi[2][DB];
+      static_for<0, 2 * DB>([&](auto X) {
+        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
+        constexpr unsigned off = qo + (unsigned)TILE + (unsigned)hh * 32 * D;
+        ds_rdtr<off>(olo[hh][d_], ta.tr[0][d_]);
+        ds_rdtr<off>(ohi[hh][d_], ta.tr[1][d_]);
       });
       // visible: query row rb + e (e = 8 (r / 4) + (r % 4)) exists and, under
       // causal masking, is at or after this lane's key: lo <= e < hi
       const int rb = r0 + 32 * hf + 4 * lg;
       const int lo = a.causal ? (int)(my_k - a.q_off) - rb : -(1 << 30);
       const int hi = k_ok ? a.nq - rb : -(1 << 30);
-      bf16x8 pf[2], dsf[2];
+      float pv[16];
+      bf16x8 pf[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -450,27 +500,72 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
           const int r = 4 * j + i, e = 8 * j + i;
           float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]);
           asm volatile("" : "+v"(t));  // computed for every lane: no branch
-          const float p = (e >= lo && e < hi) ? t : 0.f;
-          pf[r >> 3][r & 7] = (__bf16)p;
-          dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - d4[j][i]));
+          pv[r] = (e >= lo && e < hi) ? t : 0.f;
+          pf[r >> 3][r & 7] = (__bf16)pv[r];
         }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 wd[DB];
 #pragma unroll
         for (int d_ = 0; d_ < DB; ++d_) {
-          u32x2 l0 = tlo[0][hh][d_], h0 = thi[0][hh][d_], l1 = tlo[1][hh][d_], h1 = thi[1][hh][d_];
-          asm volatile("" : "+v"(l0), "+v"(h0), "+v"(l1), "+v"(h1));
-          const u32x4 wd = {l0[0], l0[1], h0[0], h0[1]}, wq = {l1[0], l1[1], h1[0], h1[1]};
-          dva[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wd), pf[hh], dva[d_], 0, 0, 0);
-          dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), dsf[hh], dka[d_], 0, 0, 0);
+          u32x2 l0 = olo[hh][d_], h0 = ohi[hh][d_];
+          asm volatile("" : "+v"(l0), "+v"(h0));
+          wd[d_] = u32x4{l0[0], l0[1], h0[0], h0[1]};
         }
+        if constexpr (DB == 4) {
+          mfma_acc4(dva[0], dva[1], dva[2], dva[3], wd[0], wd[1], wd[2], wd[3], pf[hh]);
+        } else {
+#pragma unroll
+          for (int d_ = 0; d_ < DB; ++d_)
+            dva[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wd[d_]), pf[hh], dva[d_], 0, 0, 0);
+        }
+      }
+      // Q^T for the dK product, in flight while dS is formed
+      u32x2 qlo[2][DB], qhi[2][DB];
+      static_for<0, 2 * DB>([&](auto X) {
+        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
+        constexpr unsigned off = qo + (unsigned)hh * 32 * D;
+        ds_rdtr<off>(qlo[hh][d_], ta.tr[0][d_]);
+        ds_rdtr<off>(qhi[hh][d_], ta.tr[1][d_]);
+      });
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          dsf[r >> 3][r & 7] = (__bf16)(pv[r] * (dpa[r] - d4[j][i]));
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 wq[DB];
+#pragma unroll
+        for (int d_ = 0; d_ < DB; ++d_) {
+          u32x2 l1 = qlo[hh][d_], h1 = qhi[hh][d_];
+          asm volatile("" : "+v"(l1), "+v"(h1));
+          wq[d_] = u32x4{l1[0], l1[1], h1[0], h1[1]};
+        }
+        if constexpr (DB == 4) {
+          mfma_acc4(dka[0], dka[1], dka[2], dka[3], wq[0], wq[1], wq[2], wq[3], dsf[hh]);
+        } else {
+#pragma unroll
+          for (int d_ = 0; d_ < DB; ++d_)
+            dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq[d_]), dsf[hh], dka[d_], 0, 0, 0);
+        }
+      }
     });
   };
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; it += 2) {
     tile(it, std::integral_constant<int, 0>{});
     if (it + 1 < total) tile(it + 1, std::integral_constant<int, 1>{});
+  }
+#pragma unroll
+  for (int d_ = 0; d_ < DB; ++d_) {
+    mfma_acc_drain(dka[d_]);
+    mfma_acc_drain(dva[d_]);
   }
   if (!k_ok) return;
   float* kp = a.dk + (int64_t)b * a.dk_sb + my_k * a.dk_ss + (int64_t)g * a.dk_sh;

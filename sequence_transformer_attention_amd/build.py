@@ -17,6 +17,11 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 VALU instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs unless an operand constraint says otherwise: the
+    # dK/dV kernel pins its accumulators to AGPRs by inline asm, and without
+    # this the compiler would put every other MFMA result there too and copy
+    # it back for the vector code
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

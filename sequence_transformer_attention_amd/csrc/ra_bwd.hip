@@ -323,16 +323,25 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
       });
       // key index of register r: 8 (r / 4) + (r % 4) + 4 lg; keys below lim are visible
       const int nv = min(max(nvalid - 32 * hf, 0), 32);
-      const int64_t vis = a.causal ? q0w + lr - (k0 + 32 * hf) + 1 : nv;
-      const int lim = (int)(vis < nv ? (vis > 0 ? vis : 0) : nv);
       bf16x8 dsf[2];
+      // all 32 keys of the unit exist and precede the wave's first query: no test
+      if (nv == 32 && (!a.causal || k0 + 32 * hf + 31 <= q0w)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + (r & 3) + 4 * lg;
-        float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2);
-        asm volatile("" : "+v"(t));  // computed for every lane: no branch
-        const float p = kk < lim ? t : 0.f;
-        dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2);
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
+        }
+      } else {
+        const int64_t vis = a.causal ? q0w + lr - (k0 + 32 * hf) + 1 : nv;
+        const int lim = (int)(vis < nv ? (vis > 0 ? vis : 0) : nv);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + (r & 3) + 4 * lg;
+          float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2);
+          asm volatile("" : "+v"(t));  // computed for every lane: no branch
+          const float p = kk < lim ? t : 0.f;
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
+        }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -377,6 +386,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const int kt = logical % nkt, hb = logical / nkt;
   const int g = hb % a.Hkv, b = hb / a.Hkv, G = a.Hq / a.Hkv;
   const int64_t my_k = (int64_t)kt * BK + wave * 32 + lr;
+  // the wave's last key position under causal masking (none: no mask)
+  const int64_t kmax_w = a.causal ? (int64_t)kt * BK + wave * 32 + 31 : INT64_MIN / 2;
   const bool k_ok = my_k < a.N;
 
   bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7
@@ -486,23 +497,34 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         ds_rdtr<off>(olo[hh][d_], ta.tr[0][d_]);
         ds_rdtr<off>(ohi[hh][d_], ta.tr[1][d_]);
       });
-      // visible: query row rb + e (e = 8 (r / 4) + (r % 4)) exists and, under
-      // causal masking, is at or after this lane's key: lo <= e < hi
+      // visible: under causal masking, query row rb + e (e = 8 (r / 4) +
+      // (r % 4)) is at or after this lane's key: e >= lo.  Rows past the
+      // local block need no test (their LSE is +inf: P = 0, and D = 0), nor
+      // keys past the sequence (their P only reaches their own dK, dV
+      // columns, which are not stored).
       const int rb = r0 + 32 * hf + 4 * lg;
       const int lo = a.causal ? (int)(my_k - a.q_off) - rb : -(1 << 30);
-      const int hi = k_ok ? a.nq - rb : -(1 << 30);
       float pv[16];
       bf16x8 pf[2];
+      // the wave's last key at or before the unit's first query row: no test
+      if (kmax_w - a.q_off <= (int64_t)(r0 + 32 * hf)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i, e = 8 * j + i;
-          float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]);
-          asm volatile("" : "+v"(t));  // computed for every lane: no branch
-          pv[r] = (e >= lo && e < hi) ? t : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          pv[r] = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);
           pf[r >> 3][r & 7] = (__bf16)pv[r];
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i, e = 8 * j + i;
+            float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]);
+            asm volatile("" : "+v"(t));  // computed for every lane: no branch
+            pv[r] = e >= lo ? t : 0.f;
+            pf[r >> 3][r & 7] = (__bf16)pv[r];
+          }
+      }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {

@@ -460,18 +460,44 @@ double orc_share_flops_zigzag(int64_t B, int64_t N, int64_t P, int64_t rank, int
  *
  * Layout: q, dout [B, N/P, Hq, d]; k, v [B, N, Hkv, d]; contiguous fp64.
  * qrows: (b, h, i) triples of dQ rows, dq[r*d + c]; krows: (b, g, j)
- * triples (j a row of k/v, g a kv head) of dK/dV rows, dk/dv[r*d + c]. */
+ * triples (j a row of k/v, g a kv head) of dK/dV rows, dk/dv[r*d + c].
+ * Under the load-balanced layout (zigzag) the N/P local rows are chunks
+ * rank and 2P-1-rank of 2P, and the block a ring step brings is the
+ * sender's two chunks; the formulas are unchanged, only positions differ. */
 
 typedef struct {
     const double *q, *k, *v, *dout;
     int64_t B, N, P, rank, nb, hq, hkv, d;
     int causal;
     double scale;
+    int zigzag;
 } orc_bwd;
+
+/* sequence position of local query row i */
+static int64_t bwd_qpos(const orc_bwd *w, int64_t i)
+{
+    if (!w->zigzag) return w->rank * w->nb + i;
+    const int64_t c = w->nb / 2;
+    return i < c ? w->rank * c + i : (2 * w->P - 1 - w->rank) * c + (i - c);
+}
+
+/* key rows [lo[x], hi[x]) of the block at ring step st; returns their count */
+static int bwd_step_keys(const orc_bwd *w, int64_t st, int64_t lo[2], int64_t hi[2])
+{
+    const int64_t blk = orc_ring_block(w->P, w->rank, st);
+    if (!w->zigzag) {
+        lo[0] = blk * w->nb; hi[0] = lo[0] + w->nb;
+        return 1;
+    }
+    const int64_t c = w->nb / 2;
+    lo[0] = blk * c; hi[0] = lo[0] + c;
+    lo[1] = (2 * w->P - 1 - blk) * c; hi[1] = lo[1] + c;
+    return 2;
+}
 
 static int bwd_visible(const orc_bwd *w, int64_t i, int64_t j)
 {
-    return !w->causal || j <= w->rank * w->nb + i;
+    return !w->causal || j <= bwd_qpos(w, i);
 }
 
 static double bwd_dot(const double *a, const double *b, int64_t d)
@@ -491,12 +517,14 @@ static void bwd_row_stats(const orc_bwd *w, int64_t b, int64_t h, int64_t i, dou
     const double *qi = w->q + ((b * w->nb + i) * w->hq + h) * d;
     double m = -INFINITY;
     for (int64_t st = 0; st < w->P; ++st) {
-        const int64_t blk = orc_ring_block(w->P, w->rank, st);
-        for (int64_t j = blk * w->nb; j < (blk + 1) * w->nb; ++j) {
-            if (!bwd_visible(w, i, j)) continue;
-            s[j] = w->scale * bwd_dot(qi, w->k + ((b * w->N + j) * w->hkv + g) * d, d);
-            if (s[j] > m) m = s[j];
-        }
+        int64_t lo[2], hi[2];
+        const int nr = bwd_step_keys(w, st, lo, hi);
+        for (int x = 0; x < nr; ++x)
+            for (int64_t j = lo[x]; j < hi[x]; ++j) {
+                if (!bwd_visible(w, i, j)) continue;
+                s[j] = w->scale * bwd_dot(qi, w->k + ((b * w->N + j) * w->hkv + g) * d, d);
+                if (s[j] > m) m = s[j];
+            }
     }
     double l = 0.0;
     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
@@ -545,15 +573,17 @@ static void *bwd_run(void *arg)
             double *dq = J->out0 + r * d;
             for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
             for (int64_t st = 0; st < w->P; ++st) {
-                const int64_t blk = orc_ring_block(w->P, w->rank, st);
-                for (int64_t j = blk * w->nb; j < (blk + 1) * w->nb; ++j) {
-                    if (!bwd_visible(w, i, j)) continue;
-                    const double *kj = w->k + ((b * w->N + j) * w->hkv + g) * d;
-                    const double p = exp(s[j] - lse);
-                    const double dp = bwd_dot(doi, w->v + ((b * w->N + j) * w->hkv + g) * d, d);
-                    const double ds = p * (dp - D);
-                    for (int64_t c = 0; c < d; ++c) dq[c] += w->scale * ds * kj[c];
-                }
+                int64_t lo[2], hi[2];
+                const int nr = bwd_step_keys(w, st, lo, hi);
+                for (int x = 0; x < nr; ++x)
+                    for (int64_t j = lo[x]; j < hi[x]; ++j) {
+                        if (!bwd_visible(w, i, j)) continue;
+                        const double *kj = w->k + ((b * w->N + j) * w->hkv + g) * d;
+                        const double p = exp(s[j] - lse);
+                        const double dp = bwd_dot(doi, w->v + ((b * w->N + j) * w->hkv + g) * d, d);
+                        const double ds = p * (dp - D);
+                        for (int64_t c = 0; c < d; ++c) dq[c] += w->scale * ds * kj[c];
+                    }
             }
         } else {                       /* dK, dV row (b, g, j) */
             const int64_t b = J->rows[3 * r], g = J->rows[3 * r + 1], j = J->rows[3 * r + 2];
@@ -608,15 +638,15 @@ static int bwd_threads(orc_bwd_job proto, int64_t n, int nthreads)
     return err;
 }
 
-int orc_rank_share_bwd(const double *q, const double *k, const double *v, const double *dout,
-                       int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
-                       int causal, double scale,
-                       const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
-                       double *dq, double *dk, double *dv, int nthreads)
+static int rank_share_bwd(const double *q, const double *k, const double *v, const double *dout,
+                          int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
+                          int causal, double scale,
+                          const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
+                          double *dq, double *dk, double *dv, int nthreads, int zigzag)
 {
-    if (P <= 0 || N % P != 0 || hkv <= 0 || hq % hkv != 0 || d <= 0) return -3;
+    if (P <= 0 || N % (zigzag ? 2 * P : P) != 0 || hkv <= 0 || hq % hkv != 0 || d <= 0) return -3;
     if (rank < 0 || rank >= P) return -5;
-    const orc_bwd w = {q, k, v, dout, B, N, P, rank, N / P, hq, hkv, d, causal, scale};
+    const orc_bwd w = {q, k, v, dout, B, N, P, rank, N / P, hq, hkv, d, causal, scale, zigzag};
     const int64_t G = hq / hkv;
     for (int64_t r = 0; r < nqrows; ++r)
         if (qrows[3 * r] < 0 || qrows[3 * r] >= B || qrows[3 * r + 1] < 0 || qrows[3 * r + 1] >= hq ||
@@ -659,4 +689,26 @@ int orc_rank_share_bwd(const double *q, const double *k, const double *v, const 
 done:
     free(slot); free(heads); free(lse); free(D);
     return e;
+}
+
+int orc_rank_share_bwd(const double *q, const double *k, const double *v, const double *dout,
+                       int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
+                       int causal, double scale,
+                       const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
+                       double *dq, double *dk, double *dv, int nthreads)
+{
+    return rank_share_bwd(q, k, v, dout, B, N, P, rank, hq, hkv, d, causal, scale, qrows, nqrows, krows, nkrows,
+                          dq, dk, dv, nthreads, 0);
+}
+
+/* Backward of the load-balanced share: q, dout hold the rank's 2 N/(2P)
+ * rows (chunk rank, then chunk 2P-1-rank). */
+int orc_rank_share_zigzag_bwd(const double *q, const double *k, const double *v, const double *dout,
+                              int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
+                              int causal, double scale,
+                              const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
+                              double *dq, double *dk, double *dv, int nthreads)
+{
+    return rank_share_bwd(q, k, v, dout, B, N, P, rank, hq, hkv, d, causal, scale, qrows, nqrows, krows, nkrows,
+                          dq, dk, dv, nthreads, 1);
 }

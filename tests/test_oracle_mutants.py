@@ -36,6 +36,8 @@ MUTANTS = {
     "bwd_dv_uses_ds": ("dv[c] += p * doi[c];", "dv[c] += ds * doi[c];"),
     "bwd_D_from_q": ("*D_out = bwd_dot(w->dout + ((b * w->nb + i) * w->hq + h) * d, o, d);",
                      "*D_out = bwd_dot(w->dout + ((b * w->nb + i) * w->hq + h) * d, qi, d);"),
+    "bwd_zigzag_second_chunk": ("return i < c ? w->rank * c + i : (2 * w->P - 1 - w->rank) * c + (i - c);",
+                                "return i < c ? w->rank * c + i : (2 * w->P - 2 - w->rank) * c + (i - c);"),
     "padded_real_keys_off_by_one": ("const int64_t real = n_valid - j * nb;", "const int64_t real = n_valid + 1 - j * nb;"),
     "pairs_count_off_by_one": ("int64_t c = causal ? q_off + i - kv_off + 1 : nkv;", "int64_t c = causal ? q_off + i - kv_off : nkv;"),
 }
@@ -56,6 +58,7 @@ PINS = [
     lambda: pins.test_zigzag_flops_rule_and_balance(),
     lambda: pins.test_backward_matches_torch_autograd(1, 24, 3, 2, 1, 8, True),
     lambda: pins.test_padded_share_is_attention_over_the_real_keys(1, 22, 4, 2, 1, 8, True),
+    lambda: pins.test_zigzag_backward_matches_torch_autograd(1, 24, 3, 2, 1, 8, True),
 ]
 
 

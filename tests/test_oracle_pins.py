@@ -441,6 +441,56 @@ def test_backward_contributions_of_all_ranks_sum_to_full_attention():
     np.testing.assert_allclose(dv_sum, dv1, atol=TOL, rtol=0)
 
 
+def _zigzag_rows(N, P, r):
+    """Positions of rank r's load-balanced rows: chunk r, then chunk 2P-1-r of 2P."""
+    c = N // (2 * P)
+    return np.concatenate([np.arange(r * c, (r + 1) * c), np.arange((2 * P - 1 - r) * c, (2 * P - r) * c)])
+
+
+@pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal", [
+    (1, 24, 3, 2, 1, 8, True),     # chunks of 4, GQA
+    (2, 16, 2, 2, 2, 4, True),     # chunks of 4, B = 2
+    (1, 20, 2, 1, 1, 8, False),    # no mask
+])
+def test_zigzag_backward_matches_torch_autograd(B, N, P, Hq, Hkv, d, causal):
+    """dQ of the rank's rows and its dK, dV contribution equal torch fp64
+    autograd of full attention with the upstream gradient on those rows only."""
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=N * P + 5)
+    g = torch.Generator().manual_seed(11)
+    for r in range(P):
+        pos = _zigzag_rows(N, P, r)
+        dout = torch.randn(B, len(pos), Hq, d, generator=g, dtype=torch.float64)
+        qq = q.clone().requires_grad_(True)
+        kk = k.clone().requires_grad_(True)
+        vv = v.clone().requires_grad_(True)
+        O, _ = _torch_attention(qq, kk, vv, 0, 0, causal, 0.45)
+        dfull = torch.zeros(B, N, Hq, d, dtype=torch.float64)
+        dfull[:, pos] = dout
+        (O * dfull).sum().backward()
+        dq, dk, dv = oracle.rank_share_bwd(q[:, pos], k, v, dout, P, r, causal, 0.45, zigzag=True)
+        np.testing.assert_allclose(_grid(dq, B, Hq, len(pos)), qq.grad[:, pos].numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(_grid(dk, B, Hkv, N), kk.grad.numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(_grid(dv, B, Hkv, N), vv.grad.numpy(), atol=TOL, rtol=0)
+
+
+def test_zigzag_backward_contributions_sum_to_full_attention():
+    B, N, P, Hq, Hkv, d = 1, 32, 4, 2, 1, 8
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=13)
+    dout = torch.randn(B, N, Hq, d, generator=torch.Generator().manual_seed(3), dtype=torch.float64)
+    dk_sum = np.zeros((B * Hkv * N, d)); dv_sum = np.zeros_like(dk_sum)
+    dq_all = np.zeros((B, N, Hq, d))
+    for r in range(P):
+        pos = _zigzag_rows(N, P, r)
+        dq, dk, dv = oracle.rank_share_bwd(q[:, pos], k, v, dout[:, pos], P, r, True, 0.3, zigzag=True)
+        dk_sum += dk
+        dv_sum += dv
+        dq_all[:, pos] = _grid(dq, B, Hq, len(pos))
+    dq1, dk1, dv1 = oracle.rank_share_bwd(q, k, v, dout, 1, 0, True, 0.3)
+    np.testing.assert_allclose(dq_all, _grid(dq1, B, Hq, N), atol=TOL, rtol=0)
+    np.testing.assert_allclose(dk_sum, dk1, atol=TOL, rtol=0)
+    np.testing.assert_allclose(dv_sum, dv1, atol=TOL, rtol=0)
+
+
 # ------------------------------------------------------------ input generator
 def test_inputs_are_deterministic_and_seeded():
     a = inputs.draw_qkv(1, 64, 128, 4, 2, 16, seed=7)

@@ -176,6 +176,19 @@ int ra_rank_share_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v
                       const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
                       const ra_tensor *delta, const ra_opts *opts);
 
+/* Backward of the load-balanced share (ra_rank_share_zigzag's forward):
+ * the same computation as ra_rank_share_bwd with the rank's N/P local rows
+ * being chunk `rank` (rows [0, N/(2P))) and chunk 2P-1-rank (the rest) of
+ * 2P equal chunks, at those chunks' sequence positions; dk, dv again hold
+ * this rank's contribution for every key row.  Arguments, layouts, dtypes
+ * and ownership as ra_rank_share_bwd (o and lse from ra_rank_share_zigzag);
+ * N not divisible by 2P is RA_E_SHAPE. */
+int ra_rank_share_zigzag_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                             const ra_tensor *o, const ra_tensor *lse, const ra_tensor *dout,
+                             int P, int rank, int causal,
+                             const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
+                             const ra_tensor *delta, const ra_opts *opts);
+
 /* ---- host-only queries (no GPU needed) --------------------------------- */
 
 /* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1. */

@@ -309,19 +309,23 @@ int ra_rank_share_zigzag(const ra_tensor* q, const ra_tensor* k, const ra_tensor
   return rank_share(q, k, v, P, rank, causal, opts, 1, -1);
 }
 
-int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
-                      const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal, const ra_tensor* dq,
-                      const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta, const ra_opts* opts) {
+static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
+                          const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
+                          const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta,
+                          const ra_opts* opts, int zigzag) {
+  const char* fn = zigzag ? "ra_rank_share_zigzag_bwd" : "ra_rank_share_bwd";
   int e = check_qkv(q, k, v, "k", "v");
   if (e) return e;
-  if (q->dtype != RA_BF16) return fail(RA_E_UNSUPPORTED, "ra_rank_share_bwd takes bf16 q, k, v");
+  if (q->dtype != RA_BF16) return fail(RA_E_UNSUPPORTED, "%s takes bf16 q, k, v", fn);
   if (P < 1) return fail(RA_E_RANGE, "P must be >= 1 (got %d)", P);
   if (rank < 0 || rank >= P) return fail(RA_E_RANGE, "rank %d outside [0, %d)", rank, P);
   const int64_t B = q->shape[0], nq = q->shape[1], hq = q->shape[2], d = q->shape[3];
   const int64_t N = k->shape[1];
-  if (N % P != 0)
-    return fail(RA_E_SHAPE, "sequence length %lld is not divisible by P = %d (no implicit padding)", (long long)N, P);
-  const int64_t nb = N / P;
+  const int64_t parts = zigzag ? 2 * (int64_t)P : P;
+  if (N % parts != 0)
+    return fail(RA_E_SHAPE, "sequence length %lld is not divisible by %s = %lld (no implicit padding)",
+                (long long)N, zigzag ? "2P" : "P", (long long)parts);
+  const int64_t nb = N / P;  // local rows either way (zigzag: two chunks of N/(2P))
   if (nq != nb) return fail(RA_E_SHAPE, "local query block has %lld rows, expected N/P = %lld", (long long)nq, (long long)nb);
   if ((e = check_out(o, q, "o")) || (e = check_out(dout, q, "dout")) || (e = check_out(dq, q, "dq"))) return e;
   if (o->dtype != RA_BF16 || dout->dtype != RA_BF16) return fail(RA_E_DTYPE, "o and dout must be bf16");
@@ -330,7 +334,8 @@ int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
   if (!same_shape(dk, k) || !same_shape(dv, k)) return fail(RA_E_SHAPE, "dk and dv must have the shape of k");
   if (dk->dtype != RA_F32 || dv->dtype != RA_F32) return fail(RA_E_DTYPE, "dk and dv must be fp32");
   if ((e = check_rows(lse, "lse", B, hq, nq)) || (e = check_rows(delta, "delta", B, hq, nq))) return e;
-  if ((e = check_grid(nq, RA_BWD_BM, hq, B)) || (e = check_grid(N, RA_BWD_BM, k->shape[2], B))) return e;
+  const int64_t qrows = zigzag ? 2 * ((N / parts + RA_BWD_BM - 1) / RA_BWD_BM) * RA_BWD_BM : nq;
+  if ((e = check_grid(qrows, RA_BWD_BM, hq, B)) || (e = check_grid(N, RA_BWD_BM, k->shape[2], B))) return e;
   if (B == 0 || nq == 0) return ok();
 
   RaBwdArgs a{};
@@ -347,9 +352,29 @@ int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
   a.B = (int32_t)B; a.Hq = (int32_t)hq; a.Hkv = (int32_t)k->shape[2]; a.nq = (int32_t)nq;
   a.N = N; a.nb = nb; a.q_off = (int64_t)rank * nb;
   a.P = P; a.rank = rank; a.causal = causal ? 1 : 0;
+  a.nsplit = 1;
+  if (zigzag) {
+    const int64_t c = N / parts;
+    a.nsplit = 2; a.qc = c; a.q_off = (int64_t)rank * c;
+    a.rank2 = (int32_t)(parts - 1 - rank); a.q_off2 = (parts - 1 - rank) * c;
+  }
   a.scale = resolve_scale(opts, d);
   a.c = a.scale * 1.4426950408889634f;
-  return launched(ra_launch_bwd(a, (int)d, stream_of(opts)), "ra_rank_share_bwd launch");
+  return launched(ra_launch_bwd(a, (int)d, stream_of(opts)), zigzag ? "ra_rank_share_zigzag_bwd launch"
+                                                                     : "ra_rank_share_bwd launch");
+}
+
+int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
+                      const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal, const ra_tensor* dq,
+                      const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta, const ra_opts* opts) {
+  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 0);
+}
+
+int ra_rank_share_zigzag_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
+                             const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
+                             const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta,
+                             const ra_opts* opts) {
+  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 1);
 }
 
 int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s) {

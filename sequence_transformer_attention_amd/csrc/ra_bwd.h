@@ -28,6 +28,12 @@ struct RaBwdArgs {
   int32_t B, Hq, Hkv, nq;
   int64_t N, nb, q_off;
   int32_t P, rank, causal;
+  // query split of the load-balanced share (nsplit = 2): local rows
+  // [0, qc) at positions q_off.. (ring rank `rank` over 2P chunks of qc
+  // keys), rows [qc, 2qc) at positions q_off2.. (ring rank rank2); nsplit = 1:
+  // one block of nq rows, P blocks of nb keys
+  int32_t nsplit, rank2;
+  int64_t qc, q_off2;
   float c;       // softmax scale * log2(e)
   float scale;   // softmax scale
 };

@@ -207,14 +207,22 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
-  const int nqt = (a.nq + BM - 1) / BM;
+  // query chunks (two under the load-balanced split), each with its own
+  // positions and ring order over Pe blocks of nbe keys
+  const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
+  const int nqt_c = (nqc + BM - 1) / BM, nqt = a.nsplit * nqt_c;
   const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x, nqt);
   int qt = logical % nqt;
   const int hb = logical / nqt;
   if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
+  const int chunk = qt / nqt_c;
+  const int64_t qpos0 = chunk ? a.q_off2 : a.q_off;  // position of the chunk's first row
+  const int rank_e = chunk ? a.rank2 : a.rank, Pe = a.nsplit * a.P;
+  const int64_t nbe = a.nsplit == 2 ? a.qc : a.nb;
   const int h = hb % a.Hq, b = hb / a.Hq, hk = h / (a.Hq / a.Hkv);
-  const int qrow_wg = qt * BM, qrow_w = qrow_wg + wave * 32, my_q = qrow_w + lr;
-  const bool q_ok = my_q < a.nq;
+  const int qrow_wg = (qt - chunk * nqt_c) * BM, qrow_w = qrow_wg + wave * 32;  // rows within the chunk
+  const int my_q = chunk * nqc + qrow_w + lr;                                  // local row
+  const bool q_ok = qrow_w + lr < nqc;
 
   bf16x8 qf[KC], dof[KC];  // lane: row my_q, elements 16c + 8lg .. +7
   {
@@ -241,15 +249,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
 
   const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
-  const int64_t q0_wg = a.q_off + qrow_wg, q0w = a.q_off + qrow_w;
-  const int nq_wg = min(BM, a.nq - qrow_wg);
+  const int64_t q0_wg = qpos0 + qrow_wg, q0w = qpos0 + qrow_w;
+  const int nq_wg = min(BM, nqc - qrow_wg);
   // Key block of loop step s: ring order with the rank's own block (ring
   // step 0) last, so that all query tiles of a head walk the other blocks in
   // lockstep and share the K/V stream in L2 (the own block's causal tile
   // count differs per query tile).
-  auto blk = [&](int s) -> int64_t { return ra_plan_ring_block(a.P, a.rank, (s + 1) % a.P); };
+  auto blk = [&](int s) -> int64_t { return ra_plan_ring_block(Pe, rank_e, (s + 1) % Pe); };
   auto tiles = [&](int s) -> int {
-    return (int)ra_plan_key_tiles(q0_wg, nq_wg, blk(s) * a.nb, a.nb, a.causal, BN);
+    return (int)ra_plan_key_tiles(q0_wg, nq_wg, blk(s) * nbe, nbe, a.causal, BN);
   };
   // The workgroup's key tiles in that order; the loads of the next tile are
   // in flight while the current one is computed (two LDS stages).
@@ -258,9 +266,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
     int64_t k0;
   };
   auto cur_fix = [&](Cur& c) {  // move to the first tile of the first non-empty step from c.s on
-    while (c.s < a.P && (c.nt = tiles(c.s)) == 0) ++c.s;
+    while (c.s < Pe && (c.nt = tiles(c.s)) == 0) ++c.s;
     c.u = 0;
-    c.k0 = c.s < a.P ? blk(c.s) * a.nb : 0;
+    c.k0 = c.s < Pe ? blk(c.s) * nbe : 0;
   };
   auto cur_next = [&](Cur& c) {
     if (++c.u < c.nt) return;
@@ -268,12 +276,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
     cur_fix(c);
   };
   int total = 0;
-  for (int s = 0; s < a.P; ++s) total += tiles(s);
+  for (int s = 0; s < Pe; ++s) total += tiles(s);
   Cur cc{0, 0, 0, 0}, cl{0, 0, 0, 0};  // compute cursor, load cursor
   cur_fix(cc);
   cur_fix(cl);
   auto issue = [&](int st) __attribute__((always_inline)) {
-    const int64_t k0 = cl.k0 + (int64_t)cl.u * BN, left = a.nb - (int64_t)cl.u * BN;
+    const int64_t k0 = cl.k0 + (int64_t)cl.u * BN, left = nbe - (int64_t)cl.u * BN;
     const int nvalid = left < BN ? (int)left : BN;
     load_tile<D, NW>(kb + k0 * a.k_ss, a.k_ss, nvalid, &smem[st][0][0], wave, lane);
     load_tile<D, NW>(vb + k0 * a.v_ss, a.v_ss, nvalid, &smem[st][1][0], wave, lane);
@@ -281,7 +289,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
   };
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
-    const int64_t k0 = cc.k0 + (int64_t)cc.u * BN, left = a.nb - (int64_t)cc.u * BN;
+    const int64_t k0 = cc.k0 + (int64_t)cc.u * BN, left = nbe - (int64_t)cc.u * BN;
     const int nvalid = left < BN ? (int)left : BN;
     cur_next(cc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -412,26 +420,47 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const unsigned lsd_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) float*)&lsd[0][0][0]);
 
   // Local query rows that see any key of the workgroup: under causal
-  // masking those at positions >= the first key's.  The work is the list of
-  // (query head of the kv head, 64-row tile) pairs, walked with the loads of
-  // the next pair in flight during the current one.
+  // masking those at positions >= the first key's, per query chunk (two
+  // under the load-balanced split, each with its own positions).  The work
+  // is the list of (query head of the kv head, 64-row tile) pairs, walked
+  // with the loads of the next pair in flight during the current one.
   const int64_t kfirst = (int64_t)kt * BK;
-  int64_t qlo = a.causal ? kfirst - a.q_off : 0;
-  qlo = qlo < 0 ? 0 : qlo;
-  const int ntq = (a.nq + BN - 1) / BN;
-  const int t0 = qlo >= a.nq ? ntq : (int)(qlo / BN);
-  const int nt = ntq - t0, total = G * nt;
+  const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
+  const int ntq = (nqc + BN - 1) / BN;  // tiles per chunk
+  auto first_tile = [&](int64_t qpos) -> int {
+    int64_t qlo = a.causal ? kfirst - qpos : 0;
+    qlo = qlo < 0 ? 0 : qlo;
+    return qlo >= nqc ? ntq : (int)(qlo / BN);
+  };
+  const int t0a = first_tile(a.q_off), t0b = a.nsplit == 2 ? first_tile(a.q_off2) : ntq;
+  const int na = ntq - t0a, nt = na + (ntq - t0b), total = G * nt;
+  // tile it of the walk: query head, first local row, rows in its chunk,
+  // position of its first row
+  struct TileRef {
+    int h, r0, nvalid;
+    int64_t qp0;
+  };
+  auto tile_ref = [&](int it) -> TileRef {
+    const int w = it % nt, ch = w >= na ? 1 : 0;
+    const int t = ch ? t0b + (w - na) : t0a + w;
+    TileRef r;
+    r.h = g * G + it / nt;
+    r.r0 = ch * nqc + t * BN;
+    r.nvalid = min(BN, nqc - t * BN);
+    r.qp0 = (ch ? a.q_off2 : a.q_off) + (int64_t)t * BN;
+    return r;
+  };
   float lsv = 0.f, dlv = 0.f;  // threads 0..63: LSE log2(e) and D of row tid of the tile in flight
   auto issue = [&](int it, int st) __attribute__((always_inline)) {
-    const int h = g * G + it / nt, r0 = (t0 + it % nt) * BN;
-    const int nvalid = min(BN, a.nq - r0);
+    const TileRef tr = tile_ref(it);
+    const int h = tr.h, r0 = tr.r0, nvalid = tr.nvalid;
     load_tile<D, NW>((const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss, a.q_ss,
                      nvalid, &smem[st][0][0], wave, lane);
     load_tile<D, NW>((const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)r0 * a.do_ss,
                      a.do_ss, nvalid, &smem[st][1][0], wave, lane);
     if (tid < BN) {
       const int row = r0 + tid;
-      const bool ok = row < a.nq;
+      const bool ok = tid < nvalid;
       lsv = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e : INFINITY;
       dlv = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
     }
@@ -440,7 +469,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // One tile: stage ST (compile time, so every LDS offset is an immediate).
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
-    const int r0 = (t0 + it % nt) * BN;
+    const int64_t qp0 = tile_ref(it).qp0;
+    // this lane's key relative to the tile's first query position (bounded
+    // above by the tile walk; saturated below)
+    const int64_t rel64 = my_k - qp0;
+    const int rel = rel64 < -(1 << 30) ? -(1 << 30) : (int)rel64;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (tid < BN) {
       lsd[st][0][tid] = lsv;
@@ -497,17 +530,16 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         ds_rdtr<off>(olo[hh][d_], ta.tr[0][d_]);
         ds_rdtr<off>(ohi[hh][d_], ta.tr[1][d_]);
       });
-      // visible: under causal masking, query row rb + e (e = 8 (r / 4) +
-      // (r % 4)) is at or after this lane's key: e >= lo.  Rows past the
-      // local block need no test (their LSE is +inf: P = 0, and D = 0), nor
-      // keys past the sequence (their P only reaches their own dK, dV
-      // columns, which are not stored).
-      const int rb = r0 + 32 * hf + 4 * lg;
-      const int lo = a.causal ? (int)(my_k - a.q_off) - rb : -(1 << 30);
+      // visible: under causal masking, the query at position qp0 + 32 hf +
+      // 4 lg + e (e = 8 (r / 4) + (r % 4)) is at or after this lane's key:
+      // e >= lo.  Rows past their chunk need no test (their LSE is +inf:
+      // P = 0, and D = 0), nor keys past the sequence (their P only reaches
+      // their own dK, dV columns, which are not stored).
+      const int lo = a.causal ? rel - 32 * hf - 4 * lg : -(1 << 30);
       float pv[16];
       bf16x8 pf[2];
       // the wave's last key at or before the unit's first query row: no test
-      if (kmax_w - a.q_off <= (int64_t)(r0 + 32 * hf)) {
+      if (kmax_w <= qp0 + 32 * hf) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           pv[r] = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);
@@ -609,7 +641,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
 hipError_t ra_launch_bwd(const RaBwdArgs& a, int d, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a, d);
-  const dim3 gq((unsigned)((int64_t)((a.nq + RA_BWD_BM - 1) / RA_BWD_BM) * a.Hq * a.B)), block(256);
+  const int64_t nqc = a.nsplit == 2 ? a.qc : a.nq;
+  const dim3 gq((unsigned)((int64_t)a.nsplit * ((nqc + RA_BWD_BM - 1) / RA_BWD_BM) * a.Hq * a.B)), block(256);
   const dim3 gk((unsigned)(((a.N + RA_BWD_BM - 1) / RA_BWD_BM) * a.Hkv * a.B));
   if (d == 128) {
     hipLaunchKernelGGL(bwd_dq_kernel<128>, gq, block, 0, st, a);

@@ -207,6 +207,29 @@ def test_ra_rank_share_bwd_validation():
     assert bwd(**f32) == ra.RA_E_UNSUPPORTED
 
 
+def test_ra_rank_share_zigzag_bwd_validation():
+    def bwd(q, k, v, o, lse, dout, Pn, rank, dq, dk, dv, delta):
+        return ra.lib().ra_rank_share_zigzag_bwd(P(q), P(k), P(v), P(o), P(lse), P(dout), Pn, rank, 1, P(dq),
+                                                 P(dk), P(dv), P(delta), None)
+    q, k, v = T([1, 512, 4, 128]), T([1, 4096, 1, 128]), T([1, 4096, 1, 128])
+    o, do = T([1, 512, 4, 128]), T([1, 512, 4, 128])
+    dq = T([1, 512, 4, 128], ra.RA_F32)
+    dk, dv = T([1, 4096, 1, 128], ra.RA_F32), T([1, 4096, 1, 128], ra.RA_F32)
+    good = dict(q=q, k=k, v=v, o=o, lse=rows(1, 4, 512), dout=do, Pn=8, rank=7, dq=dq, dk=dk, dv=dv,
+                delta=rows(1, 4, 512))
+    assert bwd(**dict(good, rank=8)) == ra.RA_E_RANGE
+    assert bwd(**dict(good, q=None)) == ra.RA_E_NULL
+    # N = 4104 is divisible by P = 8 but not by 2P
+    k3, v3 = T([1, 4104, 1, 128]), T([1, 4104, 1, 128])
+    q3 = T([1, 513, 4, 128])
+    bad = dict(good, q=q3, k=k3, v=v3, o=T([1, 513, 4, 128]), dout=T([1, 513, 4, 128]),
+               dq=T([1, 513, 4, 128], ra.RA_F32), dk=T([1, 4104, 1, 128], ra.RA_F32),
+               dv=T([1, 4104, 1, 128], ra.RA_F32), lse=rows(1, 4, 513), delta=rows(1, 4, 513))
+    assert bwd(**bad) == ra.RA_E_SHAPE
+    assert "2P" in ra.ra_last_error()
+    assert bwd(**dict(good, Pn=4, rank=3)) == ra.RA_E_SHAPE        # Nq != N / P
+
+
 def test_ra_finalize_validation():
     L = ra.lib()
     oacc, l = T([1, 64, 2, 64], ra.RA_F32), rows(1, 2, 64)

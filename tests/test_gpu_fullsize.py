@@ -11,7 +11,7 @@ import torch
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
-                            padded_gpu, say, stepwise_gpu, zigzag_gpu, zigzag_rows)
+                            padded_gpu, say, stepwise_gpu, zigzag_backward_gpu, zigzag_gpu, zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +105,31 @@ def test_full_size_backward_sampled_rows():
     assert_grad_close(dk[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dk_r, "dK full size")
     assert_grad_close(dv[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dv_r, "dV full size")
 
+
+def test_full_size_zigzag_backward_sampled_rows():
+    """Backward of the last rank's load-balanced share at the rank-7-of-8 size
+    (N 32768, 32 heads, d 128): sampled dQ rows of both chunks and dK/dV rows
+    of kv head 0 over the whole sequence."""
+    w = workloads.RANK7_BF16
+    r = w.P - 1
+    x = inputs.draw_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.d, w.seed + 200, w.dtype, w.dist)
+    pos = zigzag_rows(w.N, w.P, r)
+    ql = x["q"][:, pos].contiguous()
+    nq = len(pos)
+    dout = torch.randn(w.B, nq, w.Hq, w.d, generator=torch.Generator().manual_seed(w.seed + 3)).to(torch.bfloat16)
+    say("zigzag backward full size: forward + backward on the GPU")
+    dq, dk, dv = zigzag_backward_gpu(ql.to("cuda"), x["k"].to("cuda"), x["v"].to("cuda"), w.P, r, w.causal,
+                                     dout.to("cuda"))
+    torch.cuda.synchronize()
+    qrows = inputs.sample_rows(w.B, w.Hq, nq, w.seed + 4).numpy()[:512]
+    g = torch.Generator().manual_seed(w.seed + 5)
+    krows = torch.stack([torch.zeros(256, dtype=torch.long), torch.zeros(256, dtype=torch.long),
+                         torch.randint(0, w.N, (256,), generator=g)], 1).numpy()
+    say(f"zigzag backward full size: oracle on {len(qrows)} dQ rows and {len(krows)} dK/dV rows")
+    dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, w.P, r, w.causal, qrows=qrows, krows=krows,
+                                             nthreads=oracle_threads(), zigzag=True)
+    qi = torch.as_tensor(qrows)
+    ki = torch.as_tensor(krows)
+    assert_grad_close(dq[qi[:, 0], qi[:, 2], qi[:, 1]].double().cpu().numpy(), dq_r, "zigzag dQ full size")
+    assert_grad_close(dk[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dk_r, "zigzag dK full size")
+    assert_grad_close(dv[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dv_r, "zigzag dV full size")

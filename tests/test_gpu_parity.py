@@ -13,7 +13,7 @@ import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from sequence_transformer_attention_amd import ringattn as ra
 from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
-                            padded_gpu, say, stepwise_gpu, zigzag_gpu, zigzag_rows)
+                            padded_gpu, say, stepwise_gpu, zigzag_backward_gpu, zigzag_gpu, zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -196,6 +196,31 @@ def test_backward_share(B, N, P, Hq, Hkv, d, causal, ranks):
         assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nb), f"dQ rank {r}")
         assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"dK rank {r}")
         assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"dV rank {r}")
+
+
+@pytest.mark.parametrize("B,N,P,Hq,Hkv,d,causal,ranks", [
+    (1, 2048, 4, 2, 1, 128, True, (0, 3)),     # chunks of 256 rows, GQA
+    (2, 1200, 3, 2, 2, 64, True, (1, 2)),      # chunks of 200: ragged tiles in both chunks, B = 2
+    (1, 1024, 2, 2, 2, 128, False, (0,)),      # no mask
+])
+def test_zigzag_backward_share(B, N, P, Hq, Hkv, d, causal, ranks):
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=N + 5 * P)
+    dv_ = _dev(x)
+    g = torch.Generator().manual_seed(N + 1)
+    for r in ranks:
+        pos = zigzag_rows(N, P, r)
+        ql = x["q"][:, pos].contiguous()
+        nq = len(pos)
+        dout = torch.randn(B, nq, Hq, d, generator=g).to(torch.bfloat16)
+        say(f"zigzag backward B{B} N{N} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+        dq, dk, dv = zigzag_backward_gpu(ql.to(DEV), dv_["k"], dv_["v"], P, r, causal, dout.to(DEV))
+        torch.cuda.synchronize()
+        dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, P, r, causal, nthreads=oracle_threads(),
+                                                 zigzag=True)
+        grid = lambda a, H, S: a.reshape(B, H, S, d).transpose(0, 2, 1, 3)
+        assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nq), f"zigzag dQ rank {r}")
+        assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"zigzag dK rank {r}")
+        assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"zigzag dV rank {r}")
 
 
 # ------------------------------------------------------------------ edge cases

@@ -202,7 +202,8 @@ def load_balance(w, r, qd, kd, vd, mean_ms, ra, torch, reps: int = 5):
 def backward(w, r, qd, kd, vd, flop, ra, torch, reps: int = 5):
     """ra_rank_share_bwd on the same share (bf16 only): the algorithmic FLOP
     of the backward is 2.5x the forward's (five products per visible pair:
-    S, dP, dV, dQ, dK, against two)."""
+    S, dP, dV, dQ, dK, against two).  Under causal masking also
+    ra_rank_share_zigzag_bwd of the first and last rank."""
     if w.dtype != "bf16":
         return None
     dev = qd.device
@@ -234,8 +235,37 @@ def backward(w, r, qd, kd, vd, flop, ra, torch, reps: int = 5):
     bf = 2.5 * flop
     log(f"backward (prep + dQ + dK/dV): {ms:.3f} ms -> {bf / ms / 1e9:.1f} TFLOP/s "
         f"({100 * bf / ms / 1e9 / PEAK_BF16_TFLOPS:.1f} % of peak)")
-    return {"ms": round(ms, 4), "flop": bf, "tflops": round(bf / ms / 1e9, 3),
-            "frac_of_peak": round(bf / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    out = {"ms": round(ms, 4), "flop": bf, "tflops": round(bf / ms / 1e9, 3),
+           "frac_of_peak": round(bf / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    # the load-balanced shares' backward (first and last rank), same sizes
+    if w.causal and w.N % (2 * w.P) == 0 and w.P > 1:
+        # (timing only: the local Q of the timed share stands in for the
+        # load-balanced rows; the sizes are the same)
+        zz = {}
+        qz = qd
+        for rz in (0, w.P - 1):
+            ra.ra_rank_share_zigzag(qz, kd, vd, w.P, rz, w.causal, O, lse)
+
+            def runz():
+                ra.ra_rank_share_zigzag_bwd(qz, kd, vd, O, lse, dout, w.P, rz, w.causal, dq, dk, dv, delta)
+
+            runz()
+            torch.cuda.synchronize()
+            perz = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                runz()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                perz.append(e0.elapsed_time(e1))
+            mz = sorted(perz)[len(perz) // 2]
+            fz = 2.5 * ra.ra_share_flops_zigzag(w.B, w.N, w.P, rz, w.Hq, w.d, w.causal)
+            zz[f"rank{rz}"] = {"ms": round(mz, 4), "tflops": round(fz / mz / 1e9, 3)}
+        log("load-balanced backward: " + ", ".join(f"{k} {v['ms']:.3f} ms ({v['tflops']:.0f} TFLOP/s)"
+                                                   for k, v in zz.items()))
+        out["zigzag"] = zz
+    return out
 
 
 def main() -> int:

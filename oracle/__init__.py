@@ -75,6 +75,10 @@ def _load(path: Optional[str] = None):
     lib.orc_rank_share_bwd.restype = ctypes.c_int
     lib.orc_rank_share_zigzag_bwd.argtypes = lib.orc_rank_share_bwd.argtypes
     lib.orc_rank_share_zigzag_bwd.restype = ctypes.c_int
+    lib.orc_rank_share_padded_bwd.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                              ctypes.c_int, ctypes.c_double, _i64, _ip, _i64, _ip, _i64,
+                                              _dp, _dp, _dp, ctypes.c_int]
+    lib.orc_rank_share_padded_bwd.restype = ctypes.c_int
     lib.orc_ring_block.argtypes = [_i64, _i64, _i64]
     lib.orc_ring_block.restype = _i64
     lib.orc_classify.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
@@ -265,11 +269,13 @@ def zigzag_positions(N: int, P: int, rank: int) -> np.ndarray:
 
 
 def rank_share_bwd(q, k, v, dout, P: int, rank: int, causal: bool, scale: Optional[float] = None,
-                   qrows=None, krows=None, nthreads: Optional[int] = None, zigzag: bool = False):
+                   qrows=None, krows=None, nthreads: Optional[int] = None, zigzag: bool = False,
+                   n_valid: Optional[int] = None):
     """Gradients of one rank's share for the upstream gradient dout [B, N/P, Hq, d]:
     dQ of the listed (b, h, i) local rows [n, d] (default all), and this rank's
     contribution dK, dV to the listed (b, g, j) key rows [m, d] (default all).
-    zigzag: the load-balanced share (local rows = chunks rank and 2P-1-rank of 2P)."""
+    zigzag: the load-balanced share (local rows = chunks rank and 2P-1-rank of 2P).
+    n_valid: the padded share's real length (keys at or after it are masked out)."""
     lib = _load()
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, nq, hq, d = q.shape
@@ -280,10 +286,15 @@ def rank_share_bwd(q, k, v, dout, P: int, rank: int, causal: bool, scale: Option
     kr = np.ascontiguousarray(all_rows(B, hkv, N) if krows is None else np.asarray(krows, dtype=np.int64))
     nq_r, nk_r = qr.shape[0], kr.shape[0]
     dq = np.zeros((max(nq_r, 1), d)); dk = np.zeros((max(nk_r, 1), d)); dv = np.zeros((max(nk_r, 1), d))
-    fn = lib.orc_rank_share_zigzag_bwd if zigzag else lib.orc_rank_share_bwd
-    e = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, P, rank, hq, hkv, d, int(causal),
-           float(scale), qr.ctypes.data_as(_ip), nq_r, kr.ctypes.data_as(_ip), nk_r,
-           _ptr(dq), _ptr(dk), _ptr(dv), nthreads or default_threads())
+    tail = (qr.ctypes.data_as(_ip), nq_r, kr.ctypes.data_as(_ip), nk_r, _ptr(dq), _ptr(dk), _ptr(dv),
+            nthreads or default_threads())
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, P, rank, hq, hkv, d, int(causal), float(scale))
+    if n_valid is not None:
+        if zigzag:
+            raise ValueError("padding of the load-balanced share is not defined here")
+        e = lib.orc_rank_share_padded_bwd(*head, int(n_valid), *tail)
+    else:
+        e = (lib.orc_rank_share_zigzag_bwd if zigzag else lib.orc_rank_share_bwd)(*head, *tail)
     if e:
         raise ValueError(f"backward oracle failed ({e})")
     return dq[:nq_r], dk[:nk_r], dv[:nk_r]

@@ -463,7 +463,9 @@ double orc_share_flops_zigzag(int64_t B, int64_t N, int64_t P, int64_t rank, int
  * triples (j a row of k/v, g a kv head) of dK/dV rows, dk/dv[r*d + c].
  * Under the load-balanced layout (zigzag) the N/P local rows are chunks
  * rank and 2P-1-rank of 2P, and the block a ring step brings is the
- * sender's two chunks; the formulas are unchanged, only positions differ. */
+ * sender's two chunks; the formulas are unchanged, only positions differ.
+ * For an explicitly padded sequence, keys at positions >= kv_end are visible
+ * to no query (their gradients are zero). */
 
 typedef struct {
     const double *q, *k, *v, *dout;
@@ -471,6 +473,7 @@ typedef struct {
     int causal;
     double scale;
     int zigzag;
+    int64_t kv_end;
 } orc_bwd;
 
 /* sequence position of local query row i */
@@ -497,7 +500,7 @@ static int bwd_step_keys(const orc_bwd *w, int64_t st, int64_t lo[2], int64_t hi
 
 static int bwd_visible(const orc_bwd *w, int64_t i, int64_t j)
 {
-    return !w->causal || j <= bwd_qpos(w, i);
+    return j < w->kv_end && (!w->causal || j <= bwd_qpos(w, i));
 }
 
 static double bwd_dot(const double *a, const double *b, int64_t d)
@@ -642,11 +645,11 @@ static int rank_share_bwd(const double *q, const double *k, const double *v, con
                           int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
                           int causal, double scale,
                           const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
-                          double *dq, double *dk, double *dv, int nthreads, int zigzag)
+                          double *dq, double *dk, double *dv, int nthreads, int zigzag, int64_t kv_end)
 {
     if (P <= 0 || N % (zigzag ? 2 * P : P) != 0 || hkv <= 0 || hq % hkv != 0 || d <= 0) return -3;
-    if (rank < 0 || rank >= P) return -5;
-    const orc_bwd w = {q, k, v, dout, B, N, P, rank, N / P, hq, hkv, d, causal, scale, zigzag};
+    if (rank < 0 || rank >= P || kv_end < 1 || kv_end > N) return -5;
+    const orc_bwd w = {q, k, v, dout, B, N, P, rank, N / P, hq, hkv, d, causal, scale, zigzag, kv_end};
     const int64_t G = hq / hkv;
     for (int64_t r = 0; r < nqrows; ++r)
         if (qrows[3 * r] < 0 || qrows[3 * r] >= B || qrows[3 * r + 1] < 0 || qrows[3 * r + 1] >= hq ||
@@ -698,7 +701,19 @@ int orc_rank_share_bwd(const double *q, const double *k, const double *v, const 
                        double *dq, double *dk, double *dv, int nthreads)
 {
     return rank_share_bwd(q, k, v, dout, B, N, P, rank, hq, hkv, d, causal, scale, qrows, nqrows, krows, nkrows,
-                          dq, dk, dv, nthreads, 0);
+                          dq, dk, dv, nthreads, 0, N);
+}
+
+/* Backward of the padded share (orc_rank_share_padded's forward): keys at
+ * positions >= n_valid are masked out. */
+int orc_rank_share_padded_bwd(const double *q, const double *k, const double *v, const double *dout,
+                              int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t hkv, int64_t d,
+                              int causal, double scale, int64_t n_valid,
+                              const int64_t *qrows, int64_t nqrows, const int64_t *krows, int64_t nkrows,
+                              double *dq, double *dk, double *dv, int nthreads)
+{
+    return rank_share_bwd(q, k, v, dout, B, N, P, rank, hq, hkv, d, causal, scale, qrows, nqrows, krows, nkrows,
+                          dq, dk, dv, nthreads, 0, n_valid);
 }
 
 /* Backward of the load-balanced share: q, dout hold the rank's 2 N/(2P)
@@ -710,5 +725,5 @@ int orc_rank_share_zigzag_bwd(const double *q, const double *k, const double *v,
                               double *dq, double *dk, double *dv, int nthreads)
 {
     return rank_share_bwd(q, k, v, dout, B, N, P, rank, hq, hkv, d, causal, scale, qrows, nqrows, krows, nkrows,
-                          dq, dk, dv, nthreads, 1);
+                          dq, dk, dv, nthreads, 1, N);
 }

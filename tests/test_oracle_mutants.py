@@ -38,6 +38,7 @@ MUTANTS = {
                      "*D_out = bwd_dot(w->dout + ((b * w->nb + i) * w->hq + h) * d, qi, d);"),
     "bwd_zigzag_second_chunk": ("return i < c ? w->rank * c + i : (2 * w->P - 1 - w->rank) * c + (i - c);",
                                 "return i < c ? w->rank * c + i : (2 * w->P - 2 - w->rank) * c + (i - c);"),
+    "bwd_padding_key_visible": ("return j < w->kv_end && (!w->causal", "return j <= w->kv_end && (!w->causal"),
     "padded_real_keys_off_by_one": ("const int64_t real = n_valid - j * nb;", "const int64_t real = n_valid + 1 - j * nb;"),
     "pairs_count_off_by_one": ("int64_t c = causal ? q_off + i - kv_off + 1 : nkv;", "int64_t c = causal ? q_off + i - kv_off : nkv;"),
 }
@@ -59,6 +60,7 @@ PINS = [
     lambda: pins.test_backward_matches_torch_autograd(1, 24, 3, 2, 1, 8, True),
     lambda: pins.test_padded_share_is_attention_over_the_real_keys(1, 22, 4, 2, 1, 8, True),
     lambda: pins.test_zigzag_backward_matches_torch_autograd(1, 24, 3, 2, 1, 8, True),
+    lambda: pins.test_padded_backward_matches_torch_autograd(1, 22, 4, 2, 1, 8, True),
 ]
 
 

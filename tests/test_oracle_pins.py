@@ -301,6 +301,35 @@ def test_padded_share_is_attention_over_the_real_keys(B, n_valid, P, Hq, Hkv, d,
         np.testing.assert_allclose(lse.reshape(B, Hq, nb), L_t[:, :, r * nb:(r + 1) * nb].numpy(), atol=TOL, rtol=0)
 
 
+@pytest.mark.parametrize("B,n_valid,P,Hq,Hkv,d,causal", [
+    (1, 22, 4, 2, 1, 8, True),     # N = 24
+    (1, 9, 4, 1, 1, 4, True),      # N = 12: the last block holds no real key
+    (2, 13, 3, 2, 2, 4, False),    # N = 15, no mask
+])
+def test_padded_backward_matches_torch_autograd(B, n_valid, P, Hq, Hkv, d, causal):
+    """Gradients of the padded share equal torch fp64 autograd of attention
+    over the real keys; padding keys get zero dK, dV."""
+    N = P * (-(-n_valid // P))
+    q, k, v = _rand(B, N, N, Hq, Hkv, d, seed=n_valid * P + 1)
+    nb = N // P
+    g = torch.Generator().manual_seed(17)
+    for r in range(P):
+        dout = torch.randn(B, nb, Hq, d, generator=g, dtype=torch.float64)
+        ql = q[:, r * nb:(r + 1) * nb].clone().requires_grad_(True)
+        kk = k[:, :n_valid].clone().requires_grad_(True)
+        vv = v[:, :n_valid].clone().requires_grad_(True)
+        O, _ = _torch_attention(ql, kk, vv, r * nb, 0, causal, 0.5)
+        (O * dout).sum().backward()
+        dq, dk, dv = oracle.rank_share_bwd(q[:, r * nb:(r + 1) * nb], k, v, dout, P, r, causal, 0.5, n_valid=n_valid)
+        dk_t = torch.zeros(B, N, Hkv, d, dtype=torch.float64)
+        dv_t = torch.zeros(B, N, Hkv, d, dtype=torch.float64)
+        dk_t[:, :n_valid] = kk.grad
+        dv_t[:, :n_valid] = vv.grad
+        np.testing.assert_allclose(_grid(dq, B, Hq, nb), ql.grad.numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(_grid(dk, B, Hkv, N), dk_t.numpy(), atol=TOL, rtol=0)
+        np.testing.assert_allclose(_grid(dv, B, Hkv, N), dv_t.numpy(), atol=TOL, rtol=0)
+
+
 def test_padded_share_with_no_padding_is_the_share():
     B, N, P, H, d = 1, 24, 3, 2, 8
     q, k, v = _rand(B, N, N, H, H, d, seed=1)

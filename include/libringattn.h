@@ -189,6 +189,18 @@ int ra_rank_share_zigzag_bwd(const ra_tensor *q, const ra_tensor *k, const ra_te
                              const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
                              const ra_tensor *delta, const ra_opts *opts);
 
+/* Backward of the padded share (ra_rank_share_padded's forward, same n_valid):
+ * keys at positions >= n_valid see no query, so their dk, dv rows are zero
+ * and their k, v contents are never read.  Padding query rows (positions >=
+ * n_valid) are differentiated like the others through their dout rows; a
+ * caller whose loss ignores them passes zeros there.  Arguments otherwise as
+ * ra_rank_share_bwd; n_valid outside [1, N] is RA_E_RANGE. */
+int ra_rank_share_padded_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                             const ra_tensor *o, const ra_tensor *lse, const ra_tensor *dout,
+                             int P, int rank, int causal, int64_t n_valid,
+                             const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
+                             const ra_tensor *delta, const ra_opts *opts);
+
 /* ---- host-only queries (no GPU needed) --------------------------------- */
 
 /* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1. */

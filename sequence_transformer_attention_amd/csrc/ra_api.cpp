@@ -312,8 +312,8 @@ int ra_rank_share_zigzag(const ra_tensor* q, const ra_tensor* k, const ra_tensor
 static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
                           const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
                           const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta,
-                          const ra_opts* opts, int zigzag) {
-  const char* fn = zigzag ? "ra_rank_share_zigzag_bwd" : "ra_rank_share_bwd";
+                          const ra_opts* opts, int zigzag, int64_t n_valid) {
+  const char* fn = zigzag ? "ra_rank_share_zigzag_bwd" : (n_valid >= 0 ? "ra_rank_share_padded_bwd" : "ra_rank_share_bwd");
   int e = check_qkv(q, k, v, "k", "v");
   if (e) return e;
   if (q->dtype != RA_BF16) return fail(RA_E_UNSUPPORTED, "%s takes bf16 q, k, v", fn);
@@ -325,6 +325,8 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   if (N % parts != 0)
     return fail(RA_E_SHAPE, "sequence length %lld is not divisible by %s = %lld (no implicit padding)",
                 (long long)N, zigzag ? "2P" : "P", (long long)parts);
+  if (n_valid > N) return fail(RA_E_RANGE, "n_valid %lld exceeds the padded length %lld", (long long)n_valid, (long long)N);
+  if (n_valid == 0 && N > 0) return fail(RA_E_RANGE, "n_valid must be >= 1");
   const int64_t nb = N / P;  // local rows either way (zigzag: two chunks of N/(2P))
   if (nq != nb) return fail(RA_E_SHAPE, "local query block has %lld rows, expected N/P = %lld", (long long)nq, (long long)nb);
   if ((e = check_out(o, q, "o")) || (e = check_out(dout, q, "dout")) || (e = check_out(dq, q, "dq"))) return e;
@@ -353,6 +355,7 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   a.N = N; a.nb = nb; a.q_off = (int64_t)rank * nb;
   a.P = P; a.rank = rank; a.causal = causal ? 1 : 0;
   a.nsplit = 1;
+  a.kv_end = n_valid >= 0 ? n_valid : N;
   if (zigzag) {
     const int64_t c = N / parts;
     a.nsplit = 2; a.qc = c; a.q_off = (int64_t)rank * c;
@@ -360,21 +363,28 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   }
   a.scale = resolve_scale(opts, d);
   a.c = a.scale * 1.4426950408889634f;
-  return launched(ra_launch_bwd(a, (int)d, stream_of(opts)), zigzag ? "ra_rank_share_zigzag_bwd launch"
-                                                                     : "ra_rank_share_bwd launch");
+  return launched(ra_launch_bwd(a, (int)d, stream_of(opts)), fn);
 }
 
 int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
                       const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal, const ra_tensor* dq,
                       const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta, const ra_opts* opts) {
-  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 0);
+  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 0, -1);
+}
+
+int ra_rank_share_padded_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
+                             const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
+                             int64_t n_valid, const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv,
+                             const ra_tensor* delta, const ra_opts* opts) {
+  if (n_valid < 0) return fail(RA_E_RANGE, "n_valid must be >= 1");
+  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 0, n_valid);
 }
 
 int ra_rank_share_zigzag_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
                              const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
                              const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta,
                              const ra_opts* opts) {
-  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 1);
+  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 1, -1);
 }
 
 int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s) {

@@ -34,6 +34,9 @@ struct RaBwdArgs {
   // one block of nq rows, P blocks of nb keys
   int32_t nsplit, rank2;
   int64_t qc, q_off2;
+  // keys at positions >= kv_end are visible to no query (an explicitly
+  // padded sequence; N otherwise)
+  int64_t kv_end;
   float c;       // softmax scale * log2(e)
   float scale;   // softmax scale
 };

@@ -256,8 +256,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
   // lockstep and share the K/V stream in L2 (the own block's causal tile
   // count differs per query tile).
   auto blk = [&](int s) -> int64_t { return ra_plan_ring_block(Pe, rank_e, (s + 1) % Pe); };
+  // keys of block b0 * nbe .. before the key end
+  auto blk_keys = [&](int64_t k0) -> int64_t {
+    const int64_t n = a.kv_end - k0;
+    return n < 0 ? 0 : (n < nbe ? n : nbe);
+  };
   auto tiles = [&](int s) -> int {
-    return (int)ra_plan_key_tiles(q0_wg, nq_wg, blk(s) * nbe, nbe, a.causal, BN);
+    const int64_t k0 = blk(s) * nbe;
+    return (int)ra_plan_key_tiles(q0_wg, nq_wg, k0, blk_keys(k0), a.causal, BN);
   };
   // The workgroup's key tiles in that order; the loads of the next tile are
   // in flight while the current one is computed (two LDS stages).
@@ -281,7 +287,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
   cur_fix(cc);
   cur_fix(cl);
   auto issue = [&](int st) __attribute__((always_inline)) {
-    const int64_t k0 = cl.k0 + (int64_t)cl.u * BN, left = nbe - (int64_t)cl.u * BN;
+    const int64_t k0 = cl.k0 + (int64_t)cl.u * BN, left = blk_keys(cl.k0) - (int64_t)cl.u * BN;
     const int nvalid = left < BN ? (int)left : BN;
     load_tile<D, NW>(kb + k0 * a.k_ss, a.k_ss, nvalid, &smem[st][0][0], wave, lane);
     load_tile<D, NW>(vb + k0 * a.v_ss, a.v_ss, nvalid, &smem[st][1][0], wave, lane);
@@ -289,7 +295,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
   };
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
-    const int64_t k0 = cc.k0 + (int64_t)cc.u * BN, left = nbe - (int64_t)cc.u * BN;
+    const int64_t k0 = cc.k0 + (int64_t)cc.u * BN, left = blk_keys(cc.k0) - (int64_t)cc.u * BN;
     const int nvalid = left < BN ? (int)left : BN;
     cur_next(cc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -397,16 +403,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // the wave's last key position under causal masking (none: no mask)
   const int64_t kmax_w = a.causal ? (int64_t)kt * BK + wave * 32 + 31 : INT64_MIN / 2;
   const bool k_ok = my_k < a.N;
+  // a key before the key end; the others (padding) are read as zeros, see
+  // no query and get zero gradients
+  const bool k_live = my_k < a.kv_end;
+  const bool wave_live = (int64_t)kt * BK + wave * 32 + 31 < a.kv_end;  // every key of the wave
 
   bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7
   {
-    const int64_t row = k_ok ? my_k : 0;
+    const int64_t row = k_live ? my_k : 0;
     const __bf16* kp = (const __bf16*)a.k + (int64_t)b * a.k_sb + row * a.k_ss + (int64_t)g * a.k_sh + 8 * lg;
     const __bf16* vp = (const __bf16*)a.v + (int64_t)b * a.v_sb + row * a.v_ss + (int64_t)g * a.v_sh + 8 * lg;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      kf[c] = k_ok ? *(const bf16x8*)(kp + 16 * c) : bf16x8{};
-      vf[c] = k_ok ? *(const bf16x8*)(vp + 16 * c) : bf16x8{};
+      kf[c] = k_live ? *(const bf16x8*)(kp + 16 * c) : bf16x8{};
+      vf[c] = k_live ? *(const bf16x8*)(vp + 16 * c) : bf16x8{};
     }
   }
   f32x16 dka[DB], dva[DB];
@@ -433,7 +443,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     return qlo >= nqc ? ntq : (int)(qlo / BN);
   };
   const int t0a = first_tile(a.q_off), t0b = a.nsplit == 2 ? first_tile(a.q_off2) : ntq;
-  const int na = ntq - t0a, nt = na + (ntq - t0b), total = G * nt;
+  const int na = ntq - t0a, nt = na + (ntq - t0b);
+  const int total = kfirst < a.kv_end ? G * nt : 0;  // no key before the key end: nothing to do
   // tile it of the walk: query head, first local row, rows in its chunk,
   // position of its first row
   struct TileRef {
@@ -535,11 +546,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       // e >= lo.  Rows past their chunk need no test (their LSE is +inf:
       // P = 0, and D = 0), nor keys past the sequence (their P only reaches
       // their own dK, dV columns, which are not stored).
-      const int lo = a.causal ? rel - 32 * hf - 4 * lg : -(1 << 30);
+      const int lo = !k_live ? (1 << 30) : (a.causal ? rel - 32 * hf - 4 * lg : -(1 << 30));
       float pv[16];
       bf16x8 pf[2];
       // the wave's last key at or before the unit's first query row: no test
-      if (kmax_w <= qp0 + 32 * hf) {
+      if (wave_live && kmax_w <= qp0 + 32 * hf) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           pv[r] = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);

@@ -71,8 +71,11 @@ def lib() -> ctypes.CDLL:
     L.ra_rank_share_padded.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, O]
     L.ra_rank_share_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, T, T, T, O]
     L.ra_rank_share_zigzag_bwd.argtypes = L.ra_rank_share_bwd.argtypes
+    L.ra_rank_share_padded_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64,
+                                           T, T, T, T, O]
     for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share, L.ra_rank_share_zigzag,
-              L.ra_rank_share_bwd, L.ra_rank_share_padded, L.ra_rank_share_zigzag_bwd):
+              L.ra_rank_share_bwd, L.ra_rank_share_padded, L.ra_rank_share_zigzag_bwd,
+              L.ra_rank_share_padded_bwd):
         f.restype = ctypes.c_int
     L.ra_ring_block.argtypes = [i64, i64, i64]
     L.ra_ring_block.restype = i64
@@ -213,6 +216,16 @@ def ra_rank_share_zigzag_bwd(q, k, v, o, lse, dout, P: int, rank: int, causal: b
     _check(lib().ra_rank_share_zigzag_bwd(_desc(q), _desc(k), _desc(v), _desc(o), _desc(lse, True), _desc(dout),
                                           int(P), int(rank), int(bool(causal)), _desc(dq), _desc(dk), _desc(dv),
                                           _desc(delta, True), ctypes.byref(opts)))
+
+
+def ra_rank_share_padded_bwd(q, k, v, o, lse, dout, P: int, rank: int, causal: bool, n_valid: int, dq, dk, dv,
+                             delta, scale: Optional[float] = None, stream=None) -> None:
+    """Backward of the padded share (o, lse from ra_rank_share_padded with the
+    same n_valid); outputs as ra_rank_share_bwd, zero dk, dv past n_valid."""
+    opts, keep = _opts(stream, scale)
+    _check(lib().ra_rank_share_padded_bwd(_desc(q), _desc(k), _desc(v), _desc(o), _desc(lse, True), _desc(dout),
+                                          int(P), int(rank), int(bool(causal)), int(n_valid), _desc(dq), _desc(dk),
+                                          _desc(dv), _desc(delta, True), ctypes.byref(opts)))
 
 
 def ra_ring_block(P: int, rank: int, s: int) -> int:

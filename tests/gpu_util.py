@@ -130,6 +130,20 @@ def zigzag_backward_gpu(q, k, v, P, rank, causal, dout, scale=None):
     return dq, dk, dv
 
 
+def padded_backward_gpu(q, k, v, P, rank, causal, n_valid, dout, scale=None):
+    """Padded forward (bf16 O, LSE) then its backward; returns (dq, dk, dv) fp32."""
+    B, nq, hq, d = q.shape
+    O = torch.empty((B, nq, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share_padded(q, k, v, P, rank, causal, n_valid, O, lse, scale=scale)
+    dq = torch.full((B, nq, hq, d), float("nan"), dtype=torch.float32, device=q.device)
+    dk = torch.full(k.shape, float("nan"), dtype=torch.float32, device=q.device)
+    dv = torch.full(k.shape, float("nan"), dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
+    ra.ra_rank_share_padded_bwd(q, k, v, O, lse, dout, P, rank, causal, n_valid, dq, dk, dv, delta, scale=scale)
+    return dq, dk, dv
+
+
 # Gradients: bf16 operands (q, k, v, dO, the forward's bf16 O, and P and dS
 # rounded to bf16 for the MFMAs) against the exact fp64 chain rule.  Each
 # rounding is at most 2^-9 relative; the gradients are sums of such terms, so

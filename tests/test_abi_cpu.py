@@ -230,6 +230,21 @@ def test_ra_rank_share_zigzag_bwd_validation():
     assert bwd(**dict(good, Pn=4, rank=3)) == ra.RA_E_SHAPE        # Nq != N / P
 
 
+def test_ra_rank_share_padded_bwd_validation():
+    def bwd(n_valid, Pn=8, rank=7):
+        q, k, v = T([1, 512, 4, 128]), T([1, 4096, 1, 128]), T([1, 4096, 1, 128])
+        o, do = T([1, 512, 4, 128]), T([1, 512, 4, 128])
+        dq = T([1, 512, 4, 128], ra.RA_F32)
+        dk, dv = T([1, 4096, 1, 128], ra.RA_F32), T([1, 4096, 1, 128], ra.RA_F32)
+        return ra.lib().ra_rank_share_padded_bwd(P(q), P(k), P(v), P(o), P(rows(1, 4, 512)), P(do), Pn, rank, 1,
+                                                 n_valid, P(dq), P(dk), P(dv), P(rows(1, 4, 512)), None)
+    for bad in (0, -1, 4097):
+        assert bwd(bad) == ra.RA_E_RANGE, bad
+        assert "n_valid" in ra.ra_last_error()
+    assert bwd(4000, rank=8) == ra.RA_E_RANGE
+    assert bwd(4000, Pn=4, rank=3) == ra.RA_E_SHAPE
+
+
 def test_ra_finalize_validation():
     L = ra.lib()
     oacc, l = T([1, 64, 2, 64], ra.RA_F32), rows(1, 2, 64)

@@ -11,7 +11,8 @@ import torch
 import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
-                            padded_gpu, say, stepwise_gpu, zigzag_backward_gpu, zigzag_gpu, zigzag_rows)
+                            padded_backward_gpu, padded_gpu, say, stepwise_gpu, zigzag_backward_gpu, zigzag_gpu,
+                            zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +134,33 @@ def test_full_size_zigzag_backward_sampled_rows():
     assert_grad_close(dq[qi[:, 0], qi[:, 2], qi[:, 1]].double().cpu().numpy(), dq_r, "zigzag dQ full size")
     assert_grad_close(dk[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dk_r, "zigzag dK full size")
     assert_grad_close(dv[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dv_r, "zigzag dV full size")
+
+
+def test_full_size_padded_backward_sampled_rows():
+    """Backward of the rank-7-of-8 share holding 32768 - 777 real tokens (NaN
+    padding keys): sampled dQ rows, dK/dV rows of kv head 0 over the whole
+    sequence, and exact zeros on every padding key row."""
+    w = workloads.RANK7_BF16
+    n_valid = w.N - 777
+    x = inputs.workload_inputs(w)
+    x["k"][:, n_valid:] = float("nan")
+    x["v"][:, n_valid:] = float("nan")
+    d = {k: t.to("cuda") for k, t in x.items()}
+    r = w.ranks[0]
+    dout = torch.randn(w.B, w.nq, w.Hq, w.d, generator=torch.Generator().manual_seed(w.seed + 9)).to(torch.bfloat16)
+    say("padded backward full size: forward + backward on the GPU")
+    dq, dk, dv = padded_backward_gpu(d["q"], d["k"], d["v"], w.P, r, w.causal, n_valid, dout.to("cuda"))
+    torch.cuda.synchronize()
+    assert float(dk[:, n_valid:].abs().max()) == 0.0 and float(dv[:, n_valid:].abs().max()) == 0.0
+    qrows = inputs.sample_rows(w.B, w.Hq, w.nq, w.seed + 10).numpy()[:512]
+    g = torch.Generator().manual_seed(w.seed + 11)
+    krows = torch.stack([torch.zeros(256, dtype=torch.long), torch.zeros(256, dtype=torch.long),
+                         torch.randint(0, n_valid, (256,), generator=g)], 1).numpy()
+    say(f"padded backward full size: oracle on {len(qrows)} dQ rows and {len(krows)} dK/dV rows")
+    dq_r, dk_r, dv_r = oracle.rank_share_bwd(x["q"], x["k"], x["v"], dout, w.P, r, w.causal, qrows=qrows,
+                                             krows=krows, nthreads=oracle_threads(), n_valid=n_valid)
+    qi = torch.as_tensor(qrows)
+    ki = torch.as_tensor(krows)
+    assert_grad_close(dq[qi[:, 0], qi[:, 2], qi[:, 1]].double().cpu().numpy(), dq_r, "padded dQ full size")
+    assert_grad_close(dk[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dk_r, "padded dK full size")
+    assert_grad_close(dv[ki[:, 0], ki[:, 2], ki[:, 1]].double().cpu().numpy(), dv_r, "padded dV full size")

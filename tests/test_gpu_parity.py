@@ -13,7 +13,8 @@ import oracle
 from sequence_transformer_attention_amd import inputs, workloads
 from sequence_transformer_attention_amd import ringattn as ra
 from tests.gpu_util import (assert_close, assert_grad_close, backward_gpu, gather, oracle_threads, rank_share_gpu,
-                            padded_gpu, say, stepwise_gpu, zigzag_backward_gpu, zigzag_gpu, zigzag_rows)
+                            padded_backward_gpu, padded_gpu, say, stepwise_gpu, zigzag_backward_gpu, zigzag_gpu,
+                            zigzag_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -221,6 +222,35 @@ def test_zigzag_backward_share(B, N, P, Hq, Hkv, d, causal, ranks):
         assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nq), f"zigzag dQ rank {r}")
         assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"zigzag dK rank {r}")
         assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"zigzag dV rank {r}")
+
+
+@pytest.mark.parametrize("B,n_valid,P,Hq,Hkv,d,causal,ranks", [
+    (1, 3990, 4, 2, 1, 128, True, (1, 3)),     # N 3992: the last block ends in 2 padding keys
+    (2, 1133, 3, 2, 2, 64, False, (0, 2)),     # N 1134, no mask, B 2
+    (1, 1500, 4, 2, 1, 128, True, (3, 0)),     # N 2000: the last block is all padding
+])
+def test_padded_backward_share(B, n_valid, P, Hq, Hkv, d, causal, ranks):
+    """Keys past n_valid hold NaN: any read of them poisons a gradient."""
+    N = 2000 if n_valid == 1500 else P * (-(-n_valid // P))
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=n_valid + 7 * P)
+    x["k"][:, n_valid:] = float("nan")
+    x["v"][:, n_valid:] = float("nan")
+    dv_ = _dev(x)
+    nb = N // P
+    g = torch.Generator().manual_seed(n_valid)
+    for r in ranks:
+        ql = x["q"][:, r * nb:(r + 1) * nb].contiguous()
+        dout = torch.randn(B, nb, Hq, d, generator=g).to(torch.bfloat16)
+        say(f"padded backward B{B} N{N} n_valid{n_valid} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+        dq, dk, dv = padded_backward_gpu(ql.to(DEV), dv_["k"], dv_["v"], P, r, causal, n_valid, dout.to(DEV))
+        torch.cuda.synchronize()
+        dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, P, r, causal, nthreads=oracle_threads(),
+                                                 n_valid=n_valid)
+        grid = lambda a, H, S: a.reshape(B, H, S, d).transpose(0, 2, 1, 3)
+        assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nb), f"padded dQ rank {r}")
+        assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"padded dK rank {r}")
+        assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"padded dV rank {r}")
+        assert float(dk[:, n_valid:].abs().max()) == 0.0 and float(dv[:, n_valid:].abs().max()) == 0.0
 
 
 # ------------------------------------------------------------------ edge cases

@@ -28,10 +28,13 @@
 //                     registers as B operands); per 32-query unit of a
 //                     64-row Q/dO tile staged in LDS, for every query head
 //                     of the kv head, stage by stage:
-//                       S = Q K^T, then dP = dO V^T (A operands from LDS),
-//                       P (while the dP products run), dV^T += dO^T P with
-//                       dO^T from transposing reads, dS (while the dV
-//                       products run), dK^T += Q^T dS.
+//                       S = Q K^T, then dP = dO V^T (A operands from LDS)
+//                       with P formed between its MFMAs, dV^T += dO^T P
+//                       (dO^T from transposing reads) with dS formed
+//                       between its MFMAs, dK^T += Q^T dS.  One wave per
+//                       SIMD issues both streams: scheduling barriers keep
+//                       the vector work between the MFMAs, where it issues
+//                       while the matrix core runs.
 //                     The dK, dV accumulators stay in AGPRs for the whole
 //                     walk (inline-asm MFMAs; the compiler otherwise copies
 //                     them between register files every iteration); one
@@ -148,6 +151,11 @@ __device__ __forceinline__ void mfma_acc4(f32x16& c0, f32x16& c1, f32x16& c2, f3
       "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3"
       : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
       : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b));
+}
+// acc += A * B, one v_mfma_f32_32x32x16_bf16 with the accumulator pinned to
+// AGPRs (as mfma_acc4, for interleaving with vector work).
+__device__ __forceinline__ void mfma_acc1(f32x16& c, const u32x4& A, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(A), "v"(b));
 }
 // Zero an accumulator with an MFMA (zero operands, inline-constant C), so
 // that it is born in AGPRs.
@@ -496,9 +504,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       constexpr int hf = decltype(HF)::value;
       constexpr unsigned qo = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // Q unit; dO unit at + TILE
       // Stage by stage, so that each operand set is live only as long as its
-      // products need it and the vector work of one product overlaps the
-      // MFMAs of the next: S (Q rows), dP (dO rows) with P formed meanwhile,
-      // dV (dO^T) with dS formed meanwhile, dK (Q^T).
+      // products need it: S (Q rows), dP (dO rows) with P formed between its
+      // MFMAs, dV (dO^T) with dS formed between its MFMAs, dK (Q^T).
       // S = Q K^T (queries x keys); query row of register r: 8 (r / 4) + 4 lg + (r % 4)
       bf16x8 fq[KC];
 #pragma unroll
@@ -530,10 +537,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(l4[0]),
                      "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]), "+v"(d4[0]), "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
-      f32x16 dpa = f32x16{};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], vf[c], dpa, 0, 0, 0);
-      // dO^T for the dV product, in flight while P is formed
+      // dO^T for the dV product, in flight during the dP products
       u32x2 olo[2][DB], ohi[2][DB];
       static_for<0, 2 * DB>([&](auto X) {
         constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
@@ -547,46 +551,47 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       // P = 0, and D = 0), nor keys past the sequence (their P only reaches
       // their own dK, dV columns, which are not stored).
       const int lo = !k_live ? (1 << 30) : (a.causal ? rel - 32 * hf - 4 * lg : -(1 << 30));
+      // dP = dO V^T, one MFMA at a time with 16 / KC elements of P formed
+      // after each (a single wave per SIMD: the vector work issues while the
+      // matrix core runs; the scheduling barriers keep this order)
+      constexpr int PE = 16 / KC;
+      f32x16 dpa = f32x16{};
       float pv[16];
       bf16x8 pf[2];
-      // the wave's last key at or before the unit's first query row: no test
-      if (wave_live && kmax_w <= qp0 + 32 * hf) {
+      static_for<0, KC>([&](auto C) {
+        constexpr int c = decltype(C)::value;
+        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], vf[c], dpa, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pv[r] = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);
+        for (int q = 0; q < PE; ++q) {
+          const int r = PE * c + q, e = 8 * (r >> 2) + (r & 3);
+          float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);
+          asm volatile("" : "+v"(t));  // computed for every lane: no branch
+          pv[r] = e >= lo ? t : 0.f;
           pf[r >> 3][r & 7] = (__bf16)pv[r];
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * j + i, e = 8 * j + i;
-            float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[j][i]);
-            asm volatile("" : "+v"(t));  // computed for every lane: no branch
-            pv[r] = e >= lo ? t : 0.f;
-            pf[r >> 3][r & 7] = (__bf16)pv[r];
-          }
-      }
+        __builtin_amdgcn_sched_barrier(0);
+      });
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // dV^T += dO^T P, one MFMA at a time with 16 / (2 DB) elements of dS
+      // formed after each
+      constexpr int SE = 16 / (2 * DB);
+      bf16x8 dsf[2];
+      static_for<0, 2 * DB>([&](auto X) {
+        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
+        u32x2 l0 = olo[hh][d_], h0 = ohi[hh][d_];
+        asm volatile("" : "+v"(l0), "+v"(h0));
+        const u32x4 wd = {l0[0], l0[1], h0[0], h0[1]};
+        mfma_acc1(dva[d_], wd, pf[hh]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 wd[DB];
-#pragma unroll
-        for (int d_ = 0; d_ < DB; ++d_) {
-          u32x2 l0 = olo[hh][d_], h0 = ohi[hh][d_];
-          asm volatile("" : "+v"(l0), "+v"(h0));
-          wd[d_] = u32x4{l0[0], l0[1], h0[0], h0[1]};
+        for (int q = 0; q < SE; ++q) {
+          const int r = SE * x + q;
+          dsf[r >> 3][r & 7] = (__bf16)(pv[r] * (dpa[r] - d4[r >> 2][r & 3]));
         }
-        if constexpr (DB == 4) {
-          mfma_acc4(dva[0], dva[1], dva[2], dva[3], wd[0], wd[1], wd[2], wd[3], pf[hh]);
-        } else {
-#pragma unroll
-          for (int d_ = 0; d_ < DB; ++d_)
-            dva[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wd[d_]), pf[hh], dva[d_], 0, 0, 0);
-        }
-      }
-      // Q^T for the dK product, in flight while dS is formed
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // Q^T for the dK product
       u32x2 qlo[2][DB], qhi[2][DB];
       static_for<0, 2 * DB>([&](auto X) {
         constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
@@ -594,14 +599,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         ds_rdtr<off>(qlo[hh][d_], ta.tr[0][d_]);
         ds_rdtr<off>(qhi[hh][d_], ta.tr[1][d_]);
       });
-      bf16x8 dsf[2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          dsf[r >> 3][r & 7] = (__bf16)(pv[r] * (dpa[r] - d4[j][i]));
-        }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {

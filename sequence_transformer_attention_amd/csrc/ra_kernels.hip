@@ -125,11 +125,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
   const int nqt_c = (nqc + BM - 1) / BM;
   const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
-  const int logical = ra_plan_xcd_remap(blockIdx.x, gridDim.x, nqt);
-  int qt = logical % nqt;
-  const int hb = logical / nqt;
+  int hb, qt;  // later query tiles see more keys under causal masking: they start first
+  ra_plan_head_tile(ra_plan_xcd_remap(blockIdx.x, gridDim.x, nqt), gridDim.x, nqt, a.causal, &hb, &qt);
   const int h = hb % a.Hq, b = hb / a.Hq;
-  if (a.causal) qt = nqt - 1 - qt;  // later query tiles see more keys: start them first
   const int hk = h / (a.Hq / a.Hkv);
   const int chunk = qt / nqt_c;
   const int64_t qpos0 = chunk ? a.q_off2 : a.q_off;  // global position of the chunk's first row

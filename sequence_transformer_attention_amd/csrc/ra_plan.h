@@ -47,6 +47,30 @@ RA_HD int ra_plan_xcd_remap(int bid, int nwg, int run) {
   return (x / k) * k * per + i * k + (x % k);
 }
 
+// Head (batch * Hq + h) and query tile of logical workgroup l in a grid of
+// nwg = nqt * heads, after ra_plan_xcd_remap.  When every XCD holds an even
+// number of whole heads, the query tiles of each pair of heads are
+// interleaved (h0 t, h1 t, h0 t', h1 t', ...); otherwise a head's tiles are
+// consecutive.  Under causal masking later query tiles come first within a
+// head.  With one workgroup per CU the dispatcher hands the next workgroup of
+// an XCD to the first CU that frees up; interleaving two heads makes the
+// light tiles of one batch finish first and pick up the heavy tiles of the
+// next (longest-first pairing), so every CU gets the same work.  A bijection
+// on [0, nwg) -> (head, tile).
+RA_HD void ra_plan_head_tile(int l, int nwg, int nqt, int causal, int* head, int* qt) {
+  int hd, qi;
+  if (nwg % 8 == 0 && (nwg / 8) % (2 * nqt) == 0) {
+    const int pr = l / (2 * nqt), j = l % (2 * nqt);
+    hd = 2 * pr + (j & 1);
+    qi = j >> 1;
+  } else {
+    hd = l / nqt;
+    qi = l % nqt;
+  }
+  *head = hd;
+  *qt = causal ? nqt - 1 - qi : qi;
+}
+
 RA_HD int ra_plan_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, int causal) {
   if (nq <= 0 || nk <= 0) return RA_CLASS_SKIP;
   if (!causal) return RA_CLASS_FULL;

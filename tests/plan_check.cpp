@@ -47,6 +47,40 @@ int main() {
       }
     }
   }
+  // (head, query tile) of every workgroup: a bijection onto heads x tiles for
+  // every grid, causal or not; when each XCD holds an even number of whole
+  // heads, consecutive workgroups of an XCD alternate between two heads at the
+  // same tile, later tiles first under causal masking
+  for (int nqt : {1, 2, 3, 16, 32, 64, 256})
+    for (int heads : {1, 2, 3, 4, 8, 16, 32, 64})
+      for (int causal : {0, 1}) {
+        const int nwg = nqt * heads;
+        std::vector<int> seen(nwg, 0);
+        for (int b = 0; b < nwg; ++b) {
+          int h, t;
+          ra_plan_head_tile(ra_plan_xcd_remap(b, nwg, nqt), nwg, nqt, causal, &h, &t);
+          if (h < 0 || h >= heads || t < 0 || t >= nqt) {
+            std::printf("head/tile out of range: nqt %d heads %d\n", nqt, heads);
+            return 1;
+          }
+          ++seen[h * nqt + t];
+        }
+        for (int v : seen)
+          if (v != 1) { std::printf("head/tile not a bijection: nqt %d heads %d\n", nqt, heads); return 1; }
+      }
+  {
+    const int nqt = 16, heads = 32, nwg = nqt * heads;  // 4 heads per XCD
+    for (int x = 0; x < 8; ++x)
+      for (int i = 0; i + 1 < nwg / 8; i += 2) {
+        int h0, t0, h1, t1;
+        ra_plan_head_tile(ra_plan_xcd_remap(8 * i + x, nwg, nqt), nwg, nqt, 1, &h0, &t0);
+        ra_plan_head_tile(ra_plan_xcd_remap(8 * (i + 1) + x, nwg, nqt), nwg, nqt, 1, &h1, &t1);
+        if (h1 != h0 + 1 || t1 != t0 || t0 != nqt - 1 - (i / 2) % nqt) {
+          std::printf("pair order broken: xcd %d slot %d\n", x, i);
+          return 1;
+        }
+      }
+  }
   std::printf("ok\n");
   return 0;
 }

@@ -105,9 +105,14 @@ def cpu_baseline(w, x, O_gpu, lse_gpu, target_s: float):
     parity = {"rows": n, "max_abs_dO": float(np.abs(o - o_ref).max()),
               "max_abs_dLSE": float(np.abs(lse - l_ref).max()), "tol_O": "1e-2 + bf16 output rounding",
               "tol_LSE": 1e-3, "pass": bool(excess <= 0 and np.abs(lse - l_ref).max() <= 1e-3)}
+    # every row of the share, at the same rate (extrapolated, not run)
+    pos_all = np.arange(w.nq, dtype=np.float64) + r * w.nq
+    vis_all = np.minimum(pos_all + 1, w.N) if w.causal else np.full(w.nq, float(w.N))
+    share_flops = 4.0 * w.d * w.B * w.Hq * float(vis_all.sum())
     base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} random (b, h, i) rows of the same share, each against all its visible "
-                      f"keys in ring order; {flops:.3e} FLOP in {dt:.2f} s (fp64, plain C)"}
+                      f"keys in ring order; {flops:.3e} FLOP in {dt:.2f} s (fp64, plain C)",
+            "extrapolated_share_s": round(share_flops / (flops / dt), 1)}
     return base, parity
 
 

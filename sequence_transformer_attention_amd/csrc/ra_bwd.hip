@@ -408,13 +408,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const int kt = logical % nkt, hb = logical / nkt;
   const int g = hb % a.Hkv, b = hb / a.Hkv, G = a.Hq / a.Hkv;
   const int64_t my_k = (int64_t)kt * BK + wave * 32 + lr;
-  // the wave's last key position under causal masking (none: no mask)
-  const int64_t kmax_w = a.causal ? (int64_t)kt * BK + wave * 32 + 31 : INT64_MIN / 2;
   const bool k_ok = my_k < a.N;
   // a key before the key end; the others (padding) are read as zeros, see
   // no query and get zero gradients
   const bool k_live = my_k < a.kv_end;
-  const bool wave_live = (int64_t)kt * BK + wave * 32 + 31 < a.kv_end;  // every key of the wave
 
   bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7
   {

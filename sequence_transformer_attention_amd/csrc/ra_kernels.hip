@@ -200,8 +200,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // inst * 64 + L of the tile (row r, physical slot p) and loads the logical
   // slot that the swizzle puts there.  The loads are buffer loads: a scalar
   // descriptor based at the tile's first row plus a per-lane 32-bit offset
-  // fixed for the kernel.  In the last tile of a block, rows past the block
-  // end re-read the last valid row (finite data; masked in S, zero weight in P).
+  // fixed for the kernel.  The descriptor's range ends with the tile's last
+  // valid row, so in the last tile of a block the rows past the block end
+  // are out of range: the buffer unit fetches nothing for them (the data
+  // returned is zero) and no branch is needed.  Whatever those LDS rows then
+  // hold (zeros, or rows of an earlier tile: the V stages are cleared first,
+  // so never uninitialised V data) is masked in S and has zero weight in P.
   const char* kbase = (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
   const char* vbase = (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -223,30 +227,19 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
   auto issue = [&](const char* tb, int64_t stride, const unsigned* goff, int nvalid, auto STAGE)
       __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, (int)(unsigned)(BN * stride * 2), 0x00020000);
+    // range: through the end of row nvalid - 1 (nvalid >= 1; at most
+    // 63 * 2^25 + 2D bytes, as k/v row strides are at most 2^24 elements)
+    const int nrec = (nvalid - 1) * (int)stride * 2 + 2 * D;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, nrec, 0x00020000);
     // LDS destination: the wave's share of the stage.  The base goes through
     // an empty asm so that the per-stage addresses are formed here (one
     // scalar add) instead of being hoisted into registers for the kernel.
     unsigned lb = smem_lds + (unsigned)wv * NL * 1024;
     asm volatile("" : "+s"(lb));
     char* dst = (char*)&smem[0][0] + (lb - smem_lds) + decltype(STAGE)::value * TILE_BYTES;
-    if (nvalid == BN) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const unsigned off = goff[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, off, 0, 0, 0);
-      }
-    } else {
-      const int last = nvalid - 1;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        int r;
-        const unsigned sl = gslot(i, r);
-        const unsigned off = (unsigned)(r < last ? r : last) * (unsigned)stride * 2u + sl;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, off, 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, goff[i], 0, 0, 0);
   };
 
   // Per-lane LDS byte addresses inside a K or V tile (rows of 2D bytes).
@@ -582,8 +575,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     };
     using std::integral_constant;
 
-    // Prologue: descriptors of c_0..3; K(c_0..2), V(c_0..1); V stage 3
-    // cleared (the first step's P V reads it with P = 0); S^T of unit 0; K
+    // Prologue: the four V stages cleared (V stage 3 is read by the first
+    // step's P V with P = 0; rows past a block's end are never fetched, see
+    // issue); descriptors of c_0..3; K(c_0..2), V(c_0..1); S^T of unit 0; K
     // fragments of unit 1.
     fill(integral_constant<int, 0>{});
 #pragma unroll
@@ -591,16 +585,21 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     fill(integral_constant<int, 1>{});
     fill(integral_constant<int, 2>{});
     fill(integral_constant<int, 3>{});
+    {
+      constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane and stage
+#pragma unroll
+      for (int st = 4; st < 8; ++st)
+#pragma unroll
+        for (int i = 0; i < per; ++i) *(u32x4*)(&smem[st][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
+      // every wave's clearing stores land before any wave's direct loads into
+      // the same stages
+      __syncthreads();
+    }
     load_k(integral_constant<int, 0>{});
     load_k(integral_constant<int, 1>{});
     load_k(integral_constant<int, 2>{});
     load_v(integral_constant<int, 0>{});
     load_v(integral_constant<int, 1>{});
-    {
-      constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane
-#pragma unroll
-      for (int i = 0; i < per; ++i) *(u32x4*)(&smem[7][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     kread(uoff(integral_constant<int, 0>{}, H0));

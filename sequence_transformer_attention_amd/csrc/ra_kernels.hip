@@ -202,10 +202,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   // descriptor based at the tile's first row plus a per-lane 32-bit offset
   // fixed for the kernel.  The descriptor's range ends with the tile's last
   // valid row, so in the last tile of a block the rows past the block end
-  // are out of range: the buffer unit fetches nothing for them (the data
-  // returned is zero) and no branch is needed.  Whatever those LDS rows then
-  // hold (zeros, or rows of an earlier tile: the V stages are cleared first,
-  // so never uninitialised V data) is masked in S and has zero weight in P.
+  // are out of range: the buffer unit fetches nothing for them and writes
+  // zeros to their LDS bytes (range checked per dword; measured on gfx950),
+  // with no branch in the loop.  Those zero rows are masked in S and have
+  // zero weight in P.
   const char* kbase = (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
   const char* vbase = (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -575,9 +575,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     };
     using std::integral_constant;
 
-    // Prologue: the four V stages cleared (V stage 3 is read by the first
-    // step's P V with P = 0; rows past a block's end are never fetched, see
-    // issue); descriptors of c_0..3; K(c_0..2), V(c_0..1); S^T of unit 0; K
+    // Prologue: descriptors of c_0..3; K(c_0..2), V(c_0..1); V stage 3
+    // cleared (the first step's P V reads it with P = 0); S^T of unit 0; K
     // fragments of unit 1.
     fill(integral_constant<int, 0>{});
 #pragma unroll
@@ -585,21 +584,16 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     fill(integral_constant<int, 1>{});
     fill(integral_constant<int, 2>{});
     fill(integral_constant<int, 3>{});
-    {
-      constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane and stage
-#pragma unroll
-      for (int st = 4; st < 8; ++st)
-#pragma unroll
-        for (int i = 0; i < per; ++i) *(u32x4*)(&smem[st][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
-      // every wave's clearing stores land before any wave's direct loads into
-      // the same stages
-      __syncthreads();
-    }
     load_k(integral_constant<int, 0>{});
     load_k(integral_constant<int, 1>{});
     load_k(integral_constant<int, 2>{});
     load_v(integral_constant<int, 0>{});
     load_v(integral_constant<int, 1>{});
+    {
+      constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane
+#pragma unroll
+      for (int i = 0; i < per; ++i) *(u32x4*)(&smem[7][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     kread(uoff(integral_constant<int, 0>{}, H0));

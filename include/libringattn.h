@@ -169,7 +169,8 @@ int ra_rank_share_zigzag(const ra_tensor *q, const ra_tensor *k, const ra_tensor
  *               the ring would carry back to the key's owner;
  *   delta:      [B, Hq, N/P] fp32 workspace owned by the caller (D_i).
  * bf16 q/k/v only (RA_E_UNSUPPORTED otherwise); shapes and strides as for
- * ra_rank_share.  Four launches on opts->stream. */
+ * ra_rank_share, and the sequence stride of q and dout (stride[1]) also at
+ * most 2^24 elements (RA_E_RANGE otherwise).  Four launches on opts->stream. */
 int ra_rank_share_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                       const ra_tensor *o, const ra_tensor *lse, const ra_tensor *dout,
                       int P, int rank, int causal,

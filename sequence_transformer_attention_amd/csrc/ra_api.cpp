@@ -331,6 +331,9 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   if (nq != nb) return fail(RA_E_SHAPE, "local query block has %lld rows, expected N/P = %lld", (long long)nq, (long long)nb);
   if ((e = check_out(o, q, "o")) || (e = check_out(dout, q, "dout")) || (e = check_out(dq, q, "dq"))) return e;
   if (o->dtype != RA_BF16 || dout->dtype != RA_BF16) return fail(RA_E_DTYPE, "o and dout must be bf16");
+  // the dK/dV kernel loads q and dout tiles with 32-bit byte offsets, like k and v
+  if (q->stride[1] > (int64_t(1) << 24) || dout->stride[1] > (int64_t(1) << 24))
+    return fail(RA_E_RANGE, "q/dout sequence stride exceeds 2^24 elements");
   if (dq->dtype != RA_F32) return fail(RA_E_DTYPE, "dq must be fp32");
   if ((e = check_bshd(dk, "dk")) || (e = check_bshd(dv, "dv"))) return e;
   if (!same_shape(dk, k) || !same_shape(dv, k)) return fail(RA_E_SHAPE, "dk and dv must have the shape of k");

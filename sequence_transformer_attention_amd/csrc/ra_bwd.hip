@@ -171,20 +171,21 @@ __device__ __forceinline__ void mfma_acc_drain(f32x16& c) {
 }
 
 // Load a 64-row tile (rows row0 .. row0 + nvalid - 1 of a [*, D] bf16 matrix
-// with row stride `stride` elements; rows past nvalid re-read the last one)
-// into LDS at dst, swizzled.  All NW waves take a share of 1 KiB chunks.
+// with row stride `stride` elements, at most 2^24; nvalid >= 1) into LDS at
+// dst, swizzled.  All NW waves take a share of 1 KiB chunks.  The buffer
+// range ends at row nvalid - 1, so rows past it are out of range: nothing is
+// fetched for them and their LDS bytes are written as zeros.
 template <int D, int NW>
 __device__ __forceinline__ void load_tile(const __bf16* row0, int64_t stride, int nvalid, char* dst, int wave,
                                           int lane) {
   constexpr int SLOTS = D / 8, TILE = 64 * D * 2, NL = TILE / 1024 / NW;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)row0, (short)0, (int)(unsigned)(64 * stride * 2), 0x00020000);
-  const int last = nvalid - 1;
+  const int nrec = (nvalid - 1) * (int)stride * 2 + 2 * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row0, (short)0, nrec, 0x00020000);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int ls = (wave * NL + i) * 64 + lane;
     const int r = ls / SLOTS;
-    const unsigned off = (unsigned)(r < last ? r : last) * (unsigned)stride * 2u + 16u * (unsigned)swz<SLOTS>(r, ls % SLOTS);
+    const unsigned off = (unsigned)r * (unsigned)stride * 2u + 16u * (unsigned)swz<SLOTS>(r, ls % SLOTS);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (wave * NL + i) * 1024), 16, off, 0, 0, 0);
   }
 }

@@ -202,6 +202,10 @@ def test_ra_rank_share_bwd_validation():
         args[key] = bad
         assert bwd(**args) == status, key
     assert bwd(**dict(good, Pn=4, rank=3)) == ra.RA_E_SHAPE        # Nq != N / P
+    # q and dout tiles are addressed with 32-bit offsets: sequence stride at most 2^24
+    big = [512 * (1 << 25), 1 << 25, 128, 1]
+    assert bwd(**dict(good, q=T([1, 512, 4, 128], stride=big))) == ra.RA_E_RANGE
+    assert bwd(**dict(good, dout=T([1, 512, 4, 128], stride=big))) == ra.RA_E_RANGE
     f32 = dict(good, q=T([1, 512, 4, 128], ra.RA_F32), k=T([1, 4096, 1, 128], ra.RA_F32),
                v=T([1, 4096, 1, 128], ra.RA_F32))
     assert bwd(**f32) == ra.RA_E_UNSUPPORTED

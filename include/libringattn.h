@@ -221,6 +221,12 @@ int64_t ra_plan_tiles(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, in
 /* Query/key tile shape (rows bm, keys bn) the kernels use for this dtype and d. */
 int ra_tile_shape(int32_t dtype, int64_t d, int64_t *bm, int64_t *bn);
 
+/* Algorithmic FLOP of one (query block, key block) pair as one ra_step
+ * folds it, per batch entry: 4 * nq * nkv * d * hq weighted 1 for FULL, 1/2
+ * for PARTIAL, 0 for SKIP (the classes of ra_classify).  -1 for a negative
+ * argument.  Host only. */
+double ra_flops(int64_t nq, int64_t nkv, int64_t q_off, int64_t kv_off, int64_t hq, int64_t d, int causal);
+
 /* Algorithmic FLOP of one rank's share, 4 * Nq * Nkv * d * Hq * B per block,
  * weighted 1 for FULL, 1/2 for PARTIAL (the causal diagonal), 0 for SKIP. */
 double ra_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d,

@@ -423,6 +423,13 @@ int ra_tile_shape(int32_t dtype, int64_t d, int64_t* bm, int64_t* bn) {
   return ok();
 }
 
+double ra_flops(int64_t nq, int64_t nkv, int64_t q_off, int64_t kv_off, int64_t hq, int64_t d, int causal) {
+  if (nq < 0 || nkv < 0 || q_off < 0 || kv_off < 0 || hq < 0 || d < 0) return -1.0;
+  const int c = ra_plan_class(q_off, nq, kv_off, nkv, causal);
+  const double unit = 4.0 * (double)nq * (double)nkv * (double)d * (double)hq;
+  return c == RA_CLASS_FULL ? unit : (c == RA_CLASS_PARTIAL ? 0.5 * unit : 0.0);
+}
+
 double ra_share_flops(int64_t B, int64_t N, int64_t P, int64_t rank, int64_t hq, int64_t d, int causal) {
   if (P < 1 || N % P != 0 || rank < 0 || rank >= P) return -1.0;
   const int64_t nb = N / P;

@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.ra_plan_tiles.restype = i64
     L.ra_tile_shape.argtypes = [ctypes.c_int32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.ra_tile_shape.restype = ctypes.c_int
+    L.ra_flops.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    L.ra_flops.restype = ctypes.c_double
     L.ra_share_flops.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.ra_share_flops.restype = ctypes.c_double
     L.ra_share_flops_zigzag.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
@@ -249,6 +251,10 @@ def ra_tile_shape(dtype: torch.dtype, d: int):
     bm, bn = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().ra_tile_shape(_DT[dtype], d, ctypes.byref(bm), ctypes.byref(bn)))
     return bm.value, bn.value
+
+
+def ra_flops(nq: int, nkv: int, q_off: int, kv_off: int, Hq: int, d: int, causal: bool) -> float:
+    return float(lib().ra_flops(nq, nkv, q_off, kv_off, Hq, d, int(bool(causal))))
 
 
 def ra_share_flops(B: int, N: int, P: int, rank: int, Hq: int, d: int, causal: bool) -> float:

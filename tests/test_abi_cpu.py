@@ -314,6 +314,24 @@ def test_share_flops_match_oracle():
                 oracle.share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal)
 
 
+def test_block_flops_sum_to_the_share_and_follow_the_classes():
+    # per ring step, ra_flops of the (local block, arriving block) pair, times B,
+    # sums to the share's FLOP (the oracle's rule)
+    for w in workloads.ALL:
+        nb = w.N // w.P
+        for r in range(w.P):
+            tot = sum(ra.ra_flops(nb, nb, r * nb, ra.ra_ring_block(w.P, r, s) * nb, w.Hq, w.d, w.causal)
+                      for s in range(w.P))
+            assert tot * w.B == oracle.share_flops(w.B, w.N, w.P, r, w.Hq, w.d, w.causal)
+    # weights 1, 1/2, 0 by the oracle's class, on ragged blocks and offsets
+    for q_off, nq, kv_off, nkv in ((0, 7, 0, 5), (10, 3, 2, 4), (3, 5, 6, 9), (0, 1, 1, 1), (100, 64, 0, 100)):
+        for causal in (False, True):
+            c = oracle.classify(q_off, nq, kv_off, nkv, causal)
+            want = {0: 0.0, 1: 1.0, 2: 0.5}[c] * 4 * nq * nkv * 128 * 3
+            assert ra.ra_flops(nq, nkv, q_off, kv_off, 3, 128, causal) == want
+    assert ra.ra_flops(-1, 4, 0, 0, 1, 64, True) == -1.0
+
+
 def test_zigzag_share_flops_match_oracle():
     for (B, N, P, H, d) in ((1, 32768, 8, 32, 128), (1, 131072, 16, 32, 128), (2, 1200, 3, 2, 64)):
         for r in range(P):

@@ -60,6 +60,17 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, O_gpu, lse_gpu, target_s: float):
     """Oracle (fp64 C, pthreads) on a seeded sample of the share's rows."""
     import numpy as np
@@ -112,7 +123,7 @@ def cpu_baseline(w, x, O_gpu, lse_gpu, target_s: float):
     base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} random (b, h, i) rows of the same share, each against all its visible "
                       f"keys in ring order; {flops:.3e} FLOP in {dt:.2f} s (fp64, plain C)",
-            "extrapolated_share_s": round(share_flops / (flops / dt), 1)}
+            "extrapolated_share_s": round(share_flops / (flops / dt), 1), "cpu": cpu_model()}
     return base, parity
 
 

@@ -451,25 +451,38 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const int t0a = first_tile(a.q_off), t0b = a.nsplit == 2 ? first_tile(a.q_off2) : ntq;
   const int na = ntq - t0a, nt = na + (ntq - t0b);
   const int total = kfirst < a.kv_end ? G * nt : 0;  // no key before the key end: nothing to do
-  // tile it of the walk: query head, first local row, rows in its chunk,
-  // position of its first row
+  // A tile of the walk, walk index h * nt + w: query head g G + h, entry w
+  // of the head's tile list; its first local row, rows in its chunk and the
+  // position of its first row.  Two cursors step through the walk, one for
+  // the loads and one for the computation, so no tile needs a division.
   struct TileRef {
     int h, r0, nvalid;
     int64_t qp0;
   };
-  auto tile_ref = [&](int it) -> TileRef {
-    const int w = it % nt, ch = w >= na ? 1 : 0;
-    const int t = ch ? t0b + (w - na) : t0a + w;
+  struct WalkCur {
+    int h, w;
+  };
+  auto tile_ref = [&](const WalkCur& c) -> TileRef {
+    const int ch = c.w >= na ? 1 : 0;
+    const int t = ch ? t0b + (c.w - na) : t0a + c.w;
     TileRef r;
-    r.h = g * G + it / nt;
+    r.h = g * G + c.h;
     r.r0 = ch * nqc + t * BN;
     r.nvalid = min(BN, nqc - t * BN);
     r.qp0 = (ch ? a.q_off2 : a.q_off) + (int64_t)t * BN;
     return r;
   };
+  auto walk_next = [&](WalkCur& c) {
+    if (++c.w == nt) {
+      c.w = 0;
+      ++c.h;
+    }
+  };
+  WalkCur cl{0, 0}, cc{0, 0};  // load cursor, compute cursor
   float lsv = 0.f, dlv = 0.f;  // threads 0..63: LSE log2(e) and D of row tid of the tile in flight
-  auto issue = [&](int it, int st) __attribute__((always_inline)) {
-    const TileRef tr = tile_ref(it);
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const TileRef tr = tile_ref(cl);
+    walk_next(cl);
     const int h = tr.h, r0 = tr.r0, nvalid = tr.nvalid;
     load_tile<D, NW>((const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss, a.q_ss,
                      nvalid, &smem[st][0][0], wave, lane);
@@ -486,7 +499,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // One tile: stage ST (compile time, so every LDS offset is an immediate).
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
-    const int64_t qp0 = tile_ref(it).qp0;
+    const int64_t qp0 = tile_ref(cc).qp0;
+    walk_next(cc);
     // this lane's key relative to the tile's first query position (bounded
     // above by the tile walk; saturated below)
     const int64_t rel64 = my_k - qp0;
@@ -497,7 +511,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       lsd[st][1][tid] = dlv;
     }
     __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
-    if (it + 1 < total) issue(it + 1, st ^ 1);
+    if (it + 1 < total) issue(st ^ 1);
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
       constexpr unsigned qo = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // Q unit; dO unit at + TILE
@@ -617,7 +631,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       }
     });
   };
-  if (total > 0) issue(0, 0);
+  if (total > 0) issue(0);
   for (int it = 0; it < total; it += 2) {
     tile(it, std::integral_constant<int, 0>{});
     if (it + 1 < total) tile(it + 1, std::integral_constant<int, 1>{});

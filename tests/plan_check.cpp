@@ -81,6 +81,35 @@ int main() {
         }
       }
   }
+  // Dispatch of the rank-7-of-8 share (16 query tiles of 256 rows per head,
+  // 32 heads; a tile t of the diagonal block costs 7 full blocks of 64 key
+  // tiles plus 4 (t + 1) diagonal ones) on 8 XCDs of 32 CUs, one workgroup
+  // per CU, each next workgroup of an XCD to the CU that frees up first: the
+  // paired order gives every CU the same work (the makespan equals the mean
+  // load), while one head's tiles in a row leave 3 % of it on the table.
+  {
+    const int nqt = 16, heads = 32, nwg = nqt * heads, cus = 32;
+    double worst = 0, total = 0;
+    for (int x = 0; x < 8; ++x) {
+      std::vector<double> free_at(cus, 0.0);
+      for (int i = 0; i < nwg / 8; ++i) {
+        int h, t;
+        ra_plan_head_tile(ra_plan_xcd_remap(8 * i + x, nwg, nqt), nwg, nqt, 1, &h, &t);
+        const double cost = 7 * 64 + 4 * (t + 1);
+        int best = 0;
+        for (int c = 1; c < cus; ++c)
+          if (free_at[c] < free_at[best]) best = c;
+        free_at[best] += cost;
+        total += cost;
+      }
+      for (double f : free_at) worst = f > worst ? f : worst;
+    }
+    const double mean = total / (8.0 * cus);
+    if (worst > mean * 1.001) {
+      std::printf("unbalanced dispatch: makespan %g, mean load %g\n", worst, mean);
+      return 1;
+    }
+  }
   std::printf("ok\n");
   return 0;
 }

@@ -93,8 +93,10 @@ typedef struct {
     const ra_tensor *lse_out;   /* log-sum-exp [B, Hq, Nq, 1] fp32, natural log; optional */
 } ra_opts;
 
-/* Fill the running state with the empty state: o_acc = 0, m = -inf, l = 0.
- * o_acc fp32 [B, Nq, H, d]; m, l fp32 [B, H, Nq, 1]. */
+/* Fill the running state with the empty state: o_acc = 0, m = -inf, l = 0
+ * (the state before the first block of "Ring Attention" / "Computation";
+ * as a merge operand it changes nothing).  o_acc fp32 [B, Nq, H, d] with
+ * d in {64, 128}; m, l fp32 [B, H, Nq, 1].  Caller-owned, written in place. */
 int ra_state_init(const ra_tensor *o_acc, const ra_tensor *m, const ra_tensor *l,
                   const ra_opts *opts);
 
@@ -110,9 +112,41 @@ int ra_step(const ra_tensor *q, const ra_tensor *k_blk, const ra_tensor *v_blk,
             int64_t q_off, int64_t kv_off, int causal, const ra_opts *opts);
 
 /* Normalise the running state: O = o_acc / l, and LSE = m + ln l.
- * O goes to opts->o_out when given (bf16 or fp32), else in place into o_acc.
- * LSE goes to opts->lse_out when given, which then needs opts->m. */
+ * Source: glossary page "sequence parallelism transformers", section
+ * "Implementation Considerations", item "Numerical Stability" (the softmax
+ * normalisation is carried as (m, l) and applied once all blocks are in),
+ * and section "Ring Attention", item "Computation" (the accumulated result
+ * is then full softmax attention).  The LSE output (natural log) is the one
+ * statistic the backward needs.
+ *   o_acc: fp32 [B, S, H, d], d in {64, 128}, read (or overwritten in place);
+ *   l, opts->m: fp32 [B, H, S, 1], read;
+ *   opts->o_out: [B, S, H, d] bf16 or fp32, written, optional (NULL: O is
+ *   written in place into o_acc); opts->lse_out: fp32 [B, H, S, 1], written,
+ *   optional, needs opts->m (RA_E_NULL otherwise).
+ * A row with l = 0 (no visible key) gives 0/0 like the definition.  All
+ * buffers are the caller's; errors as for every call.  One launch,
+ * HBM-bound: (6d + 12) bytes per row for a bf16 O. */
 int ra_finalize(const ra_tensor *o_acc, const ra_tensor *l, const ra_opts *opts);
+
+/* Merge a second partial state into the running state, in place:
+ *   m' = max(m, m_b); w = e^{m - m'}, w_b = e^{m_b - m'} (0 for a side with
+ *   m = -inf); l' = w l + w_b l_b; o_acc' = w o_acc + w_b o_b.
+ * Source: glossary page "sequence parallelism transformers", section "Ring
+ * Attention", item "Computation" (each block's result is accumulated and
+ * the accumulation equals full attention), and section "Implementation
+ * Considerations", item "Numerical Stability" (the running maximum and sum
+ * per row).  The pages print no formula: this is the exact log-sum-exp
+ * rescaling to the common maximum, the only combination of two partials
+ * over disjoint key sets that gives the softmax over their union.  The
+ * empty state (0, -inf, 0) is its identity, and it is commutative and
+ * associative up to rounding, so blocks may arrive in any order.
+ *   o_acc, o_b: fp32 [B, S, H, d], d in {64, 128} (o_acc read and written,
+ *               o_b read);
+ *   m, l, m_b, l_b: fp32 [B, H, S, 1] (m, l read and written).
+ * All buffers are the caller's.  One launch, HBM-bound: 3 (4d + 8) bytes per
+ * row.  Errors as for every call. */
+int ra_merge(const ra_tensor *o_acc, const ra_tensor *m, const ra_tensor *l,
+             const ra_tensor *o_b, const ra_tensor *m_b, const ra_tensor *l_b, const ra_opts *opts);
 
 /* One rank's whole share in one launch: the local query block
  * q [B, N/P, Hq, d] of rank `rank` (global positions rank*N/P..) against the
@@ -120,7 +154,20 @@ int ra_finalize(const ra_tensor *o_acc, const ra_tensor *l, const ra_opts *opts)
  * at step s), causal blocks skipped per (q_off, kv_off), the running state
  * kept on chip, normalised at the end.  Writes O to opts->o_out (required)
  * and LSE to opts->lse_out (optional).  N % P != 0 or Nq != N/P is
- * RA_E_SHAPE: uneven lengths are not padded silently. */
+ * RA_E_SHAPE: uneven lengths are not padded silently.
+ * Source: glossary page "sequence parallelism transformers", section
+ * "Fundamentals", item "Sequence Dimension Splitting" (contiguous chunks of
+ * N/P), section "Ring Attention", items "Ring Communication" (the block
+ * order) and "Computation" (attend, accumulate; equal to full attention),
+ * section "Implementation Considerations", item "Numerical Stability" (the
+ * running max and sum); with P = 1, section "Ulysses Sequence Parallelism",
+ * item "Attention Computation".  The causal rule and the skipping of blocks
+ * with no visible key are not on the pages: a key is visible iff its global
+ * position is at or before the query's (the usual autoregressive mask), and
+ * a block that holds no visible key for any local query is never read.
+ *   q: [B, N/P, Hq, d]; k, v: [B, N, Hkv, d] (the whole sequence, block j =
+ *   rows [j N/P, (j+1) N/P)); o_out [B, N/P, Hq, d] bf16 or fp32; lse_out
+ *   [B, Hq, N/P, 1] fp32 natural log.  All device buffers are the caller's. */
 int ra_rank_share(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                   int P, int rank, int causal, const ra_opts *opts);
 
@@ -204,17 +251,28 @@ int ra_rank_share_padded_bwd(const ra_tensor *q, const ra_tensor *k, const ra_te
 
 /* ---- host-only queries (no GPU needed) --------------------------------- */
 
-/* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1. */
+/* Block held by `rank` at ring step s: (rank - s) mod P.  -1 if P < 1.
+ * Source: glossary page "sequence parallelism transformers", section "Ring
+ * Attention", item "Ring Communication" (blocks move one rank up the ring
+ * per step, so a rank receives from the rank below it).  Host only. */
 int64_t ra_ring_block(int64_t P, int64_t rank, int64_t s);
 
 /* Class of the (query positions [q_off, q_off+nq), key positions
  * [kv_off, kv_off+nkv)) pair: 0 = SKIP (no visible pair), 1 = FULL (all
- * visible), 2 = PARTIAL. */
+ * visible), 2 = PARTIAL.  The pages define neither causal masking nor block
+ * skipping: the rule is that of causal attention at global positions (a key
+ * is visible iff kv <= q, all keys visible when causal == 0), applied per
+ * (q_off, kv_off) pair; the kernels take their block and tile decisions
+ * with the same function.  Host only. */
 int ra_classify(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal);
 
 /* Tile plan of one step as the kernels use it: out[ti * ceil(nkv/bn) + tj] =
  * ra_classify of query tile ti (bm rows) and key tile tj (bn keys), tails
- * ragged.  Returns the number of tiles written, or a negative ra_status. */
+ * ragged.  Returns the number of tiles written, or a negative ra_status.
+ * Same source as ra_classify (glossary page "sequence parallelism
+ * transformers", section "Flash Attention with Sequence Parallelism", item
+ * "Tiled Computation", for the tiling; the causal classes are not on the
+ * pages).  out: host array of out_len entries, caller-owned.  Host only. */
 int64_t ra_plan_tiles(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv, int causal,
                       int64_t bm, int64_t bn, int8_t *out, int64_t out_len);
 
@@ -224,7 +282,10 @@ int ra_tile_shape(int32_t dtype, int64_t d, int64_t *bm, int64_t *bn);
 /* Algorithmic FLOP of one (query block, key block) pair as one ra_step
  * folds it, per batch entry: 4 * nq * nkv * d * hq weighted 1 for FULL, 1/2
  * for PARTIAL, 0 for SKIP (the classes of ra_classify).  -1 for a negative
- * argument.  Host only. */
+ * argument.  Host only.  The pages give no FLOP count: 4 d per (query, key)
+ * pair is the two products Q K^T and P V of 2 d FLOP each, and the causal
+ * diagonal block is halved (its visible pairs are half the block, up to the
+ * diagonal itself). */
 double ra_flops(int64_t nq, int64_t nkv, int64_t q_off, int64_t kv_off, int64_t hq, int64_t d, int causal);
 
 /* Algorithmic FLOP of one rank's share, 4 * Nq * Nkv * d * Hq * B per block,

@@ -119,10 +119,13 @@ int check_qkv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const 
   return RA_OK;
 }
 
-int check_grid(int64_t nq, int64_t bm, int64_t hq, int64_t B) {
-  const int64_t wg = ((nq + bm - 1) / bm) * hq * B;
-  if (wg > (int64_t)std::numeric_limits<int32_t>::max())
-    return fail(RA_E_RANGE, "too many query tiles for one launch (%lld)", (long long)wg);
+// A launch of ceil(rows / bm) * heads * B workgroups of `threads` threads: HIP
+// takes at most 2^32 - 1 work-items along the grid's x dimension.
+int check_grid(int64_t rows, int64_t bm, int64_t heads, int64_t B, int64_t threads) {
+  const int64_t wg = ((rows + bm - 1) / bm) * heads * B;
+  if (wg > (int64_t)std::numeric_limits<uint32_t>::max() / threads)
+    return fail(RA_E_RANGE, "launch too large: %lld workgroups of %lld threads exceed 2^32 - 1 work-items",
+                (long long)wg, (long long)threads);
   return RA_OK;
 }
 
@@ -143,6 +146,18 @@ int launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// A state kernel (init, merge, finalize) over [B, S, H, d] rows.
+int check_state_grid(int64_t B, int64_t H, int64_t S, int64_t d) {
+  if (B > std::numeric_limits<int32_t>::max() || H > std::numeric_limits<int32_t>::max() ||
+      S > std::numeric_limits<int32_t>::max())
+    return fail(RA_E_RANGE, "state dimensions exceed 2^31 - 1");
+  const int64_t wg = ra_state_workgroups(B, H, S, d);
+  if (wg > (int64_t)std::numeric_limits<uint32_t>::max() / RA_STATE_THREADS)
+    return fail(RA_E_RANGE, "launch too large: %lld workgroups of %d threads exceed 2^32 - 1 work-items",
+                (long long)wg, RA_STATE_THREADS);
+  return RA_OK;
+}
+
 int check_out(const ra_tensor* o, const ra_tensor* like, const char* name) {
   int e = check_bshd(o, name);
   if (e) return e;
@@ -160,8 +175,9 @@ int ra_state_init(const ra_tensor* o_acc, const ra_tensor* m, const ra_tensor* l
   if (o_acc->dtype != RA_F32) return fail(RA_E_DTYPE, "o_acc must be fp32");
   const int64_t B = o_acc->shape[0], S = o_acc->shape[1], H = o_acc->shape[2], d = o_acc->shape[3];
   if ((e = check_rows(m, "m", B, H, S)) || (e = check_rows(l, "l", B, H, S))) return e;
-  if (d % 4 != 0) return fail(RA_E_UNSUPPORTED, "head_dim must be a multiple of 4");
-  if (B * S * H * d == 0) return ok();
+  if (d != 64 && d != 128) return fail(RA_E_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  if ((e = check_state_grid(B, H, S, d))) return e;
+  if (B * S * H == 0) return ok();
   RaInitArgs a{};
   a.oacc = (float*)o_acc->data;
   set_bshd(o_acc, a.oa_sb, a.oa_ss, a.oa_sh);
@@ -186,7 +202,7 @@ int ra_step(const ra_tensor* q, const ra_tensor* k_blk, const ra_tensor* v_blk, 
   if ((e = check_rows(m, "m", B, hq, nq)) || (e = check_rows(l, "l", B, hq, nq))) return e;
   if (q_off < 0 || kv_off < 0) return fail(RA_E_RANGE, "q_off and kv_off must be >= 0");
   const int64_t bm = q->dtype == RA_BF16 ? RA_BF16_BM : RA_F32_BM;
-  if ((e = check_grid(nq, bm, hq, B))) return e;
+  if ((e = check_grid(nq, bm, hq, B, q->dtype == RA_BF16 ? RA_BF16_THREADS : RA_F32_THREADS))) return e;
   if (B == 0 || nq == 0 || ra_plan_class(q_off, nq, kv_off, nkv, causal) == RA_CLASS_SKIP) return ok();
 
   RaAttnArgs a{};
@@ -223,6 +239,7 @@ int ra_finalize(const ra_tensor* o_acc, const ra_tensor* l, const ra_opts* opts)
     if (!mt) return fail(RA_E_NULL, "lse_out needs opts->m");
     if ((e = check_rows(mt, "m", B, H, S)) || (e = check_rows(lse, "lse_out", B, H, S))) return e;
   }
+  if ((e = check_state_grid(B, H, S, d))) return e;
   if (B * S * H == 0) return ok();
   RaFinArgs a{};
   a.oacc = (const float*)o_acc->data; set_bshd(o_acc, a.oa_sb, a.oa_ss, a.oa_sh);
@@ -238,6 +255,30 @@ int ra_finalize(const ra_tensor* o_acc, const ra_tensor* l, const ra_opts* opts)
   }
   a.B = (int32_t)B; a.S = (int32_t)S; a.H = (int32_t)H; a.d = (int32_t)d;
   return launched(ra_launch_finalize(a, stream_of(opts)), "ra_finalize launch");
+}
+
+int ra_merge(const ra_tensor* o_acc, const ra_tensor* m, const ra_tensor* l, const ra_tensor* o_b,
+             const ra_tensor* m_b, const ra_tensor* l_b, const ra_opts* opts) {
+  int e;
+  if ((e = check_bshd(o_acc, "o_acc")) || (e = check_bshd(o_b, "o_b"))) return e;
+  if (o_acc->dtype != RA_F32 || o_b->dtype != RA_F32) return fail(RA_E_DTYPE, "o_acc and o_b must be fp32");
+  if (!same_shape(o_acc, o_b)) return fail(RA_E_SHAPE, "o_b must have the shape of o_acc");
+  const int64_t B = o_acc->shape[0], S = o_acc->shape[1], H = o_acc->shape[2], d = o_acc->shape[3];
+  if ((e = check_rows(m, "m", B, H, S)) || (e = check_rows(l, "l", B, H, S)) || (e = check_rows(m_b, "m_b", B, H, S)) ||
+      (e = check_rows(l_b, "l_b", B, H, S)))
+    return e;
+  if (d != 64 && d != 128) return fail(RA_E_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  if ((e = check_state_grid(B, H, S, d))) return e;
+  if (B * S * H == 0) return ok();
+  RaMergeArgs a{};
+  a.oa = (float*)o_acc->data; set_bshd(o_acc, a.oa_sb, a.oa_ss, a.oa_sh);
+  a.ma = (float*)m->data; set_rows(m, a.ma_sb, a.ma_sh, a.ma_ss);
+  a.la = (float*)l->data; set_rows(l, a.la_sb, a.la_sh, a.la_ss);
+  a.ob = (const float*)o_b->data; set_bshd(o_b, a.ob_sb, a.ob_ss, a.ob_sh);
+  a.mb = (const float*)m_b->data; set_rows(m_b, a.mb_sb, a.mb_sh, a.mb_ss);
+  a.lb = (const float*)l_b->data; set_rows(l_b, a.lb_sb, a.lb_sh, a.lb_ss);
+  a.B = (int32_t)B; a.H = (int32_t)H; a.S = (int32_t)S; a.d = (int32_t)d;
+  return launched(ra_launch_merge(a, stream_of(opts)), "ra_merge launch");
 }
 
 // One rank's share in one launch.  zigzag == 0: the local rows are block
@@ -268,7 +309,9 @@ static int rank_share(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
   if ((e = check_out(opts->o_out, q, "o_out"))) return e;
   if (opts->lse_out && (e = check_rows(opts->lse_out, "lse_out", B, hq, nq))) return e;
   const int64_t bm = q->dtype == RA_BF16 ? RA_BF16_BM : RA_F32_BM;
-  if ((e = check_grid(zigzag ? 2 * ((nb + bm - 1) / bm) * bm : nq, bm, hq, B))) return e;
+  if ((e = check_grid(zigzag ? 2 * ((nb + bm - 1) / bm) * bm : nq, bm, hq, B,
+                      q->dtype == RA_BF16 ? RA_BF16_THREADS : RA_F32_THREADS)))
+    return e;
   if (B == 0 || nq == 0) return ok();
 
   RaAttnArgs a{};
@@ -340,7 +383,10 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   if (dk->dtype != RA_F32 || dv->dtype != RA_F32) return fail(RA_E_DTYPE, "dk and dv must be fp32");
   if ((e = check_rows(lse, "lse", B, hq, nq)) || (e = check_rows(delta, "delta", B, hq, nq))) return e;
   const int64_t qrows = zigzag ? 2 * ((N / parts + RA_BWD_BM - 1) / RA_BWD_BM) * RA_BWD_BM : nq;
-  if ((e = check_grid(qrows, RA_BWD_BM, hq, B)) || (e = check_grid(N, RA_BWD_BM, k->shape[2], B))) return e;
+  if ((e = check_grid(qrows, RA_BWD_BM, hq, B, RA_BWD_THREADS)) ||
+      (e = check_grid(N, RA_BWD_BM, k->shape[2], B, RA_BWD_THREADS)) ||
+      (e = check_grid(nq, RA_BWD_THREADS, hq, B, RA_BWD_THREADS)))  // prep: one thread per query row
+    return e;
   if (B == 0 || nq == 0) return ok();
 
   RaBwdArgs a{};

@@ -43,5 +43,6 @@ struct RaBwdArgs {
 
 // Rows of a workgroup: queries of the dQ kernel, keys of the dK/dV kernel.
 constexpr int RA_BWD_BM = 128, RA_BWD_BN = 64;
+constexpr int RA_BWD_THREADS = 256;  // threads per workgroup of every backward kernel
 
 hipError_t ra_launch_bwd(const RaBwdArgs& a, int d, hipStream_t s);

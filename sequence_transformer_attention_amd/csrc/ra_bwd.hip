@@ -345,18 +345,17 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
         ds_rdtr<off>(thi[hh][d_], ta.tr[1][d_]);
       });
       // key index of register r: 8 (r / 4) + (r % 4) + 4 lg; keys below lim are visible
-      const int nv = min(max(nvalid - 32 * hf, 0), 32);
+      const int nv = ra_plan_half_valid(nvalid, hf, 32);
       bf16x8 dsf[2];
       // all 32 keys of the unit exist and precede the wave's first query: no test
-      if (nv == 32 && (!a.causal || k0 + 32 * hf + 31 <= q0w)) {
+      if (!ra_plan_tile_masked<int64_t>(k0 + 32 * hf - q0w, nv, 32, a.causal)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(sacc[r] * a.c - lse2);
           dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
         }
       } else {
-        const int64_t vis = a.causal ? q0w + lr - (k0 + 32 * hf) + 1 : nv;
-        const int lim = (int)(vis < nv ? (vis > 0 ? vis : 0) : nv);
+        const int lim = (int)ra_plan_visible_prefix(q0w + lr, k0 + 32 * hf, nv, a.causal);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = 8 * (r >> 2) + (r & 3) + 4 * lg;
@@ -443,11 +442,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   const int64_t kfirst = (int64_t)kt * BK;
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
   const int ntq = (nqc + BN - 1) / BN;  // tiles per chunk
-  auto first_tile = [&](int64_t qpos) -> int {
-    int64_t qlo = a.causal ? kfirst - qpos : 0;
-    qlo = qlo < 0 ? 0 : qlo;
-    return qlo >= nqc ? ntq : (int)(qlo / BN);
-  };
+  auto first_tile = [&](int64_t qpos) -> int { return ra_plan_first_query_tile(kfirst, qpos, nqc, BN, a.causal); };
   const int t0a = first_tile(a.q_off), t0b = a.nsplit == 2 ? first_tile(a.q_off2) : ntq;
   const int na = ntq - t0a, nt = na + (ntq - t0b);
   const int total = kfirst < a.kv_end ? G * nt : 0;  // no key before the key end: nothing to do

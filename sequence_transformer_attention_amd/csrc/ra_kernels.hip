@@ -323,7 +323,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       if (rem > 0) {
         drel[j] = crel;
         const int nv = cleft < BN ? cleft : BN;
-        dv[j] = nv + ((nv < BN || (a.causal && crel + BN - 1 > 0)) ? 128 : 0);
+        dv[j] = nv + (ra_plan_tile_masked<int>(crel, nv, BN, a.causal) ? 128 : 0);
         dka[j] = cka;
         dva[j] = cva;
         if (--rem > 0) {
@@ -412,22 +412,14 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
     // Softmax of the unit whose S^T is in sacc[x], at key position k0 with
     // nvalid valid keys.  Mask (a rare branch before the step's region): keys
     // kvi < lim of the unit are visible to this lane's query: lim = valid keys,
-    // cut at the query's own position under causal masking, 0 for SKIP (no
-    // visible key for these rows: p = 0).  The key index of register r is
+    // cut at the query's own position under causal masking (0 when the whole
+    // unit lies after it: p = 0).  The key index of register r is
     // 8 (r / 4) + (r % 4) + 4 lg.
-    const int nqw = min(32, nqc - qrow_w);
     auto sm_mask = [&](int x, int64_t k0, int nvalid) __attribute__((always_inline)) {
       // every key valid and, under causal masking, at or before the wave's
       // first query: nothing to mask (rows past nq are never stored)
-      const bool plain = nvalid == 32 && (!a.causal || k0 + 31 <= q0w);
-      if (__builtin_expect(!plain, 0)) {
-        const int cls = ra_plan_class(q0w, nqw, k0, nvalid, a.causal);
-        int64_t lim64 = cls == RA_CLASS_SKIP ? 0 : nvalid;
-        if (a.causal) {
-          const int64_t vis = q0w + lr - k0 + 1;
-          lim64 = vis < lim64 ? (vis > 0 ? vis : 0) : lim64;
-        }
-        const int lim = (int)lim64 - 4 * lg;
+      if (__builtin_expect(ra_plan_tile_masked<int64_t>(k0 - q0w, nvalid, 32, a.causal), 0)) {
+        const int lim = (int)ra_plan_visible_prefix(q0w + lr, k0, nvalid, a.causal) - 4 * lg;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           sacc[x][r] = (8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : sacc[x][r];
@@ -565,7 +557,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (sm) sm_fix(X);
     };
-    auto half_valid = [](int nv, int hf) { const int x = nv - 32 * hf; return x < 0 ? 0 : (x > 32 ? 32 : x); };
+    auto half_valid = [](int nv, int hf) { return ra_plan_half_valid(nv, hf, 32); };
     const std::true_type T;
     const std::false_type F;
     // byte offset of half H of the tile in stage S (K and V regions alike)
@@ -834,51 +826,6 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
   }
 }
 
-// O = o_acc / l and LSE = m + ln l; one thread per 4 channels of a row, rows
-// in [B, S, H] order so consecutive threads touch consecutive 16-byte chunks.
-__global__ void __launch_bounds__(256) finalize_kernel(RaFinArgs a) {
-  const int nd4 = a.d / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.S * a.H * nd4;
-  if (idx >= total) return;
-  const int c4 = (int)(idx % nd4);
-  const int64_t row = idx / nd4;
-  const int h = (int)(row % a.H);
-  const int64_t t = row / a.H;
-  const int s = (int)(t % a.S), b = (int)(t / a.S);
-  const float lv = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)s * a.l_ss];
-  const f32x4 x = *(const f32x4*)(a.oacc + (int64_t)b * a.oa_sb + (int64_t)s * a.oa_ss + (int64_t)h * a.oa_sh + 4 * c4);
-  const float inv = 1.f / lv;
-  const int64_t ob = (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 4 * c4;
-  if (a.o_bf16)
-    *(bf16x4*)((__bf16*)a.o + ob) = bf16x4{(__bf16)(x[0] * inv), (__bf16)(x[1] * inv),
-                                          (__bf16)(x[2] * inv), (__bf16)(x[3] * inv)};
-  else
-    *(f32x4*)((float*)a.o + ob) = f32x4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
-  if (c4 == 0 && a.lse) {
-    const float mv = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)s * a.m_ss];
-    a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)s * a.lse_ss] = mv + logf(lv);
-  }
-}
-
-__global__ void __launch_bounds__(256) init_kernel(RaInitArgs a) {
-  const int nd4 = a.d / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.S * a.H * nd4;
-  if (idx >= total) return;
-  const int c4 = (int)(idx % nd4);
-  const int64_t row = idx / nd4;
-  const int h = (int)(row % a.H);
-  const int64_t t = row / a.H;
-  const int s = (int)(t % a.S), b = (int)(t / a.S);
-  *(f32x4*)(a.oacc + (int64_t)b * a.oa_sb + (int64_t)s * a.oa_ss + (int64_t)h * a.oa_sh + 4 * c4) =
-      f32x4{0.f, 0.f, 0.f, 0.f};
-  if (c4 == 0) {
-    a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)s * a.m_ss] = -INFINITY;
-    a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)s * a.l_ss] = 0.f;
-  }
-}
-
 }  // namespace
 
 hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t st) {
@@ -892,19 +839,5 @@ hipError_t ra_launch_attn_f32(const RaAttnArgs& a, int d, hipStream_t st) {
   const dim3 grid((unsigned)(ra_query_tiles(a, RA_F32_BM) * a.Hq * a.B)), block(64);
   if (d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, block, 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t ra_launch_finalize(const RaFinArgs& a, hipStream_t st) {
-  const int64_t total = (int64_t)a.B * a.S * a.H * (a.d / 4);
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  hipLaunchKernelGGL(finalize_kernel, grid, block, 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t ra_launch_init(const RaInitArgs& a, hipStream_t st) {
-  const int64_t total = (int64_t)a.B * a.S * a.H * (a.d / 4);
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  hipLaunchKernelGGL(init_kernel, grid, block, 0, st, a);
   return hipGetLastError();
 }

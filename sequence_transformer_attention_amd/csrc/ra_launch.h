@@ -54,9 +54,27 @@ struct RaInitArgs {
   int32_t B, H, S, d;
 };
 
+// (oa, ma, la) <- merge((oa, ma, la), (ob, mb, lb)), in place.
+struct RaMergeArgs {
+  float* oa; int64_t oa_sb, oa_ss, oa_sh;
+  float* ma; int64_t ma_sb, ma_sh, ma_ss;
+  float* la; int64_t la_sb, la_sh, la_ss;
+  const float* ob; int64_t ob_sb, ob_ss, ob_sh;
+  const float* mb; int64_t mb_sb, mb_sh, mb_ss;
+  const float* lb; int64_t lb_sb, lb_sh, lb_ss;
+  int32_t B, H, S, d;
+};
+
+// Threads per workgroup of the state kernels (init, merge, finalize), and
+// their workgroup count for a [B, S, H, d] state (d = 64 or 128).
+constexpr int RA_STATE_THREADS = 256;
+int64_t ra_state_workgroups(int64_t B, int64_t H, int64_t S, int64_t d);
+
 // Tile shape of the attention kernels (query rows per workgroup, keys per tile).
 constexpr int RA_BF16_BM = 256, RA_BF16_BN = 64;
 constexpr int RA_F32_BM = 64, RA_F32_BN = 64;
+// Threads per workgroup of the attention kernels.
+constexpr int RA_BF16_THREADS = 512, RA_F32_THREADS = 64;
 
 // Query tiles of a launch: per chunk ceil(rows / BM), times the chunk count.
 inline int64_t ra_query_tiles(const RaAttnArgs& a, int bm) {
@@ -68,3 +86,4 @@ hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t s);
 hipError_t ra_launch_attn_f32(const RaAttnArgs& a, int d, hipStream_t s);
 hipError_t ra_launch_finalize(const RaFinArgs& a, hipStream_t s);
 hipError_t ra_launch_init(const RaInitArgs& a, hipStream_t s);
+hipError_t ra_launch_merge(const RaMergeArgs& a, hipStream_t s);

@@ -93,3 +93,42 @@ RA_HD int64_t ra_plan_key_tiles(int64_t q0, int64_t nq, int64_t k0, int64_t nk, 
   }
   return (n + bn - 1) / bn;
 }
+
+// Mask decision of a run of bn key slots holding nvalid keys (nvalid <= bn),
+// the first at relative position rel = (its global position) - q0, for the
+// queries at global positions q0, q0 + 1, ...: the run needs the masked
+// softmax unless all bn keys exist and, under causal masking, the last lies
+// at or before q0 (then every key is visible to every query from q0 on, the
+// pair is FULL).  I is the integer type of the caller (the kernels pass
+// 32-bit relative positions saturated at +-2^30, which keeps the sign).
+template <typename I>
+RA_HD bool ra_plan_tile_masked(I rel, I nvalid, I bn, int causal) {
+  return nvalid < bn || (causal && rel + bn - 1 > 0);
+}
+
+// Keys visible to the query at global position q in a run of nvalid keys
+// from global position k0: always a prefix, keys k0 .. k0 + lim - 1.
+RA_HD int64_t ra_plan_visible_prefix(int64_t q, int64_t k0, int64_t nvalid, int causal) {
+  if (!causal) return nvalid;
+  const int64_t vis = q - k0 + 1;
+  return vis < nvalid ? (vis > 0 ? vis : 0) : nvalid;
+}
+
+// Valid keys of slot half hf (0 or 1) of a run of nvalid keys of 2 * half
+// slots (a 64-key tile processed as two 32-key units).
+RA_HD int ra_plan_half_valid(int nvalid, int hf, int half) {
+  const int x = nvalid - half * hf;
+  return x < 0 ? 0 : (x > half ? half : x);
+}
+
+// First query tile (bn rows, from local row 0 at global position qpos, nqc
+// rows) that sees the key at global position kfirst, or the tile count when
+// none does: under causal masking the rows before kfirst see no key at or
+// after it; without masking every row sees every key.
+RA_HD int ra_plan_first_query_tile(int64_t kfirst, int64_t qpos, int nqc, int bn, int causal) {
+  const int ntq = (nqc + bn - 1) / bn;
+  int64_t qlo = causal ? kfirst - qpos : 0;
+  qlo = qlo < 0 ? 0 : qlo;
+  return qlo >= nqc ? ntq : (int)(qlo / bn);
+}
+

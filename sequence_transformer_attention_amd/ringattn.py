@@ -11,7 +11,6 @@ loading fails loudly otherwise.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -66,6 +65,7 @@ def lib() -> ctypes.CDLL:
     L.ra_state_init.argtypes = [T, T, T, O]
     L.ra_step.argtypes = [T, T, T, T, T, T, i64, i64, ctypes.c_int, O]
     L.ra_finalize.argtypes = [T, T, O]
+    L.ra_merge.argtypes = [T, T, T, T, T, T, O]
     L.ra_rank_share.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
     L.ra_rank_share_zigzag.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, O]
     L.ra_rank_share_padded.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, O]
@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
     L.ra_rank_share_zigzag_bwd.argtypes = L.ra_rank_share_bwd.argtypes
     L.ra_rank_share_padded_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64,
                                            T, T, T, T, O]
-    for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_rank_share, L.ra_rank_share_zigzag,
+    for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_merge, L.ra_rank_share, L.ra_rank_share_zigzag,
               L.ra_rank_share_bwd, L.ra_rank_share_padded, L.ra_rank_share_zigzag_bwd,
               L.ra_rank_share_padded_bwd):
         f.restype = ctypes.c_int
@@ -171,6 +171,15 @@ def ra_finalize(o_acc, l, m=None, o_out=None, lse_out=None, stream=None) -> None
     """O = o_acc / l into o_out (or in place); LSE = m + ln l into lse_out."""
     opts, keep = _opts(stream, None, m=m, o_out=o_out, lse_out=lse_out)
     _check(lib().ra_finalize(_desc(o_acc), _desc(l, True), ctypes.byref(opts)))
+
+
+def ra_merge(o_acc, m, l, o_b, m_b, l_b, stream=None) -> None:
+    """Fold the partial state (o_b, m_b, l_b) into (o_acc, m, l) in place
+    (log-sum-exp rescaling to the common maximum); o fp32 [B, S, H, d],
+    m, l fp32 [B, H, S]."""
+    opts, keep = _opts(stream)
+    _check(lib().ra_merge(_desc(o_acc), _desc(m, True), _desc(l, True), _desc(o_b), _desc(m_b, True),
+                          _desc(l_b, True), ctypes.byref(opts)))
 
 
 def ra_rank_share(q, k, v, P: int, rank: int, causal: bool, o_out, lse_out=None,
@@ -271,7 +280,3 @@ def ra_last_error() -> str:
 
 def ra_version() -> str:
     return lib().ra_version().decode()
-
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)

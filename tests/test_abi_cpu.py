@@ -267,6 +267,58 @@ def test_ra_state_init_validation():
     assert L.ra_state_init(P(T([1, 8, 2, 64], ra.RA_F32)), P(rows(1, 2, 7)), P(rows(1, 2, 8)), None) == ra.RA_E_SHAPE
 
 
+def test_ra_state_init_rejects_other_head_dims():
+    L = ra.lib()
+    assert L.ra_state_init(P(T([1, 8, 2, 96], ra.RA_F32)), P(rows(1, 2, 8)), P(rows(1, 2, 8)), None) == \
+        ra.RA_E_UNSUPPORTED
+
+
+def test_ra_merge_validation():
+    L = ra.lib()
+    oa, ob = T([1, 64, 2, 128], ra.RA_F32), T([1, 64, 2, 128], ra.RA_F32)
+    m, l, mb, lb = rows(1, 2, 64), rows(1, 2, 64), rows(1, 2, 64), rows(1, 2, 64)
+
+    def merge(oa=oa, m=m, l=l, ob=ob, mb=mb, lb=lb):
+        return L.ra_merge(P(oa), P(m), P(l), P(ob), P(mb), P(lb), None)
+
+    assert merge(oa=None) == ra.RA_E_NULL
+    assert merge(lb=None) == ra.RA_E_NULL
+    assert merge(ob=T([1, 64, 2, 128])) == ra.RA_E_DTYPE                   # bf16 state
+    assert merge(ob=T([1, 63, 2, 128], ra.RA_F32)) == ra.RA_E_SHAPE         # shapes differ
+    assert merge(mb=rows(1, 2, 63)) == ra.RA_E_SHAPE
+    assert merge(l=T([1, 2, 64, 1], ra.RA_BF16, [128, 64, 1, 1])) == ra.RA_E_DTYPE
+    assert merge(oa=T([1, 64, 2, 128], ra.RA_F32, data=FAKE + 8)) == ra.RA_E_LAYOUT
+    assert merge(oa=T([1, 64, 2, 96], ra.RA_F32), ob=T([1, 64, 2, 96], ra.RA_F32)) == ra.RA_E_UNSUPPORTED
+    e0, e1 = T([1, 0, 2, 128], ra.RA_F32), T([1, 0, 2, 128], ra.RA_F32)
+    assert merge(oa=e0, ob=e1, m=rows(1, 2, 0), l=rows(1, 2, 0), mb=rows(1, 2, 0), lb=rows(1, 2, 0)) == ra.RA_OK
+
+
+def test_launches_beyond_the_work_item_limit_are_rejected():
+    """A grid is at most 2^32 - 1 work-items along x: the bf16 forward runs
+    512 threads per 256 query rows, the backward 256 per 128 rows, the state
+    kernels 256 per 32 rows (d = 128)."""
+    L = ra.lib()
+    heads = (1 << 23) + 1                        # one 256-row tile each: > 2^32 / 512 workgroups
+    q, k = T([1, 256, heads, 128]), T([1, 256, 1, 128])
+    assert share(q, k, k, 1, 0, o_out=T([1, 256, heads, 128])) == ra.RA_E_RANGE
+    assert "work-items" in ra.ra_last_error()
+    assert step(q, k, k, T([1, 256, heads, 128], ra.RA_F32), rows(1, heads, 256), rows(1, heads, 256)) == \
+        ra.RA_E_RANGE
+    # backward: 128-row tiles of 256 threads
+    hb = (1 << 24) + 1
+    qb, ob = T([1, 128, hb, 128]), T([1, 128, hb, 128])
+    g = T([1, 128, hb, 128], ra.RA_F32)
+    dk = T([1, 128, 1, 128], ra.RA_F32)
+    assert L.ra_rank_share_bwd(P(qb), P(k := T([1, 128, 1, 128])), P(k), P(ob), P(rows(1, hb, 128)), P(ob), 1, 0, 1,
+                               P(g), P(dk), P(dk), P(rows(1, hb, 128)), None) == ra.RA_E_RANGE
+    # state kernels: 32 rows of d = 128 per 256-thread workgroup
+    big = T([1, 1 << 20, 1 << 10, 128], ra.RA_F32)
+    st = rows(1, 1 << 10, 1 << 20)
+    assert L.ra_state_init(P(big), P(st), P(st), None) == ra.RA_E_RANGE
+    assert L.ra_finalize(P(big), P(st), None) == ra.RA_E_RANGE
+    assert L.ra_merge(P(big), P(st), P(st), P(big), P(st), P(st), None) == ra.RA_E_RANGE
+
+
 # ------------------------------------------------------------- host planner
 def test_ring_block_and_classes_match_golden_schedules():
     path = os.path.join(ROOT, "tests", "golden", "ring_schedules.txt")

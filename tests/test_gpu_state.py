@@ -1,0 +1,148 @@
+"""GPU parity of the state kernels (ra_state_init, ra_merge, ra_finalize)
+against the fp64 oracle.
+
+ra_merge folds a second partial state into the running state by log-sum-exp
+rescaling (glossary page "sequence parallelism transformers", section "Ring
+Attention", item "Computation"; section "Implementation Considerations", item
+"Numerical Stability").  Its arithmetic is fp32, so it is held to the fp32
+bar (1e-5) on states of order one, with empty sides (m = -inf) exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_transformer_attention_amd import inputs
+from sequence_transformer_attention_amd import ringattn as ra
+from tests.gpu_util import assert_close, gather, oracle_threads, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL_F32 = 1e-5
+
+
+def _state(B, S, H, d, seed, empty_frac=0.0, bhsd=False):
+    """A seeded partial state (o [B, S, H, d], m, l [B, H, S]) of order one;
+    a fraction of the rows empty (o = 0, m = -inf, l = 0).  bhsd: o stored
+    as a [B, H, S, d] buffer and passed as a permuted view, m and l with a
+    padded row stride."""
+    g = torch.Generator().manual_seed(seed)
+    o = torch.randn(B, S, H, d, generator=g)
+    m = 2.0 * torch.randn(B, H, S, generator=g)
+    l = 0.5 + 1.5 * torch.rand(B, H, S, generator=g)
+    if empty_frac > 0:
+        e = torch.rand(B, H, S, generator=g) < empty_frac
+        m[e] = -float("inf")
+        l[e] = 0.0
+        o.permute(0, 2, 1, 3)[e] = 0.0
+    if bhsd:
+        od = o.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+        md = torch.empty(B, H, S + 5, device=DEV)[:, :, :S]
+        ld = torch.empty(B, H, S + 5, device=DEV)[:, :, :S]
+        md.copy_(m)
+        ld.copy_(l)
+    else:
+        od, md, ld = o.to(DEV), m.to(DEV), l.to(DEV)
+    return (o, m, l), (od, md, ld)
+
+
+def _flat(o, m, l):
+    """(o [B, S, H, d], m, l [B, H, S]) -> oracle rows (m [n], l [n], o [n, d]), rows in (b, h, s) order."""
+    d = o.shape[-1]
+    return (m.reshape(-1).double().cpu().numpy(), l.reshape(-1).double().cpu().numpy(),
+            o.permute(0, 2, 1, 3).reshape(-1, d).double().cpu().numpy())
+
+
+@pytest.mark.parametrize("B,S,H,d,bhsd", [
+    (1, 100, 3, 128, False),    # ragged row blocks (32 rows per workgroup at d = 128)
+    (2, 33, 2, 64, False),      # d = 64 (64 rows per workgroup), B = 2
+    (1, 4096, 4, 128, True),    # strided views of both states
+    (1, 1, 1, 64, False),       # a single row
+])
+def test_merge_matches_the_oracle(B, S, H, d, bhsd):
+    say(f"ra_merge B{B} S{S} H{H} d{d} bhsd={bhsd}")
+    (oa, ma, la), (oad, mad, lad) = _state(B, S, H, d, seed=S + d, empty_frac=0.2, bhsd=bhsd)
+    (ob, mb, lb), (obd, mbd, lbd) = _state(B, S, H, d, seed=S + d + 1, empty_frac=0.2, bhsd=bhsd)
+    ra.ra_merge(oad, mad, lad, obd, mbd, lbd)
+    torch.cuda.synchronize()
+    m_ref, l_ref, o_ref = oracle.merge(_flat(oa, ma, la), _flat(ob, mb, lb))
+    mg, lg, og = _flat(oad, mad, lad)
+    both_empty = np.isneginf(m_ref)
+    say(f"  rows {len(m_ref)}, empty on both sides {int(both_empty.sum())}")
+    assert np.array_equal(mg, m_ref), "m is the larger of two fp32 values: exact"
+    assert np.all(lg[both_empty] == 0) and np.all(og[both_empty] == 0), "two empty sides stay empty"
+    el, eo = float(np.abs(lg - l_ref).max()), float(np.abs(og - o_ref).max())
+    say(f"  max|dl| {el:.2e}, max|do| {eo:.2e} (tol {TOL_F32})")
+    assert el <= TOL_F32 and eo <= TOL_F32
+    # the second operand is read only
+    _, _, ob2 = _flat(obd, mbd, lbd)
+    assert np.array_equal(ob2, _flat(ob, mb, lb)[2])
+
+
+def test_merge_with_the_empty_state_is_the_identity():
+    B, S, H, d = 1, 257, 2, 128
+    (oa, ma, la), (oad, mad, lad) = _state(B, S, H, d, seed=5)
+    e_o = torch.full((B, S, H, d), float("nan"), device=DEV)
+    e_m = torch.full((B, H, S), float("nan"), device=DEV)
+    e_l = torch.full((B, H, S), float("nan"), device=DEV)
+    ra.ra_state_init(e_o, e_m, e_l)
+    torch.cuda.synchronize()
+    assert torch.all(e_o == 0) and torch.all(e_m == -float("inf")) and torch.all(e_l == 0)
+    ra.ra_merge(oad, mad, lad, e_o, e_m, e_l)          # A <- merge(A, empty)
+    ra.ra_merge(e_o, e_m, e_l, oad, mad, lad)          # empty <- merge(empty, A)
+    torch.cuda.synchronize()
+    for o, m, l in ((oad, mad, lad), (e_o, e_m, e_l)):
+        assert torch.equal(m.cpu(), ma) and torch.equal(l.cpu(), la) and torch.equal(o.cpu(), oa)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_two_ring_halves_merged_equal_the_share(dt):
+    """The rank's blocks split between two running states (the first half of
+    the ring steps in one, the second half in the other), merged and
+    normalised: the share, within the dtype's tolerance."""
+    B, Hq, Hkv, d, N, P, r = 1, 4, 2, 128, 2048, 4, 3
+    nb = N // P
+    x = inputs.draw_qkv(B, nb, N, Hq, Hkv, d, seed=71, dtype=dt)
+    q, k, v = (x[t].to(DEV) for t in "qkv")
+    states = []
+    for half in (range(0, 2), range(2, 4)):
+        oacc = torch.empty((B, nb, Hq, d), device=DEV)
+        m = torch.empty((B, Hq, nb), device=DEV)
+        l = torch.empty_like(m)
+        ra.ra_state_init(oacc, m, l)
+        for s in half:
+            j = ra.ra_ring_block(P, r, s)
+            ra.ra_step(q, k[:, j * nb:(j + 1) * nb], v[:, j * nb:(j + 1) * nb], oacc, m, l, r * nb, j * nb, True)
+        states.append((oacc, m, l))
+    (oa, ma, la), (ob, mb, lb) = states
+    ra.ra_merge(oa, ma, la, ob, mb, lb)
+    O = torch.full((B, nb, Hq, d), float("nan"), device=DEV)
+    lse = torch.full((B, Hq, nb), float("nan"), device=DEV)
+    ra.ra_finalize(oa, la, m=ma, o_out=O, lse_out=lse)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(B, Hq, nb)
+    o_ref, l_ref = oracle.rank_share(x["q"], x["k"], x["v"], P, r, True, rows=rows, nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"{dt} two merged halves")
+
+
+@pytest.mark.parametrize("S,H,d,o_dtype,in_place", [
+    (100, 3, 128, torch.bfloat16, False),
+    (33, 2, 64, torch.float32, False),
+    (300, 2, 128, None, True),          # O written over o_acc
+])
+def test_finalize_matches_the_oracle(S, H, d, o_dtype, in_place):
+    say(f"ra_finalize S{S} H{H} d{d} out {o_dtype} in_place={in_place}")
+    (o, m, l), (od, md, ld) = _state(2, S, H, d, seed=S)
+    lse = torch.full((2, H, S), float("nan"), device=DEV)
+    if in_place:
+        ra.ra_finalize(od, ld, m=md, lse_out=lse)
+        out = od
+    else:
+        out = torch.full((2, S, H, d), float("nan"), dtype=o_dtype, device=DEV)
+        ra.ra_finalize(od, ld, m=md, o_out=out, lse_out=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.finalize(_flat(o, m, l))
+    rows = oracle.all_rows(2, H, S)
+    og, lg = gather(out, lse, rows)
+    assert_close(og, lg, o_ref, l_ref, "f32", "finalize", out_bf16=o_dtype == torch.bfloat16)

@@ -222,7 +222,9 @@ def test_empty_visible_set_is_merge_identity():
 
 # --------------------------------------------------------------- ring order
 def test_ring_order_matches_a_simulated_ring():
-    """Each GPU sends its block to GPU i+1 and receives from GPU i-1, P steps."""
+    """Glossary page "sequence parallelism transformers", section "Ring
+    Attention", item "Ring Communication": blocks travel one hop up the ring
+    per step, so after s steps rank r holds block (r - s) mod P."""
     for P in range(1, 10):
         held = list(range(P))                   # step 0: each rank holds its own block
         for s in range(P):

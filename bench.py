@@ -111,8 +111,9 @@ def cpu_baseline(w, x, O_gpu, lse_gpu, target_s: float):
     rt = torch.as_tensor(rows, dtype=torch.long, device=O_gpu.device)
     o = O_gpu[rt[:, 0], rt[:, 2], rt[:, 1]].double().cpu().numpy()
     lse = lse_gpu[rt[:, 0], rt[:, 1], rt[:, 2]].double().cpu().numpy()
-    # O is timed as bf16: allow the format's own rounding (half a bf16 ulp) on top of 1e-2
-    excess = float((np.abs(o - o_ref) - (1e-2 + np.abs(o_ref) * 2.0 ** -9)).max())
+    # O is timed as bf16: allow the format's own rounding (half a bf16 ulp,
+    # at most 2^-8 of the value rounded) on top of 1e-2
+    excess = float((np.abs(o - o_ref) - (1e-2 + (np.abs(o_ref) + 1e-2) * 2.0 ** -8)).max())
     parity = {"rows": n, "max_abs_dO": float(np.abs(o - o_ref).max()),
               "max_abs_dLSE": float(np.abs(lse - l_ref).max()), "tol_O": "1e-2 + bf16 output rounding",
               "tol_LSE": 1e-3, "pass": bool(excess <= 0 and np.abs(lse - l_ref).max() <= 1e-3)}

@@ -67,7 +67,7 @@ struct RaMergeArgs {
 
 // Threads per workgroup of the state kernels (init, merge, finalize), and
 // their workgroup count for a [B, S, H, d] state (d = 64 or 128).
-constexpr int RA_STATE_THREADS = 256;
+constexpr int RA_STATE_THREADS = 512;
 int64_t ra_state_workgroups(int64_t B, int64_t H, int64_t S, int64_t d);
 
 // Tile shape of the attention kernels (query rows per workgroup, keys per tile).

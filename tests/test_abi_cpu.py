@@ -296,7 +296,7 @@ def test_ra_merge_validation():
 def test_launches_beyond_the_work_item_limit_are_rejected():
     """A grid is at most 2^32 - 1 work-items along x: the bf16 forward runs
     512 threads per 256 query rows, the backward 256 per 128 rows, the state
-    kernels 256 per 32 rows (d = 128)."""
+    kernels 512 per 64 rows (d = 128)."""
     L = ra.lib()
     heads = (1 << 23) + 1                        # one 256-row tile each: > 2^32 / 512 workgroups
     q, k = T([1, 256, heads, 128]), T([1, 256, 1, 128])
@@ -311,7 +311,7 @@ def test_launches_beyond_the_work_item_limit_are_rejected():
     dk = T([1, 128, 1, 128], ra.RA_F32)
     assert L.ra_rank_share_bwd(P(qb), P(k := T([1, 128, 1, 128])), P(k), P(ob), P(rows(1, hb, 128)), P(ob), 1, 0, 1,
                                P(g), P(dk), P(dk), P(rows(1, hb, 128)), None) == ra.RA_E_RANGE
-    # state kernels: 32 rows of d = 128 per 256-thread workgroup
+    # state kernels: 64 rows of d = 128 per 512-thread workgroup
     big = T([1, 1 << 20, 1 << 10, 128], ra.RA_F32)
     st = rows(1, 1 << 10, 1 << 20)
     assert L.ra_state_init(P(big), P(st), P(st), None) == ra.RA_E_RANGE

@@ -224,6 +224,21 @@ int ra_rank_share_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v
                       const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
                       const ra_tensor *delta, const ra_opts *opts);
 
+/* ra_rank_share_bwd without the caller's `delta` workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  D_i = <dO_i, O_i> goes to a
+ * workspace the library holds in a static device array, one per device, of
+ * 2^20 fp32 rows (4 MiB, kept until the process ends): B * Hq * N/P above
+ * 2^20 is RA_E_RANGE.  The call allocates nothing.  Every call on one device
+ * uses that device's array, so calls that may overlap on one device (other
+ * streams, other host threads) race: order them.  Arguments, outputs and
+ * errors otherwise as ra_rank_share_bwd. */
+int ra_rank_share_bwd_noalloc(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                              const ra_tensor *o, const ra_tensor *lse, const ra_tensor *dout,
+                              int P, int rank, int causal,
+                              const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
+                              const ra_opts *opts);
+
 /* Backward of the load-balanced share (ra_rank_share_zigzag's forward):
  * the same computation as ra_rank_share_bwd with the rank's N/P local rows
  * being chunk `rank` (rows [0, N/(2P))) and chunk 2P-1-rank (the rest) of

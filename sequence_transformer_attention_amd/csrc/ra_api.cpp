@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <limits>
+#include <mutex>
 
 #include "ra_bwd.h"
 #include "ra_launch.h"
@@ -162,6 +163,40 @@ int check_out(const ra_tensor* o, const ra_tensor* like, const char* name) {
   int e = check_bshd(o, name);
   if (e) return e;
   if (!same_shape(o, like)) return fail(RA_E_SHAPE, "%s must have the shape of %s", name, "the queries");
+  return RA_OK;
+}
+
+// ---- the allocation-free backward's workspace
+//
+// ra_rank_share_bwd_noalloc keeps D_i = <dO_i, O_i> (the `delta` workspace of
+// ra_rank_share_bwd) in this array instead of a caller buffer.  In host code
+// the name is a host-side stand-in, never a device address: each device holds
+// its own copy, whose address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept in g_scratch_ptr.
+// The prep kernel writes every entry a call reads, so nothing needs clearing;
+// calls that overlap on one device share the array and race.
+constexpr int64_t kNoallocMaxRows = int64_t(1) << 20;  // 4 MiB of fp32 per device
+static __device__ __align__(256) float scratch[kNoallocMaxRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use).
+int scratch_of_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RA_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_E_RANGE, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RA_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
   return RA_OK;
 }
 
@@ -355,8 +390,10 @@ int ra_rank_share_zigzag(const ra_tensor* q, const ra_tensor* k, const ra_tensor
 static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
                           const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
                           const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta,
-                          const ra_opts* opts, int zigzag, int64_t n_valid) {
-  const char* fn = zigzag ? "ra_rank_share_zigzag_bwd" : (n_valid >= 0 ? "ra_rank_share_padded_bwd" : "ra_rank_share_bwd");
+                          const ra_opts* opts, int zigzag, int64_t n_valid, bool noalloc = false) {
+  const char* fn = noalloc ? "ra_rank_share_bwd_noalloc"
+                           : (zigzag ? "ra_rank_share_zigzag_bwd"
+                                     : (n_valid >= 0 ? "ra_rank_share_padded_bwd" : "ra_rank_share_bwd"));
   int e = check_qkv(q, k, v, "k", "v");
   if (e) return e;
   if (q->dtype != RA_BF16) return fail(RA_E_UNSUPPORTED, "%s takes bf16 q, k, v", fn);
@@ -381,13 +418,22 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   if ((e = check_bshd(dk, "dk")) || (e = check_bshd(dv, "dv"))) return e;
   if (!same_shape(dk, k) || !same_shape(dv, k)) return fail(RA_E_SHAPE, "dk and dv must have the shape of k");
   if (dk->dtype != RA_F32 || dv->dtype != RA_F32) return fail(RA_E_DTYPE, "dk and dv must be fp32");
-  if ((e = check_rows(lse, "lse", B, hq, nq)) || (e = check_rows(delta, "delta", B, hq, nq))) return e;
+  if ((e = check_rows(lse, "lse", B, hq, nq))) return e;
+  if (noalloc) {
+    if (B * hq * nq > kNoallocMaxRows)
+      return fail(RA_E_RANGE, "%s: B * Hq * Nq = %lld query rows exceed its workspace of %lld rows", fn,
+                  (long long)(B * hq * nq), (long long)kNoallocMaxRows);
+  } else if ((e = check_rows(delta, "delta", B, hq, nq))) {
+    return e;
+  }
   const int64_t qrows = zigzag ? 2 * ((N / parts + RA_BWD_BM - 1) / RA_BWD_BM) * RA_BWD_BM : nq;
   if ((e = check_grid(qrows, RA_BWD_BM, hq, B, RA_BWD_THREADS)) ||
       (e = check_grid(N, RA_BWD_BM, k->shape[2], B, RA_BWD_THREADS)) ||
       (e = check_grid(nq, RA_BWD_THREADS, hq, B, RA_BWD_THREADS)))  // prep: one thread per query row
     return e;
   if (B == 0 || nq == 0) return ok();
+  float* ws = nullptr;
+  if (noalloc && (e = scratch_of_current_device(&ws))) return e;
 
   RaBwdArgs a{};
   a.q = q->data; set_bshd(q, a.q_sb, a.q_ss, a.q_sh);
@@ -396,7 +442,11 @@ static int rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tenso
   a.o = o->data; set_bshd(o, a.o_sb, a.o_ss, a.o_sh);
   a.dout = dout->data; set_bshd(dout, a.do_sb, a.do_ss, a.do_sh);
   a.lse = (const float*)lse->data; set_rows(lse, a.lse_sb, a.lse_sh, a.lse_ss);
-  a.delta = (float*)delta->data; set_rows(delta, a.de_sb, a.de_sh, a.de_ss);
+  if (noalloc) {  // [B, Hq, Nq], contiguous
+    a.delta = ws; a.de_sb = hq * nq; a.de_sh = nq; a.de_ss = 1;
+  } else {
+    a.delta = (float*)delta->data; set_rows(delta, a.de_sb, a.de_sh, a.de_ss);
+  }
   a.dq = (float*)dq->data; set_bshd(dq, a.dq_sb, a.dq_ss, a.dq_sh);
   a.dk = (float*)dk->data; set_bshd(dk, a.dk_sb, a.dk_ss, a.dk_sh);
   a.dv = (float*)dv->data; set_bshd(dv, a.dv_sb, a.dv_ss, a.dv_sh);
@@ -419,6 +469,12 @@ int ra_rank_share_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
                       const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal, const ra_tensor* dq,
                       const ra_tensor* dk, const ra_tensor* dv, const ra_tensor* delta, const ra_opts* opts) {
   return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, delta, opts, 0, -1);
+}
+
+int ra_rank_share_bwd_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,
+                              const ra_tensor* lse, const ra_tensor* dout, int P, int rank, int causal,
+                              const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv, const ra_opts* opts) {
+  return rank_share_bwd(q, k, v, o, lse, dout, P, rank, causal, dq, dk, dv, nullptr, opts, 0, -1, true);
 }
 
 int ra_rank_share_padded_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* o,

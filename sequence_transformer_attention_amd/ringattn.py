@@ -71,10 +71,11 @@ def lib() -> ctypes.CDLL:
     L.ra_rank_share_padded.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, O]
     L.ra_rank_share_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, T, T, T, O]
     L.ra_rank_share_zigzag_bwd.argtypes = L.ra_rank_share_bwd.argtypes
+    L.ra_rank_share_bwd_noalloc.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, T, T, O]
     L.ra_rank_share_padded_bwd.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64,
                                            T, T, T, T, O]
     for f in (L.ra_state_init, L.ra_step, L.ra_finalize, L.ra_merge, L.ra_rank_share, L.ra_rank_share_zigzag,
-              L.ra_rank_share_bwd, L.ra_rank_share_padded, L.ra_rank_share_zigzag_bwd,
+              L.ra_rank_share_bwd, L.ra_rank_share_bwd_noalloc, L.ra_rank_share_padded, L.ra_rank_share_zigzag_bwd,
               L.ra_rank_share_padded_bwd):
         f.restype = ctypes.c_int
     L.ra_ring_block.argtypes = [i64, i64, i64]
@@ -216,6 +217,17 @@ def ra_rank_share_bwd(q, k, v, o, lse, dout, P: int, rank: int, causal: bool, dq
     _check(lib().ra_rank_share_bwd(_desc(q), _desc(k), _desc(v), _desc(o), _desc(lse, True), _desc(dout),
                                    int(P), int(rank), int(bool(causal)), _desc(dq), _desc(dk), _desc(dv),
                                    _desc(delta, True), ctypes.byref(opts)))
+
+
+def ra_rank_share_bwd_noalloc(q, k, v, o, lse, dout, P: int, rank: int, causal: bool, dq, dk, dv,
+                              scale: Optional[float] = None, stream=None) -> None:
+    """ra_rank_share_bwd with the D workspace held by the library (a static
+    device array of 2^20 rows per device): the call allocates nothing;
+    calls overlapping on one device race."""
+    opts, keep = _opts(stream, scale)
+    _check(lib().ra_rank_share_bwd_noalloc(_desc(q), _desc(k), _desc(v), _desc(o), _desc(lse, True), _desc(dout),
+                                           int(P), int(rank), int(bool(causal)), _desc(dq), _desc(dk), _desc(dv),
+                                           ctypes.byref(opts)))
 
 
 def ra_rank_share_zigzag_bwd(q, k, v, o, lse, dout, P: int, rank: int, causal: bool, dq, dk, dv, delta,

@@ -398,3 +398,24 @@ def test_tile_shape():
     assert ra.ra_tile_shape(torch.float32, 64) == (64, 64)
     with pytest.raises(ra.RaError):
         ra.ra_tile_shape(torch.bfloat16, 96)
+
+
+def test_ra_rank_share_bwd_noalloc_validation():
+    """The allocation-free backward validates like ra_rank_share_bwd (without
+    a workspace argument) and refuses more query rows than its 2^20-row
+    workspace before any HIP call."""
+    L = ra.lib()
+    q, k = T([1, 512, 4, 128]), T([1, 4096, 1, 128])
+    g, gk = T([1, 512, 4, 128], ra.RA_F32), T([1, 4096, 1, 128], ra.RA_F32)
+
+    def call(q=q, k=k, o=q, lse=rows(1, 4, 512), dout=q, P_=8, rank=7, dq=g, dk=gk, dv=gk):
+        return L.ra_rank_share_bwd_noalloc(P(q), P(k), P(k), P(o), P(lse), P(dout), P_, rank, 1, P(dq), P(dk),
+                                           P(dv), None)
+
+    assert call(q=None) == ra.RA_E_NULL
+    assert call(rank=8) == ra.RA_E_RANGE
+    assert call(lse=rows(1, 4, 511)) == ra.RA_E_SHAPE
+    assert call(dq=T([1, 512, 4, 128])) == ra.RA_E_DTYPE
+    big_q, big_g = T([1, 512, 2049, 128]), T([1, 512, 2049, 128], ra.RA_F32)   # 2^20 + 512 rows
+    assert call(q=big_q, o=big_q, dout=big_q, dq=big_g, lse=rows(1, 2049, 512)) == ra.RA_E_RANGE
+    assert "workspace" in ra.ra_last_error()

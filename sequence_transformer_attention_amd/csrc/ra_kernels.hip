@@ -8,10 +8,14 @@
 // per query row; section "Flash Attention with Sequence Parallelism", item
 // "Tiled Computation" -- each block is processed in tiles that stay on chip.
 //
-// bf16 path (attn_bf16_kernel): one workgroup = 8 waves = 256 query rows of
-// one head; each wave owns 32 query rows; the two waves that share a SIMD
-// (w and w + 4) feed its matrix core and vector ALU from two instruction
-// streams.  Keys come in tiles of 64, processed as two 32-key units:
+// bf16 path.  Two forms of the same pipeline; the library launches the
+// second (attn_bf16_w64_kernel, 64 query rows per wave, one wave per SIMD,
+// described where it is defined), which reads half as much from LDS per
+// MFMA.  The first (attn_bf16_kernel) is described here: one workgroup = 8
+// waves = 256 query rows of one head; each wave owns 32 query rows; the two
+// waves that share a SIMD (w and w + 4) feed its matrix core and vector ALU
+// from two instruction streams.  Keys come in tiles of 64, processed as two
+// 32-key units:
 //   S^T (keys x queries) = K Q^T   v_mfma_f32_32x32x16_bf16; K from LDS is the
 //                                  A operand, the Q fragment stays in VGPRs
 //                                  for the whole kernel as the B operand
@@ -697,6 +701,610 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(RaAttnArgs a) {
   }
 }
 
+// bf16 path with 64 query rows per wave (attn_bf16_w64_kernel): one
+// workgroup = 4 waves = 256 query rows, one wave per SIMD.  Every K and V^T
+// fragment a wave reads from LDS feeds the MFMAs of two 32-row blocks (rb =
+// 0, 1), so a key tile costs half the LDS reads and half the tile
+// bookkeeping per MFMA of the 32-rows-per-wave form above.  The price is the
+// register file: the output accumulators of both row blocks (2 x D/32 x 16
+// fp32) live in AGPRs, pinned there by the P V products being inline-asm
+// MFMAs, and a SIMD's matrix core is fed by one instruction stream, so each
+// pipeline step alternates single MFMAs with short runs of the softmax's
+// vector work (16 slots of two MFMAs per 32-key unit).  Everything else --
+// tile walk, direct loads, swizzle, lazy softmax with exact redo, epilogue --
+// is the form above, per row block.
+
+// The MFMAs of attn_bf16_w64_kernel, inline asm so that the operands sit in
+// the register file the kernel needs them in (the builtins leave that to the
+// compiler, which then runs out of VGPRs and copies between the files).
+// The compiler does not see the wait states around inline-asm MFMAs (gfx950,
+// as the compiler itself spaces its own MFMAs: 2 after a vector write of an
+// operand, none between dependent products, 12 before a vector read of a
+// result):
+//   - after a vector write of an operand: the P V product's leading s_nop 1
+//     (its A operand may have just been assembled by vector moves, its C may
+//     have just been rescaled); the S^T product's operands come from LDS
+//     reads (waited for) and from the Q fragments, written once before the
+//     first product, which has its own s_nop;
+//   - before a vector read of a result: the kernel's drains (16 wait
+//     states), and otherwise whole pipeline slots between the write and the
+//     read.
+// S^T (keys x queries) = K Q^T, k-step 0 (C = 0) and later k-steps; the
+// accumulator in VGPRs, the Q fragment (B) in AGPRs.
+__device__ __forceinline__ void mfma_s_first(f32x16& c, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_s_next(f32x16& c, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(k), "a"(q));
+}
+// O^T += V^T P^T with the accumulator pinned to AGPRs.
+__device__ __forceinline__ void mfma_pv(f32x16& c, const bf16x8& A, const bf16x8& B) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(A), "v"(B));
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
+  constexpr int NW = 4, RB = 2, BM = NW * 32 * RB, BN = RA_BF16_BN;
+  constexpr int SLOTS = D / 8;                 // 16-byte slots per row
+  constexpr int TILE_BYTES = BN * D * 2;       // one K or V tile
+  constexpr int NL = TILE_BYTES / 1024 / NW;   // 1 KiB direct loads per wave per tile
+  constexpr int KC = D / 16;                   // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;                   // 32-channel blocks of O^T
+  static_assert(NL * 1024 * NW == TILE_BYTES, "tile split");
+  static_assert(BM == RA_BF16_BM && BN == 64, "64-key tiles, processed as two 32-key units");
+  // [0] .. [3]: K stages; [4] .. [7]: V stages (tile c_t in K and V stage t % 4)
+  __shared__ __attribute__((aligned(1024))) char smem[8][TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep per-wave values in SGPRs
+  const int lr = lane & 31, lg = lane >> 5;
+
+  // query tiles: nqt_c per chunk of nqc rows (one chunk unless the share is split)
+  const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
+  const int nqt_c = (nqc + BM - 1) / BM;
+  const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
+  int hb, qt;  // later query tiles see more keys under causal masking: they start first
+  ra_plan_head_tile(ra_plan_xcd_remap(blockIdx.x, gridDim.x, nqt), gridDim.x, nqt, a.causal, &hb, &qt);
+  const int h = hb % a.Hq, b = hb / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int chunk = qt / nqt_c;
+  const int64_t qpos0 = chunk ? a.q_off2 : a.q_off;  // global position of the chunk's first row
+  const int rank_e = chunk ? a.rank2 : a.rank;        // its ring order
+
+  const int qrow_wg = (qt - chunk * nqt_c) * BM;      // rows within the chunk
+  const int qrow_w = qrow_wg + wave * 32 * RB;        // the wave's first row
+  int my_q[RB];                                       // local rows (q, o, lse, state) of the lane
+  bool q_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    my_q[rb] = chunk * nqc + qrow_w + 32 * rb + lr;
+    q_ok[rb] = qrow_w + 32 * rb + lr < nqc;
+  }
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[my_q[rb]][16c + 8lg .. +7].
+  bf16x8 qf[RB][KC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)(q_ok[rb] ? my_q[rb] : 0) * a.q_ss +
+                       (int64_t)h * a.q_sh + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (q_ok[rb]) w = *(const u32x4*)(qp + 16 * c);
+      qf[rb][c] = __builtin_bit_cast(bf16x8, w);
+      asm volatile("" : "+a"(qf[rb][c]));  // from here on the fragment lives in AGPRs
+    }
+  }
+
+  // Running state per row block.  o[rb][db][r] = O^T[32db + 8(r/4) + 4lg +
+  // r%4][my_q[rb]] (unnormalised, in AGPRs); m2 = running max of s * c (log2
+  // units); lsum = this lane's half of the row sum.
+  f32x16 o[RB][DB];
+  float m2[RB], lsum[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m2[rb] = -INFINITY;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x16{};
+    if (a.state_in && q_ok[rb]) {
+      const float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q[rb] * a.oa_ss + (int64_t)h * a.oa_sh;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 x = *(const f32x4*)(op + 32 * db + 8 * j + 4 * lg);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[rb][db][4 * j + i] = x[i];
+        }
+      const float mv = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q[rb] * a.m_ss];
+      const float lv = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q[rb] * a.l_ss];
+      m2[rb] = mv * kLog2e;  // -inf stays -inf
+      lsum[rb] = lg == 0 ? lv : 0.f;
+    }
+  }
+  // The accumulators are read by vector code (a redo, the epilogue) only
+  // after this: 16 wait states after the last MFMA that wrote them.
+  auto ofrag_drain = [&o]() __attribute__((always_inline)) {
+    if constexpr (DB == 4)
+      asm volatile("s_nop 7\n\ts_nop 7"
+                   : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]), "+a"(o[1][1]),
+                     "+a"(o[1][2]), "+a"(o[1][3]));
+    else
+      asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+  };
+
+  const int64_t q0_wg = qpos0 + qrow_wg;
+  const int nq_wg = min(BM, nqc - qrow_wg);
+  const int nsteps = a.ring ? a.P : 1;
+  // Block order as in attn_bf16_kernel: ring order with the rank's own block
+  // (ring step 0) folded last.
+  auto step_kv_off = [&](int s) -> int64_t {
+    return a.ring ? (int64_t)ra_plan_ring_block32(a.P, rank_e, (s + 1) % a.P) * a.nkv : a.kv_off;
+  };
+  auto step_keys = [&](int s) -> int64_t {
+    const int64_t n = a.kv_end - step_kv_off(s);
+    return n < 0 ? 0 : (n < a.nkv ? n : a.nkv);
+  };
+  auto step_tiles = [&](int s) -> int {
+    return (int)ra_plan_key_tiles(q0_wg, nq_wg, step_kv_off(s), step_keys(s), a.causal, BN);
+  };
+
+  // Direct loads, as in attn_bf16_kernel, with the tile split over 4 waves.
+  const char* kbase = (const char*)a.k + 2 * ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
+  const char* vbase = (const char*)a.v + 2 * ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto gslot = [&](int i, int& r) -> unsigned {
+    const int ls = (wv * NL + i) * 64 + lane;
+    r = ls / SLOTS;
+    return 16u * (unsigned)swz<SLOTS>(r, ls % SLOTS);
+  };
+  unsigned koffg[NL], voffg[NL];  // row strides of k and v: at most 2^24 elements
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    int r;
+    const unsigned sl = gslot(i, r);
+    koffg[i] = (unsigned)r * (unsigned)a.k_ss * 2u + sl;
+    voffg[i] = (unsigned)r * (unsigned)a.v_ss * 2u + sl;
+  }
+  const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
+  auto issue = [&](const char* tb, int64_t stride, const unsigned* goff, int nvalid, auto STAGE)
+      __attribute__((always_inline)) {
+    const int nrec = (nvalid - 1) * (int)stride * 2 + 2 * D;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, nrec, 0x00020000);
+    unsigned lb = smem_lds + (unsigned)wv * NL * 1024;
+    asm volatile("" : "+s"(lb));
+    char* dst = (char*)&smem[0][0] + (lb - smem_lds) + decltype(STAGE)::value * TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, goff[i], 0, 0, 0);
+  };
+
+  unsigned kaddr[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) kaddr[c] = smem_lds + lr * 2 * D + 16 * swz<SLOTS>(lr, 2 * c + lg);
+  const int vj = lane & 15, ve = vj >> 2, vc = vj & 3, vgrp = lane >> 4;
+  const int vx = 2 * (vgrp & 1) + (vc >> 1);
+  unsigned voff[2][DB];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int r = 4 * lg + ve + 8 * half;
+      voff[half][db] = smem_lds + 4 * TILE_BYTES + r * 2 * D + 16 * swz<SLOTS>(r, 4 * db + vx) + 8 * (vc & 1);
+    }
+
+  int n = 0;
+  for (int s = 0; s < nsteps; ++s) n += step_tiles(s);
+
+  if (n > 0) {  // workgroup-uniform
+    const int64_t roff = a.ring ? 0 : a.kv_off;
+    const int64_t q0w = qpos0 + qrow_w;          // the wave's first query position
+    const int64_t kstep = (int64_t)BN * a.k_ss * 2, vstep = (int64_t)BN * a.v_ss * 2;
+    constexpr int kRelSat = 1 << 30;
+    int cs = 0, cu = 0, cnt = 0, crel = 0, cleft = 0;
+    const char* cka = kbase;
+    const char* cva = vbase;
+    auto cur_set = [&]() {
+      cu = 0;
+      cnt = step_tiles(cs);
+      const int64_t kv = step_kv_off(cs), rel = kv - q0w;
+      crel = rel < -kRelSat ? -kRelSat : (rel > kRelSat ? kRelSat : (int)rel);
+      cleft = (int)step_keys(cs);
+      cka = kbase + (kv - roff) * a.k_ss * 2;
+      cva = vbase + (kv - roff) * a.v_ss * 2;
+    };
+    while (step_tiles(cs) == 0) ++cs;
+    cur_set();
+    int rem = n;
+    int drel[4], dv[4];  // dv: valid rows, + 128 if the tile needs a mask for some row of the wave
+    const char* dka[4];
+    const char* dva[4];
+    auto fill = [&](auto SLOT) __attribute__((always_inline)) {
+      constexpr int j = decltype(SLOT)::value;
+      if (rem > 0) {
+        drel[j] = crel;
+        const int nv = cleft < BN ? cleft : BN;
+        dv[j] = nv + (ra_plan_tile_masked<int>(crel, nv, BN, a.causal) ? 128 : 0);
+        dka[j] = cka;
+        dva[j] = cva;
+        if (--rem > 0) {
+          if (++cu < cnt) {
+            crel += BN;
+            cleft -= BN;
+            cka += kstep;
+            cva += vstep;
+          } else {
+            do {
+              ++cs;
+            } while (cs < nsteps && step_tiles(cs) == 0);
+            if (cs < nsteps) cur_set();
+          }
+        }
+      }
+    };
+    auto load_k = [&](auto ST) __attribute__((always_inline)) {
+      constexpr int j = decltype(ST)::value;
+      issue(dka[j], a.k_ss, koffg, dv[j] & 127, ST);
+    };
+    auto load_v = [&](auto ST) __attribute__((always_inline)) {
+      constexpr int j = decltype(ST)::value;
+      issue(dva[j], a.v_ss, voffg, dv[j] & 127, std::integral_constant<int, 4 + j>{});
+    };
+
+    f32x16 sacc[2][RB];       // S^T of units with even / odd index, per row block
+    bf16x8 pf[2][RB][2];      // P^T of units with even / odd index, per row block and 16-key group
+    bf16x8 kf[KC];            // K fragments of the next S^T
+    u32x2 vlo[2][DB], vhi[2][DB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        sacc[i][rb] = f32x16{};
+        pf[i][rb][0] = pf[i][rb][1] = bf16x8{};
+      }
+
+    auto kread = [&kf, &kaddr](auto KO) __attribute__((always_inline)) {
+      constexpr unsigned ko = decltype(KO)::value;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[c]) : "v"(kaddr[c]), "i"(ko));
+    };
+    auto kwait0 = [&kf]() __attribute__((always_inline)) {
+      if constexpr (KC == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]), "+v"(kf[4]),
+                     "+v"(kf[5]), "+v"(kf[6]), "+v"(kf[7]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]));
+    };
+    auto vread = [&vlo, &vhi, &voff](auto HH, auto VO, unsigned rt) __attribute__((always_inline)) {
+      constexpr int hh = decltype(HH)::value;
+      constexpr unsigned vo = decltype(VO)::value + (unsigned)hh * 32 * D;
+#pragma unroll
+      for (int x = 0; x < DB; ++x) {
+        const unsigned a0 = voff[0][x] + rt, a1 = voff[1][x] + rt;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vlo[hh][x]) : "v"(a0), "i"(vo));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vhi[hh][x]) : "v"(a1), "i"(vo));
+      }
+    };
+    auto vwait0 = [&vlo, &vhi]() __attribute__((always_inline)) {
+      if constexpr (D == 128)
+        asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(vlo[0][0]), "+v"(vhi[0][0]), "+v"(vlo[0][1]), "+v"(vhi[0][1]),
+                     "+v"(vlo[0][2]), "+v"(vhi[0][2]), "+v"(vlo[0][3]), "+v"(vhi[0][3]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(vlo[0][0]), "+v"(vhi[0][0]), "+v"(vlo[0][1]), "+v"(vhi[0][1]));
+    };
+    auto vwait1 = [&vlo, &vhi](auto KN) __attribute__((always_inline)) {
+      constexpr int pend = decltype(KN)::value ? KC : 0;  // K reads issued after group 1
+      if constexpr (D == 128)
+        asm volatile("s_waitcnt lgkmcnt(%8)" : "+v"(vlo[1][0]), "+v"(vhi[1][0]), "+v"(vlo[1][1]), "+v"(vhi[1][1]),
+                     "+v"(vlo[1][2]), "+v"(vhi[1][2]), "+v"(vlo[1][3]), "+v"(vhi[1][3]) : "n"(pend));
+      else
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(vlo[1][0]), "+v"(vhi[1][0]), "+v"(vlo[1][1]), "+v"(vhi[1][1])
+                     : "n"(pend));
+    };
+
+    // Mask of row block rb's unit (as attn_bf16_kernel's sm_mask, for the
+    // wave's rows 32 rb ..).
+    auto sm_mask = [&](int x, int rb, int64_t k0, int nvalid) __attribute__((always_inline)) {
+      const int64_t q0r = q0w + 32 * rb;
+      if (__builtin_expect(ra_plan_tile_masked<int64_t>(k0 - q0r, nvalid, 32, a.causal), 0)) {
+        const int lim = (int)ra_plan_visible_prefix(q0r + lr, k0, nvalid, a.causal) - 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[x][rb][r] = (8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : sacc[x][rb][r];
+      }
+    };
+    // Softmax sub-step j of a step (row block j % 2, keys 2k, 2k+1 of the
+    // lane's 16 with k = j / 2), software-pipelined over the slots: the
+    // exponent arguments of sub-step j are formed in the slot before, so a
+    // slot runs the two exponentials (sm_a) under one MFMA and the sums, the
+    // bf16 P and the next sub-step's arguments (sm_b) under the other.
+    float sm_ps[RB][4], sm_tot[RB] = {0.f, 0.f}, sm_p[RB][2], sm_arg[2];
+    auto sm_args = [&](auto X, auto J) __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value, j = decltype(J)::value, rb = j % 2, k = j / 2;
+      const f32x16& s = sacc[x][rb];
+      sm_arg[0] = fmaf(s[2 * k], a.c, -m2[rb]);
+      sm_arg[1] = fmaf(s[2 * k + 1], a.c, -m2[rb]);
+      asm volatile("" : "+v"(sm_arg[0]), "+v"(sm_arg[1]));
+    };
+    auto sm_a = [&](auto X, auto R, auto K) __attribute__((always_inline)) {
+      constexpr int rb = decltype(R)::value;
+      sm_p[rb][0] = fast_exp2(sm_arg[0]);
+      sm_p[rb][1] = fast_exp2(sm_arg[1]);
+      asm volatile("" : "+v"(sm_p[rb][0]), "+v"(sm_p[rb][1]));
+    };
+    auto sm_b = [&](auto X, auto R, auto K) __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value, rb = decltype(R)::value, k = decltype(K)::value;
+      if constexpr (2 * k + rb + 1 < 16) sm_args(X, std::integral_constant<int, 2 * k + rb + 1>{});
+      const float p0 = sm_p[rb][0], p1 = sm_p[rb][1];
+      if constexpr (k < 4) sm_ps[rb][k] = p0 + p1;
+      else sm_ps[rb][k - 4] += p0 + p1;
+      pf[x][rb][k >> 2][2 * (k & 3)] = (__bf16)p0;
+      pf[x][rb][k >> 2][2 * (k & 3) + 1] = (__bf16)p1;
+      asm volatile("" : "+v"(sm_ps[rb][k & 3]), "+v"(pf[x][rb][k >> 2]));
+      if constexpr (k == 7) {
+        sm_tot[rb] = (sm_ps[rb][0] + sm_ps[rb][1]) + (sm_ps[rb][2] + sm_ps[rb][3]);
+        asm volatile("" : "+v"(sm_tot[rb]));
+      }
+    };
+    // After the step: redo a row block's unit if any lane asks for it (as
+    // attn_bf16_kernel's sm_fix), then add its row sum.
+    auto sm_fix = [&](auto X, auto R) __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value, rb = decltype(R)::value;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(sm_tot[rb] <= kRedoSum)) != 0, 0)) {
+        const f32x16& s = sacc[x][rb];
+        float mx = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax3(s[6], s[7], s[8]));
+        mx = vmax3(mx, vmax3(s[9], s[10], s[11]), vmax3(s[12], s[13], s[14]));
+        mx = vmax3(mx, s[15], s[15]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float tm = vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1])) * a.c;
+        const bool up = tm > m2[rb];
+        const float alpha = up ? fast_exp2(m2[rb] - tm) : 1.f;
+        m2[rb] = up ? tm : m2[rb];
+        const float muse = m2[rb] == -INFINITY ? 0.f : m2[rb];
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float p0 = fast_exp2(fmaf(s[2 * k], a.c, -muse));
+          const float p1 = fast_exp2(fmaf(s[2 * k + 1], a.c, -muse));
+          tot += p0 + p1;
+          pf[x][rb][k >> 2][2 * (k & 3)] = (__bf16)p0;
+          pf[x][rb][k >> 2][2 * (k & 3) + 1] = (__bf16)p1;
+          asm volatile("" : "+v"(pf[x][rb][k >> 2]), "+v"(tot));
+        }
+        sm_tot[rb] = tot;
+        lsum[rb] *= alpha;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+          ofrag_drain();
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
+        }
+      }
+      lsum[rb] += sm_tot[rb];
+    };
+
+    // MFMAs of a step.  S^T(u+1) of row block rb, k-step c, into sacc[XN][rb];
+    // O^T += V^T P^T(u-1) of row block rb for 16-key group hh and channel
+    // block db, P from pf[XP][rb].
+    auto mma_s = [&](auto XN, auto R, auto C) __attribute__((always_inline)) {
+      constexpr int xn = decltype(XN)::value, rb = decltype(R)::value, c = decltype(C)::value;
+      if constexpr (c == 0)
+        mfma_s_first(sacc[xn][rb], kf[0], qf[rb][0]);
+      else
+        mfma_s_next(sacc[xn][rb], kf[c], qf[rb][c]);
+    };
+    auto mma_pv = [&](auto XP, auto R, auto M) __attribute__((always_inline)) {
+      constexpr int xp = decltype(XP)::value, rb = decltype(R)::value, m = decltype(M)::value;
+      constexpr int hh = m / DB, db = m % DB;
+      const u32x4 w = {vlo[hh][db][0], vlo[hh][db][1], vhi[hh][db][0], vhi[hh][db][1]};
+      mfma_pv(o[rb][db], __builtin_bit_cast(bf16x8, w), pf[xp][rb][hh]);
+    };
+    // Pipeline step for unit u (S^T(u) in sacc[X], P(u-1) in pf[1-X]), 16
+    // slots.  Slots 0 .. KC-1 (two slots per k-step when D = 64): the S^T(u+1)
+    // chains of both row blocks; the remaining slots: O^T += V^T P^T(u-1),
+    // one MFMA per row block.  Each slot is MFMA, first half of a softmax
+    // sub-step, MFMA, second half, in that order (scheduling barriers), so
+    // the vector work issues while the matrix core runs.  The sixteen
+    // softmax sub-steps (8 per row block) take one slot each.
+    auto step = [&](auto X, auto SN, auto PV, auto SM, auto KN, auto VO, unsigned vrt, auto KO, auto load)
+        __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value;
+      constexpr bool sn = decltype(SN)::value, pv = decltype(PV)::value, sm = decltype(SM)::value;
+      constexpr bool kn = decltype(KN)::value;
+      constexpr int NS = 16;                  // slots
+      constexpr int SSLOTS = 2 * KC;          // MFMAs of S^T(u+1), 2 per slot
+      constexpr int SS = SSLOTS / 2;          // slots holding them
+      static_assert(SS + RB * 2 * DB / 2 == NS || D == 64, "16 slots at D = 128");
+      if constexpr (sm) sm_args(X, std::integral_constant<int, 0>{});
+      static_for<0, NS>([&](auto SL) {
+        constexpr int sl = decltype(SL)::value;
+        // slot sl's two MFMAs: index j = 2 sl, 2 sl + 1 of the step's list
+        // (S^T(u+1): j < SSLOTS, rb = j % 2, k-step j / 2; then P V: the
+        // rest, rb = j % 2, m = (j - SSLOTS) / 2)
+        auto mfma_j = [&](auto J) __attribute__((always_inline)) {
+          constexpr int j = decltype(J)::value;
+          if constexpr (j < SSLOTS) {
+            if constexpr (sn) mma_s(std::integral_constant<int, 1 - x>{}, std::integral_constant<int, j % 2>{},
+                                    std::integral_constant<int, j / 2>{});
+          } else if constexpr (j - SSLOTS < RB * 2 * DB) {
+            if constexpr (pv) mma_pv(std::integral_constant<int, 1 - x>{}, std::integral_constant<int, j % 2>{},
+                                     std::integral_constant<int, (j - SSLOTS) / 2>{});
+          }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (sl == 0) {
+          if constexpr (sn) kwait0();
+          if constexpr (pv) vread(std::integral_constant<int, 0>{}, VO, vrt);
+        }
+        if constexpr (sl == 1 && pv) vread(std::integral_constant<int, 1>{}, VO, vrt);
+        if constexpr (sl == SS) {
+          if constexpr (pv) vwait0();
+          if constexpr (kn) kread(KO);
+        }
+        if constexpr (sl == SS + DB && pv) vwait1(KN);  // the K reads for the next step (if any) are younger
+        if constexpr (sl == 4) load();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_j(std::integral_constant<int, 2 * sl>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (sm) sm_a(X, std::integral_constant<int, sl % 2>{}, std::integral_constant<int, sl / 2>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_j(std::integral_constant<int, 2 * sl + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (sm) sm_b(X, std::integral_constant<int, sl % 2>{}, std::integral_constant<int, sl / 2>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (sm) {
+        sm_fix(X, std::integral_constant<int, 0>{});
+        sm_fix(X, std::integral_constant<int, 1>{});
+      }
+    };
+    auto half_valid = [](int nv, int hf) { return ra_plan_half_valid(nv, hf, 32); };
+    const std::true_type T;
+    const std::false_type F;
+    auto uoff = [](auto S, auto H) {
+      return std::integral_constant<unsigned, (unsigned)decltype(S)::value * TILE_BYTES +
+                                                  (unsigned)decltype(H)::value * 64 * D>{};
+    };
+    using std::integral_constant;
+    const integral_constant<int, 0> X0, H0, R0;
+    const integral_constant<int, 1> X1, H1, R1;
+
+    // Prologue: descriptors of c_0..3; K(c_0..2), V(c_0..1); V stage 3
+    // cleared (the first step's P V reads it with P = 0); S^T of unit 0 for
+    // both row blocks; K fragments of unit 1.
+    fill(integral_constant<int, 0>{});
+#pragma unroll
+    for (int j = 1; j < 4; ++j) drel[j] = drel[0], dv[j] = dv[0], dka[j] = dka[0], dva[j] = dva[0];
+    fill(integral_constant<int, 1>{});
+    fill(integral_constant<int, 2>{});
+    fill(integral_constant<int, 3>{});
+    load_k(integral_constant<int, 0>{});
+    load_k(integral_constant<int, 1>{});
+    load_k(integral_constant<int, 2>{});
+    load_v(integral_constant<int, 0>{});
+    load_v(integral_constant<int, 1>{});
+    {
+      constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane
+#pragma unroll
+      for (int i = 0; i < per; ++i) *(u32x4*)(&smem[7][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    kread(uoff(integral_constant<int, 0>{}, H0));
+    kwait0();
+    asm volatile("s_nop 4" ::: "memory");  // the Q fragments' moves into AGPRs precede this
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mfma_s_first(sacc[0][rb], kf[0], qf[rb][0]);
+#pragma unroll
+    for (int c = 1; c < KC; ++c)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mfma_s_next(sacc[0][rb], kf[c], qf[rb][c]);
+    // S^T of unit 0 is read by vector code (a mask) right at the first step
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
+    kread(uoff(integral_constant<int, 0>{}, H1));  // unit 1 (waited for at the first step)
+
+    auto head = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NL) : "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto iter = [&](auto J) __attribute__((always_inline)) {  // iteration t, J = t % 4
+      constexpr int j = decltype(J)::value;
+      const integral_constant<int, j> SJ;
+      const integral_constant<int, (j + 1) & 3> SJ1;
+      const integral_constant<int, (j + 2) & 3> SJ2;
+      const integral_constant<int, (j + 3) & 3> SJ3;
+      const bool mt = dv[j] >= 128;
+      if (__builtin_expect(mt, 0)) {
+        sm_mask(0, 0, q0w + 0 + drel[j], half_valid(dv[j] & 127, 0));
+        sm_mask(0, 1, q0w + drel[j], half_valid(dv[j] & 127, 0));
+      }
+      step(X0, T, T, T, T, uoff(SJ3, H1), 0u, uoff(SJ1, H0), [&]() __attribute__((always_inline)) { load_k(SJ3); });
+      if (__builtin_expect(mt, 0)) {
+        sm_mask(1, 0, q0w + drel[j] + 32, half_valid(dv[j] & 127, 1));
+        sm_mask(1, 1, q0w + drel[j] + 32, half_valid(dv[j] & 127, 1));
+      }
+      step(X1, T, T, T, T, uoff(SJ, H0), 0u, uoff(SJ1, H1), [&]() __attribute__((always_inline)) { load_v(SJ2); });
+      fill(SJ);
+    };
+    int t = 0;
+    for (;;) {
+      iter(integral_constant<int, 0>{});
+      if (++t == n) break;
+      head();
+      iter(integral_constant<int, 1>{});
+      if (++t == n) break;
+      head();
+      iter(integral_constant<int, 2>{});
+      if (++t == n) break;
+      head();
+      iter(integral_constant<int, 3>{});
+      if (++t == n) break;
+      head();
+    }
+    step(X0, F, T, F, F, uoff(integral_constant<int, 0>{}, H1), (unsigned)((n - 1) & 3) * TILE_BYTES,
+         uoff(integral_constant<int, 0>{}, H0), []() {});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // Epilogue, per row block: the two halves of each row sum live in lanes
+  // lr and lr + 32.
+  ofrag_drain();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float ltot;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum[rb]), __float_as_uint(lsum[rb]), false,
+                                                       false);
+      ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (!q_ok[rb]) continue;
+    if (a.out_state) {
+      float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q[rb] * a.oa_ss + (int64_t)h * a.oa_sh;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 x = {o[rb][db][4 * j], o[rb][db][4 * j + 1], o[rb][db][4 * j + 2], o[rb][db][4 * j + 3]};
+          *(f32x4*)(op + 32 * db + 8 * j + 4 * lg) = x;
+        }
+      if (lg == 0) {
+        a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q[rb] * a.m_ss] = m2[rb] * kLn2;
+        a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q[rb] * a.l_ss] = ltot;
+      }
+    } else {
+      const float inv = 1.f / ltot;
+      const int64_t base = (int64_t)b * a.o_sb + (int64_t)my_q[rb] * a.o_ss + (int64_t)h * a.o_sh;
+      if (a.o_bf16) {
+        __bf16* op = (__bf16*)a.o + base;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x4 x = {(__bf16)(o[rb][db][4 * j] * inv), (__bf16)(o[rb][db][4 * j + 1] * inv),
+                        (__bf16)(o[rb][db][4 * j + 2] * inv), (__bf16)(o[rb][db][4 * j + 3] * inv)};
+            *(bf16x4*)(op + 32 * db + 8 * j + 4 * lg) = x;
+          }
+      } else {
+        float* op = (float*)a.o + base;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4 x = {o[rb][db][4 * j] * inv, o[rb][db][4 * j + 1] * inv, o[rb][db][4 * j + 2] * inv,
+                       o[rb][db][4 * j + 3] * inv};
+            *(f32x4*)(op + 32 * db + 8 * j + 4 * lg) = x;
+          }
+      }
+      if (lg == 0 && a.lse)
+        a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)my_q[rb] * a.lse_ss] =
+            (m2[rb] + __log2f(ltot)) * kLn2;
+    }
+  }
+}
+
 // fp32 path: one wave per workgroup, one query row per lane, fp32 FMA
 // throughout (dot products, softmax, P V).  K and V tiles of 64 keys are
 // staged in LDS and read by all lanes at the same address (broadcast).
@@ -829,9 +1437,9 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
 }  // namespace
 
 hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t st) {
-  const dim3 grid((unsigned)(ra_query_tiles(a, RA_BF16_BM) * a.Hq * a.B)), block(512);
-  if (d == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, st, a);
+  const dim3 grid((unsigned)(ra_query_tiles(a, RA_BF16_BM) * a.Hq * a.B)), block(RA_BF16_THREADS);
+  if (d == 128) hipLaunchKernelGGL(attn_bf16_w64_kernel<128>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(attn_bf16_w64_kernel<64>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,14 +1,15 @@
 // Host check of the causal decisions the kernels take, against the oracle's
 // classifier (oracle/ra_oracle.c, linked in by tests/test_plan_native.py).
 //
-// The forward kernel (and the dQ kernel, which walks keys the same way)
-// takes three integer decisions per workgroup of BM = 256 query rows (8 waves
-// of 32) and key block [k0, k0 + nk):
+// The forward kernels (and the dQ kernel, which walks keys the same way)
+// take three integer decisions per workgroup of BM = 256 query rows (waves of
+// 32 or 64 rows, in row blocks of 32) and key block [k0, k0 + nk):
 //   1. how many 64-key tiles to walk: ra_plan_key_tiles;
 //   2. per tile and wave, whether the softmax needs its masked form:
 //      ra_plan_tile_masked on the tile's position relative to the wave's first
 //      query (32-bit, saturated at -2^30 as the kernel's tile cursor keeps it),
-//      then per 32-key unit (ra_plan_half_valid keys) the same test again;
+//      then per 32-key unit (ra_plan_half_valid keys) and row block the same
+//      test again;
 //   3. per masked unit and query row, the visible keys: a prefix of
 //      ra_plan_visible_prefix keys.
 // The dK/dV kernel starts its walk over query tiles of 64 rows at
@@ -32,7 +33,7 @@ int64_t orc_visible_pairs(int64_t q_off, int64_t nq, int64_t kv_off, int64_t nkv
 
 namespace {
 
-constexpr int BM = 256, WAVE_ROWS = 32, BN = 64, UNIT = 32;
+constexpr int BM = 256, BN = 64, UNIT = 32;
 long long g_checked = 0;
 
 bool fail(const char* what, long long q0, long long nq, long long k0, long long nk, int causal, long long a,
@@ -42,8 +43,11 @@ bool fail(const char* what, long long q0, long long nq, long long k0, long long 
   return false;
 }
 
-// One forward workgroup (rows [q0, q0 + nq), nq <= BM) against one key block.
-bool check_forward(int64_t q0, int nq, int64_t k0, int64_t nk, int causal) {
+// One forward workgroup (rows [q0, q0 + nq), nq <= BM) against one key
+// block; waves of wave_rows rows, each in row blocks of 32 (the 32- and the
+// 64-rows-per-wave kernels: the tile flag is taken for the wave's first
+// row, the unit tests per row block).
+bool check_forward(int64_t q0, int nq, int64_t k0, int64_t nk, int causal, int wave_rows) {
   const int64_t n = ra_plan_key_tiles(q0, nq, k0, nk, causal, BN);
   const int64_t all = (nk + BN - 1) / BN;
   for (int64_t t = 0; t < all; ++t) {
@@ -53,9 +57,9 @@ bool check_forward(int64_t q0, int nq, int64_t k0, int64_t nk, int causal) {
     ++g_checked;
     if (walked != visible) return fail("tile walked iff it holds a visible pair", q0, nq, k0, nk, causal, walked, visible);
   }
-  for (int w = 0; w * WAVE_ROWS < nq; ++w) {
-    const int64_t q0w = q0 + w * WAVE_ROWS;
-    const int nqw = nq - w * WAVE_ROWS < WAVE_ROWS ? nq - w * WAVE_ROWS : WAVE_ROWS;
+  for (int w = 0; w * wave_rows < nq; ++w) {
+    const int64_t q0w = q0 + w * wave_rows;
+    const int nqw = nq - w * wave_rows < wave_rows ? nq - w * wave_rows : wave_rows;
     // the kernel's cursor: relative position of the block saturated at
     // +-2^30, then advanced by BN per tile
     const int64_t rel0 = k0 - q0w;
@@ -72,25 +76,30 @@ bool check_forward(int64_t q0, int nq, int64_t k0, int64_t nk, int causal) {
       for (int hf = 0; hf < 2; ++hf) {
         const int nvu = ra_plan_half_valid(nvt, hf, UNIT);
         const int64_t ku = kt + hf * UNIT;
-        const bool masked = flag && ra_plan_tile_masked<int64_t>(ku - q0w, nvu, UNIT, causal);
-        if (!masked) {
-          // the plain softmax: every one of the unit's 32 slots holds a key
-          // visible to every row of the wave
-          const int64_t vis = orc_visible_pairs(q0w, nqw, ku, nvu, causal);
-          ++g_checked;
-          if (nvu != UNIT || vis != (int64_t)nqw * UNIT)
-            return fail("unmasked unit has every pair visible", q0w, nqw, ku, nvu, causal, (long long)nqw * UNIT, vis);
-          tile_pairs += (int64_t)nqw * UNIT;
-          continue;
-        }
-        for (int i = 0; i < nqw; ++i) {
-          const int64_t lim = ra_plan_visible_prefix(q0w + i, ku, nvu, causal);
-          const int64_t vis_all = orc_visible_pairs(q0w + i, 1, ku, nvu, causal);
-          const int64_t vis_pre = orc_visible_pairs(q0w + i, 1, ku, lim, causal);
-          ++g_checked;
-          if (lim != vis_all || vis_pre != lim)
-            return fail("visible prefix is exactly the visible keys", q0w + i, 1, ku, nvu, causal, lim, vis_all);
-          tile_pairs += lim;
+        for (int rb = 0; rb * 32 < nqw; ++rb) {
+          const int64_t q0r = q0w + 32 * rb;
+          const int nqr = nqw - 32 * rb < 32 ? nqw - 32 * rb : 32;
+          const bool masked = flag && ra_plan_tile_masked<int64_t>(ku - q0r, nvu, UNIT, causal);
+          if (!masked) {
+            // the plain softmax: every one of the unit's 32 slots holds a key
+            // visible to every row of the row block
+            const int64_t vis = orc_visible_pairs(q0r, nqr, ku, nvu, causal);
+            ++g_checked;
+            if (nvu != UNIT || vis != (int64_t)nqr * UNIT)
+              return fail("unmasked unit has every pair visible", q0r, nqr, ku, nvu, causal, (long long)nqr * UNIT,
+                          vis);
+            tile_pairs += (int64_t)nqr * UNIT;
+            continue;
+          }
+          for (int i = 0; i < nqr; ++i) {
+            const int64_t lim = ra_plan_visible_prefix(q0r + i, ku, nvu, causal);
+            const int64_t vis_all = orc_visible_pairs(q0r + i, 1, ku, nvu, causal);
+            const int64_t vis_pre = orc_visible_pairs(q0r + i, 1, ku, lim, causal);
+            ++g_checked;
+            if (lim != vis_all || vis_pre != lim)
+              return fail("visible prefix is exactly the visible keys", q0r + i, 1, ku, nvu, causal, lim, vis_all);
+            tile_pairs += lim;
+          }
         }
       }
       // the two units cover exactly the tile's keys
@@ -135,7 +144,8 @@ int main() {
           for (int64_t nk : nks) {
             const int64_t k0 = q0 + dk;
             if (k0 < 0) continue;
-            if (!check_forward(q0, nq, k0, nk, causal)) return 1;
+            for (int wr : {32, 64})
+              if (!check_forward(q0, nq, k0, nk, causal, wr)) return 1;
           }
   // random positions, including a block far before the queries (the
   // saturated relative position) and long blocks
@@ -146,7 +156,8 @@ int main() {
     const int64_t q0 = (it % 50 == 0) ? (int64_t(3) << 30) + (int64_t)(rng() % 1000) : (int64_t)(rng() % 20000);
     const int64_t nk = 1 + (int64_t)(rng() % 2000);
     const int64_t k0 = (it % 50 == 0) ? (int64_t)(rng() % 1000) : (int64_t)(rng() % 22000);
-    if (!check_forward(q0, nq, k0, nk, causal)) return 1;
+    for (int wr : {32, 64})
+      if (!check_forward(q0, nq, k0, nk, causal, wr)) return 1;
   }
   for (int causal = 0; causal < 2; ++causal)
     for (int64_t qpos : {0, 64, 100, 1000})

@@ -147,16 +147,27 @@ def padded_backward_gpu(q, k, v, P, rank, causal, n_valid, dout, scale=None):
 
 # Gradients: bf16 operands (q, k, v, dO, the forward's bf16 O, and P and dS
 # rounded to bf16 for the MFMAs) against the exact fp64 chain rule.  Each
-# rounding is at most 2^-9 relative; the gradients are sums of such terms, so
-# the error is bounded relative to the gradient's own scale.
+# rounding is at most 2^-8 relative; a gradient row is a sum of such terms,
+# so its error is bounded relative to the row's own scale.  The bound is
+# taken per row (one query's dQ, one key's dK or dV): an error confined to
+# the rows of small magnitude cannot hide behind the largest row of the
+# tensor.
 GRAD_TOL = 1e-2
 
 
 def assert_grad_close(g, g_ref, what: str):
-    """max |g - g_ref| <= GRAD_TOL * max(1, max |g_ref|) (fp64 numpy arrays)."""
+    """Per row: max |g - g_ref| <= GRAD_TOL * max(1, max |g_ref| of that
+    row) (fp64 numpy arrays, rows = every index but the last); an absolute
+    floor of GRAD_TOL."""
     assert np.isfinite(g).all(), f"{what}: non-finite gradient"
-    scale = max(1.0, float(np.abs(g_ref).max()) if g_ref.size else 1.0)
-    err = float(np.abs(g - g_ref).max()) if g.size else 0.0
-    say(f"{what}: max|d| = {err:.3e}, max|ref| = {scale:.3e} (tol {GRAD_TOL} x {scale:.3g})")
-    assert err <= GRAD_TOL * scale, f"{what}: max |g - g_ref| = {err} > {GRAD_TOL * scale}"
+    if not g.size:
+        return
+    g, g_ref = g.reshape(-1, g.shape[-1]), g_ref.reshape(-1, g_ref.shape[-1])
+    scale = np.maximum(1.0, np.abs(g_ref).max(axis=1))
+    err = np.abs(g - g_ref).max(axis=1)
+    worst = int(np.argmax(err / scale))
+    say(f"{what}: max|d| = {float(err.max()):.3e}; worst row {worst}: {float(err[worst]):.3e} against "
+        f"{GRAD_TOL} x {float(scale[worst]):.3g} ({len(err)} rows)")
+    assert (err <= GRAD_TOL * scale).all(), \
+        f"{what}: row {worst}: max |g - g_ref| = {float(err[worst])} > {GRAD_TOL * float(scale[worst])}"
 

@@ -295,10 +295,10 @@ def test_ra_merge_validation():
 
 def test_launches_beyond_the_work_item_limit_are_rejected():
     """A grid is at most 2^32 - 1 work-items along x: the bf16 forward runs
-    512 threads per 256 query rows, the backward 256 per 128 rows, the state
+    256 threads per 256 query rows, the backward 256 per 128 rows, the state
     kernels 512 per 64 rows (d = 128)."""
     L = ra.lib()
-    heads = (1 << 23) + 1                        # one 256-row tile each: > 2^32 / 512 workgroups
+    heads = (1 << 24) + 1                        # one 256-row tile each: > 2^32 / 256 workgroups
     q, k = T([1, 256, heads, 128]), T([1, 256, 1, 128])
     assert share(q, k, k, 1, 0, o_out=T([1, 256, heads, 128])) == ra.RA_E_RANGE
     assert "work-items" in ra.ra_last_error()

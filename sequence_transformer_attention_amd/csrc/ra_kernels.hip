@@ -868,16 +868,17 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     voffg[i] = (unsigned)r * (unsigned)a.v_ss * 2u + sl;
   }
   const unsigned smem_lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]);
-  auto issue = [&](const char* tb, int64_t stride, const unsigned* goff, int nvalid, auto STAGE)
+  // Chunk CHUNK (1 KiB, one instruction) of the wave's share of a tile:
+  // the loads of a tile are spread over consecutive pipeline slots.
+  auto issue = [&](const char* tb, int64_t stride, const unsigned* goff, int nvalid, auto STAGE, auto CHUNK)
       __attribute__((always_inline)) {
     const int nrec = (nvalid - 1) * (int)stride * 2 + 2 * D;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, nrec, 0x00020000);
     unsigned lb = smem_lds + (unsigned)wv * NL * 1024;
     asm volatile("" : "+s"(lb));
     char* dst = (char*)&smem[0][0] + (lb - smem_lds) + decltype(STAGE)::value * TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, goff[i], 0, 0, 0);
+    constexpr int i = decltype(CHUNK)::value;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * 1024), 16, goff[i], 0, 0, 0);
   };
 
   unsigned kaddr[KC];
@@ -943,13 +944,19 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
         }
       }
     };
-    auto load_k = [&](auto ST) __attribute__((always_inline)) {
+    auto load_k = [&](auto ST, auto CH) __attribute__((always_inline)) {
       constexpr int j = decltype(ST)::value;
-      issue(dka[j], a.k_ss, koffg, dv[j] & 127, ST);
+      issue(dka[j], a.k_ss, koffg, dv[j] & 127, ST, CH);
     };
-    auto load_v = [&](auto ST) __attribute__((always_inline)) {
+    auto load_v = [&](auto ST, auto CH) __attribute__((always_inline)) {
       constexpr int j = decltype(ST)::value;
-      issue(dva[j], a.v_ss, voffg, dv[j] & 127, std::integral_constant<int, 4 + j>{});
+      issue(dva[j], a.v_ss, voffg, dv[j] & 127, std::integral_constant<int, 4 + j>{}, CH);
+    };
+    auto load_k_all = [&](auto ST) __attribute__((always_inline)) {
+      static_for<0, NL>([&](auto CH) { load_k(ST, CH); });
+    };
+    auto load_v_all = [&](auto ST) __attribute__((always_inline)) {
+      static_for<0, NL>([&](auto CH) { load_v(ST, CH); });
     };
 
     f32x16 sacc[2][RB];       // S^T of units with even / odd index, per row block
@@ -1144,7 +1151,7 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
           if constexpr (kn) kread(KO);
         }
         if constexpr (sl == SS + DB && pv) vwait1(KN);  // the K reads for the next step (if any) are younger
-        if constexpr (sl == 4) load();
+        if constexpr (sl >= 2 && sl < 2 + NL) load(std::integral_constant<int, sl - 2>{});
         __builtin_amdgcn_sched_barrier(0);
         mfma_j(std::integral_constant<int, 2 * sl>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -1180,11 +1187,11 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     fill(integral_constant<int, 1>{});
     fill(integral_constant<int, 2>{});
     fill(integral_constant<int, 3>{});
-    load_k(integral_constant<int, 0>{});
-    load_k(integral_constant<int, 1>{});
-    load_k(integral_constant<int, 2>{});
-    load_v(integral_constant<int, 0>{});
-    load_v(integral_constant<int, 1>{});
+    load_k_all(integral_constant<int, 0>{});
+    load_k_all(integral_constant<int, 1>{});
+    load_k_all(integral_constant<int, 2>{});
+    load_v_all(integral_constant<int, 0>{});
+    load_v_all(integral_constant<int, 1>{});
     {
       constexpr int per = TILE_BYTES / (NW * 64 * 16);  // 16-byte stores per lane
 #pragma unroll
@@ -1221,12 +1228,14 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
         sm_mask(0, 0, q0w + 0 + drel[j], half_valid(dv[j] & 127, 0));
         sm_mask(0, 1, q0w + drel[j], half_valid(dv[j] & 127, 0));
       }
-      step(X0, T, T, T, T, uoff(SJ3, H1), 0u, uoff(SJ1, H0), [&]() __attribute__((always_inline)) { load_k(SJ3); });
+      step(X0, T, T, T, T, uoff(SJ3, H1), 0u, uoff(SJ1, H0),
+           [&](auto CH) __attribute__((always_inline)) { load_k(SJ3, CH); });
       if (__builtin_expect(mt, 0)) {
         sm_mask(1, 0, q0w + drel[j] + 32, half_valid(dv[j] & 127, 1));
         sm_mask(1, 1, q0w + drel[j] + 32, half_valid(dv[j] & 127, 1));
       }
-      step(X1, T, T, T, T, uoff(SJ, H0), 0u, uoff(SJ1, H1), [&]() __attribute__((always_inline)) { load_v(SJ2); });
+      step(X1, T, T, T, T, uoff(SJ, H0), 0u, uoff(SJ1, H1),
+           [&](auto CH) __attribute__((always_inline)) { load_v(SJ2, CH); });
       fill(SJ);
     };
     int t = 0;
@@ -1245,7 +1254,7 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
       head();
     }
     step(X0, F, T, F, F, uoff(integral_constant<int, 0>{}, H1), (unsigned)((n - 1) & 3) * TILE_BYTES,
-         uoff(integral_constant<int, 0>{}, H0), []() {});
+         uoff(integral_constant<int, 0>{}, H0), [](auto) {});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 

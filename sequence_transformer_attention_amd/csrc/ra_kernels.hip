@@ -1314,15 +1314,28 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
   }
 }
 
-// fp32 path: one wave per workgroup, one query row per lane, fp32 FMA
-// throughout (dot products, softmax, P V).  K and V tiles of 64 keys are
-// staged in LDS and read by all lanes at the same address (broadcast).
+// fp32 path: fp32 FMA throughout (dot products, softmax, P V).  A workgroup
+// takes 64 query rows; each row belongs to LPR = D / 64 lanes of one wave
+// (lanes l and l ^ 32 when D = 128), each holding 64 channels of the row's
+// Q and O in registers, so the partial dot products of a key meet in one
+// cross-lane swap.  K and V tiles of 64 keys are staged in LDS and read by
+// all lanes of a half at the same address (broadcast).  The online softmax
+// runs over chunks of 16 keys held in registers: chunk max, rescale of O
+// and l when it grows, exponentials, O += p V.
 template <int D>
-__global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
-  constexpr int BM = RA_F32_BM, BN = RA_F32_BN;
+__global__ void __launch_bounds__(64 * (D / 64)) attn_f32_kernel(RaAttnArgs a) {
+  constexpr int BM = RA_F32_BM, BN = RA_F32_BN, CH = 16;
+  constexpr int LPR = D / 64, DL = D / LPR;  // lanes per row, channels per lane
+  constexpr int NT = 64 * LPR;               // threads
+  static_assert(DL == 64 && BM == 64, "64 channels per lane, 64 rows per workgroup");
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int tid = threadIdx.x;
+  // row of the workgroup and channel half: rows 32 w .. 32 w + 31 in wave w
+  // when a row takes two lanes (l, l ^ 32), else row = lane
+  const int lrow = LPR == 2 ? (tid >> 6) * 32 + (tid & 31) : tid;
+  const int half = LPR == 2 ? (tid >> 5) & 1 : 0;
+  const int c0 = half * DL;
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;  // rows per chunk
   const int nqt_c = (nqc + BM - 1) / BM;
   const int nqt = (a.nsplit == 2 ? 2 : 1) * nqt_c;
@@ -1333,27 +1346,30 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
   const int chunk = qt / nqt_c;
   const int64_t qpos0 = chunk ? a.q_off2 : a.q_off;
   const int rank_e = chunk ? a.rank2 : a.rank;
-  const int qrow = (qt - chunk * nqt_c) * BM + tid;  // row within the chunk
+  const int qrow0 = (qt - chunk * nqt_c) * BM;      // the workgroup's first row within the chunk
+  const int qrow = qrow0 + lrow;
   const int my_q = chunk * nqc + qrow;
   const bool q_ok = qrow < nqc;
 
-  float q[D], o[D];
+  float q[DL], o[DL];
   {
-    const float* qp = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)my_q * a.q_ss + (int64_t)h * a.q_sh;
+    const float* qp = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)my_q * a.q_ss + (int64_t)h * a.q_sh + c0;
 #pragma unroll
-    for (int c = 0; c < D; c += 4) {
+    for (int c = 0; c < DL; c += 4) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       if (q_ok) x = *(const f32x4*)(qp + c);
       q[c] = x[0]; q[c + 1] = x[1]; q[c + 2] = x[2]; q[c + 3] = x[3];
     }
   }
+  // running max m2 (log2 units of the scaled logits) and sum l, the same in
+  // both lanes of a row
   float m2 = -INFINITY, lsum = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; ++c) o[c] = 0.f;
+  for (int c = 0; c < DL; ++c) o[c] = 0.f;
   if (a.state_in && q_ok) {
-    const float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh;
+    const float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh + c0;
 #pragma unroll
-    for (int c = 0; c < D; c += 4) {
+    for (int c = 0; c < DL; c += 4) {
       f32x4 x = *(const f32x4*)(op + c);
       o[c] = x[0]; o[c + 1] = x[1]; o[c + 2] = x[2]; o[c + 3] = x[3];
     }
@@ -1361,8 +1377,9 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
     lsum = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q * a.l_ss];
   }
 
-  const int64_t q0_wg = qpos0 + (qrow - tid);
-  const int nq_wg = min(BM, nqc - (qrow - tid));
+  const int64_t q0_wg = qpos0 + qrow0;
+  const int nq_wg = min(BM, nqc - qrow0);
+  const int64_t qpos = qpos0 + qrow;
   const int nsteps = a.ring ? a.P : 1;
   for (int s = 0; s < nsteps; ++s) {
     const int64_t jb = a.ring ? ra_plan_ring_block(a.P, rank_e, s) : 0;
@@ -1376,70 +1393,97 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(RaAttnArgs a) {
       const float* kb = (const float*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + (row0 + (int64_t)u * BN) * a.k_ss;
       const float* vb = (const float*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + (row0 + (int64_t)u * BN) * a.v_ss;
       __syncthreads();
-      for (int id = tid; id < BN * D / 4; id += 64) {
-        const int row = id / (D / 4), c4 = id % (D / 4);
+      for (int id = tid; id < BN * D / 4; id += NT) {
+        const int r = id / (D / 4), c4 = id % (D / 4);
         f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-        if (row < nvalid) {
-          kx = *(const f32x4*)(kb + (int64_t)row * a.k_ss + 4 * c4);
-          vx = *(const f32x4*)(vb + (int64_t)row * a.v_ss + 4 * c4);
+        if (r < nvalid) {
+          kx = *(const f32x4*)(kb + (int64_t)r * a.k_ss + 4 * c4);
+          vx = *(const f32x4*)(vb + (int64_t)r * a.v_ss + 4 * c4);
         }
-        *(f32x4*)(Ks + row * D + 4 * c4) = kx;
-        *(f32x4*)(Vs + row * D + 4 * c4) = vx;
+        *(f32x4*)(Ks + r * D + 4 * c4) = kx;
+        *(f32x4*)(Vs + r * D + 4 * c4) = vx;
       }
       __syncthreads();
       const int64_t k0 = kv_off + (int64_t)u * BN;
-      const int64_t qpos = qpos0 + qrow;
-      float sc[BN];
-      float mx = -INFINITY;
-      for (int j = 0; j < BN; ++j) {
-        float dot = 0.f;
+      // visible keys of this row in the tile: a prefix of lim
+      const int lim = (int)ra_plan_visible_prefix(qpos, k0, nvalid, a.causal);
+      for (int j0 = 0; j0 < BN; j0 += CH) {
+        if (j0 >= lim) break;  // the rest of the tile is masked for this row (uniform per wave when it matters)
+        float sc[CH];
 #pragma unroll
-        for (int c = 0; c < D; ++c) dot = fmaf(q[c], Ks[j * D + c], dot);
-        const bool vis = j < nvalid && (!a.causal || k0 + j <= qpos);
-        sc[j] = vis ? dot : -INFINITY;
-        mx = fmaxf(mx, sc[j]);
+        for (int j = 0; j < CH; ++j) {
+          const float* kr = Ks + (j0 + j) * D + c0;
+          float dot = 0.f;
+#pragma unroll
+          for (int c = 0; c < DL; c += 4) {
+            const f32x4 kx = *(const f32x4*)(kr + c);
+            dot = fmaf(q[c], kx[0], dot);
+            dot = fmaf(q[c + 1], kx[1], dot);
+            dot = fmaf(q[c + 2], kx[2], dot);
+            dot = fmaf(q[c + 3], kx[3], dot);
+          }
+          if constexpr (LPR == 2) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
+            dot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          }
+          sc[j] = j0 + j < lim ? dot * a.c : -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int j = 1; j < CH; ++j) mx = fmaxf(mx, sc[j]);
+        const float m_new = fmaxf(m2, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        if (m_new > m2) {  // rescale only when the max grows (alpha = 0 when m2 was -inf)
+          const float alpha = exp2f(m2 - m_use);
+          lsum *= alpha;
+#pragma unroll
+          for (int c = 0; c < DL; ++c) o[c] *= alpha;
+          m2 = m_new;
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const float p = exp2f(sc[j] - m_use);
+          lsum += p;
+          const float* vr = Vs + (j0 + j) * D + c0;
+#pragma unroll
+          for (int c = 0; c < DL; c += 4) {
+            const f32x4 vx = *(const f32x4*)(vr + c);
+            o[c] = fmaf(p, vx[0], o[c]);
+            o[c + 1] = fmaf(p, vx[1], o[c + 1]);
+            o[c + 2] = fmaf(p, vx[2], o[c + 2]);
+            o[c + 3] = fmaf(p, vx[3], o[c + 3]);
+          }
+        }
       }
-      const float m_new = fmaxf(m2, mx * a.c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m2 - m_use);
-      lsum *= alpha;
-#pragma unroll
-      for (int c = 0; c < D; ++c) o[c] *= alpha;
-      for (int j = 0; j < BN; ++j) {
-        const float p = exp2f(fmaf(sc[j], a.c, -m_use));
-        lsum += p;
-#pragma unroll
-        for (int c = 0; c < D; ++c) o[c] = fmaf(p, Vs[j * D + c], o[c]);
-      }
-      m2 = m_new;
     }
   }
 
   if (!q_ok) return;
   if (a.out_state) {
-    float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh;
+    float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q * a.oa_ss + (int64_t)h * a.oa_sh + c0;
 #pragma unroll
-    for (int c = 0; c < D; c += 4) *(f32x4*)(op + c) = f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]};
-    a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q * a.m_ss] = m2 * kLn2;
-    a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q * a.l_ss] = lsum;
+    for (int c = 0; c < DL; c += 4) *(f32x4*)(op + c) = f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]};
+    if (half == 0) {
+      a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q * a.m_ss] = m2 * kLn2;
+      a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q * a.l_ss] = lsum;
+    }
   } else {
     const float inv = 1.f / lsum;
-    const int64_t base = (int64_t)b * a.o_sb + (int64_t)my_q * a.o_ss + (int64_t)h * a.o_sh;
+    const int64_t base = (int64_t)b * a.o_sb + (int64_t)my_q * a.o_ss + (int64_t)h * a.o_sh + c0;
     if (a.o_bf16) {
       __bf16* op = (__bf16*)a.o + base;
 #pragma unroll
-      for (int c = 0; c < D; c += 4)
+      for (int c = 0; c < DL; c += 4)
         *(bf16x4*)(op + c) = bf16x4{(__bf16)(o[c] * inv), (__bf16)(o[c + 1] * inv),
                                     (__bf16)(o[c + 2] * inv), (__bf16)(o[c + 3] * inv)};
     } else {
       float* op = (float*)a.o + base;
 #pragma unroll
-      for (int c = 0; c < D; c += 4)
+      for (int c = 0; c < DL; c += 4)
         *(f32x4*)(op + c) = f32x4{o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
     }
-    if (a.lse)
-      a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)my_q * a.lse_ss] =
-          m2 * kLn2 + logf(lsum);
+    if (half == 0 && a.lse)
+      a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)my_q * a.lse_ss] = m2 * kLn2 + logf(lsum);
   }
 }
 
@@ -1453,7 +1497,7 @@ hipError_t ra_launch_attn_bf16(const RaAttnArgs& a, int d, hipStream_t st) {
 }
 
 hipError_t ra_launch_attn_f32(const RaAttnArgs& a, int d, hipStream_t st) {
-  const dim3 grid((unsigned)(ra_query_tiles(a, RA_F32_BM) * a.Hq * a.B)), block(64);
+  const dim3 grid((unsigned)(ra_query_tiles(a, RA_F32_BM) * a.Hq * a.B)), block(64 * (d / 64));
   if (d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, block, 0, st, a);
   return hipGetLastError();

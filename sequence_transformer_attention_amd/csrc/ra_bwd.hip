@@ -171,15 +171,16 @@ __device__ __forceinline__ void mfma_acc_drain(f32x16& c) {
 }
 
 // Load a 64-row tile (rows row0 .. row0 + nvalid - 1 of a [*, D] bf16 matrix
-// with row stride `stride` elements, at most 2^24; nvalid >= 1) into LDS at
+// with row stride `stride` elements, at most 2^24; nvalid <= 64) into LDS at
 // dst, swizzled.  All NW waves take a share of 1 KiB chunks.  The buffer
-// range ends at row nvalid - 1, so rows past it are out of range: nothing is
-// fetched for them and their LDS bytes are written as zeros.
+// range ends at row nvalid - 1 (is empty for nvalid <= 0), so rows past it
+// are out of range: nothing is fetched for them and their LDS bytes are
+// written as zeros.
 template <int D, int NW>
 __device__ __forceinline__ void load_tile(const __bf16* row0, int64_t stride, int nvalid, char* dst, int wave,
                                           int lane) {
   constexpr int SLOTS = D / 8, TILE = 64 * D * 2, NL = TILE / 1024 / NW;
-  const int nrec = (nvalid - 1) * (int)stride * 2 + 2 * D;
+  const int nrec = nvalid > 0 ? (nvalid - 1) * (int)stride * 2 + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row0, (short)0, nrec, 0x00020000);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
@@ -394,12 +395,42 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
     }
 }
 
+// S (queries x keys) = Q K^T and dP = dO V^T of the dK/dV kernel: A (Q or dO
+// rows) in VGPRs, B (the lane's key: K or V) in AGPRs, the accumulator in
+// VGPRs.  Inline asm (the compiler would keep K and V in VGPRs): before a
+// vector read of the result the caller waits with qk_drain.
+__device__ __forceinline__ void mfma_qk_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_qk_next(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+// 16 wait states between the last MFMA writing c and a vector read of c
+// (gfx950 needs 12 after an 8-pass MFMA).
+__device__ __forceinline__ void qk_drain(f32x16& c) { asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c)); }
+
+// dK and dV of one kv head for 128 keys per workgroup, 32 per wave (lane =
+// key lr, both lane halves): K and V of the lane's key stay in AGPRs, the
+// dK and dV accumulators too.  The query rows that see the keys are walked
+// in tiles of QT = 128 rows (four 32-row units), Q and dO tiles staged in
+// LDS in two stages with the next tile's loads in flight.  Per unit:
+//   S = Q K^T, dP = dO V^T (8 + 8 MFMAs), P = exp2(S c - LSE log2 e)
+//   under the causal mask, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS
+// with dO^T and Q^T from transposing LDS reads.  The LDS reads are issued
+// ahead of their products: a unit's dO rows before its S products, its dO^T
+// and Q^T before its dP products, the next unit's Q rows and row statistics
+// during this unit's dK products (within a tile), so only the first unit of
+// a tile waits for its Q rows.
 template <int D>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
-  constexpr int NW = 4, BK = NW * 32, BN = RA_BWD_BN, KC = D / 16, DB = D / 32, TILE = BN * D * 2;
-  // two stages of (Q tile, dO tile) and of their rows' (LSE log2(e), D)
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];
-  __shared__ __attribute__((aligned(16))) float lsd[2][2][BN];
+  constexpr int NW = 4, BK = NW * 32, QT = 128, NU = QT / 32, KC = D / 16, DB = D / 32;
+  constexpr int TILE = QT * D * 2;           // one Q or dO tile
+  constexpr unsigned DO_REGION = 2 * TILE;   // dO tiles follow both Q stages
+  static_assert(2 * TILE <= 65536, "LDS offsets within a region fit the 16-bit immediate");
+  // [Q stage 0 | Q stage 1 | dO stage 0 | dO stage 1]; row statistics
+  // (LSE log2(e), D) of both stages
+  __shared__ __attribute__((aligned(1024))) char smem[4][TILE];
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][QT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -413,7 +444,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // no query and get zero gradients
   const bool k_live = my_k < a.kv_end;
 
-  bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7
+  bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7 (AGPRs from here on)
   {
     const int64_t row = k_live ? my_k : 0;
     const __bf16* kp = (const __bf16*)a.k + (int64_t)b * a.k_sb + row * a.k_ss + (int64_t)g * a.k_sh + 8 * lg;
@@ -422,6 +453,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     for (int c = 0; c < KC; ++c) {
       kf[c] = k_live ? *(const bf16x8*)(kp + 16 * c) : bf16x8{};
       vf[c] = k_live ? *(const bf16x8*)(vp + 16 * c) : bf16x8{};
+      asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
     }
   }
   f32x16 dka[DB], dva[DB];
@@ -430,26 +462,21 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     mfma_acc_zero(dka[db]);
     mfma_acc_zero(dva[db]);
   }
-  TileAddr<D> ta;
-  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0][0]), lane);
+  TileAddr<D> ta;  // per-lane addresses in a 64-row tile (offsets: region, stage, unit)
+  ta.init((unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)&smem[0][0]), lane);
   const unsigned lsd_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) float*)&lsd[0][0][0]);
+  const unsigned lsd_lane = lsd_base + 16u * (unsigned)lg;  // + 4 floats per lane group
 
-  // Local query rows that see any key of the workgroup: under causal
-  // masking those at positions >= the first key's, per query chunk (two
-  // under the load-balanced split, each with its own positions).  The work
-  // is the list of (query head of the kv head, 64-row tile) pairs, walked
-  // with the loads of the next pair in flight during the current one.
+  // The walk: (query head of the kv head, 128-row tile) pairs over the local
+  // rows that see any key of the workgroup (under causal masking those at
+  // positions >= the first key's, per query chunk), as in the 64-row form.
   const int64_t kfirst = (int64_t)kt * BK;
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
-  const int ntq = (nqc + BN - 1) / BN;  // tiles per chunk
-  auto first_tile = [&](int64_t qpos) -> int { return ra_plan_first_query_tile(kfirst, qpos, nqc, BN, a.causal); };
+  const int ntq = (nqc + QT - 1) / QT;  // tiles per chunk
+  auto first_tile = [&](int64_t qpos) -> int { return ra_plan_first_query_tile(kfirst, qpos, nqc, QT, a.causal); };
   const int t0a = first_tile(a.q_off), t0b = a.nsplit == 2 ? first_tile(a.q_off2) : ntq;
   const int na = ntq - t0a, nt = na + (ntq - t0b);
   const int total = kfirst < a.kv_end ? G * nt : 0;  // no key before the key end: nothing to do
-  // A tile of the walk, walk index h * nt + w: query head g G + h, entry w
-  // of the head's tile list; its first local row, rows in its chunk and the
-  // position of its first row.  Two cursors step through the walk, one for
-  // the loads and one for the computation, so no tile needs a division.
   struct TileRef {
     int h, r0, nvalid;
     int64_t qp0;
@@ -462,9 +489,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     const int t = ch ? t0b + (c.w - na) : t0a + c.w;
     TileRef r;
     r.h = g * G + c.h;
-    r.r0 = ch * nqc + t * BN;
-    r.nvalid = min(BN, nqc - t * BN);
-    r.qp0 = (ch ? a.q_off2 : a.q_off) + (int64_t)t * BN;
+    r.r0 = ch * nqc + t * QT;
+    r.nvalid = min(QT, nqc - t * QT);
+    r.qp0 = (ch ? a.q_off2 : a.q_off) + (int64_t)t * QT;
     return r;
   };
   auto walk_next = [&](WalkCur& c) {
@@ -474,24 +501,47 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     }
   };
   WalkCur cl{0, 0}, cc{0, 0};  // load cursor, compute cursor
-  float lsv = 0.f, dlv = 0.f;  // threads 0..63: LSE log2(e) and D of row tid of the tile in flight
+  float lsv = 0.f, dlv = 0.f;  // threads 0..QT-1: LSE log2(e) and D of row tid of the tile in flight
   auto issue = [&](int st) __attribute__((always_inline)) {
     const TileRef tr = tile_ref(cl);
     walk_next(cl);
     const int h = tr.h, r0 = tr.r0, nvalid = tr.nvalid;
-    load_tile<D, NW>((const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss, a.q_ss,
-                     nvalid, &smem[st][0][0], wave, lane);
-    load_tile<D, NW>((const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)r0 * a.do_ss,
-                     a.do_ss, nvalid, &smem[st][1][0], wave, lane);
-    if (tid < BN) {
+    const __bf16* qrow = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss;
+    const __bf16* drow = (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)r0 * a.do_ss;
+#pragma unroll
+    for (int half = 0; half < QT / 64; ++half) {
+      load_tile<D, NW>(qrow + (int64_t)(64 * half) * a.q_ss, a.q_ss, nvalid - 64 * half,
+                       &smem[st][0] + half * (TILE / 2), wave, lane);
+      load_tile<D, NW>(drow + (int64_t)(64 * half) * a.do_ss, a.do_ss, nvalid - 64 * half,
+                       &smem[2 + st][0] + half * (TILE / 2), wave, lane);
+    }
+    if (tid < QT) {
       const int row = r0 + tid;
       const bool ok = tid < nvalid;
       lsv = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e : INFINITY;
       dlv = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
     }
   };
-  const unsigned lsd_lane = lsd_base + 16u * (unsigned)lg;  // + 4 floats per lane group
+
+  // LDS reads are asm with immediate offsets, issued ahead of their
+  // products and waited for with counts: LDS reads complete in order, and
+  // at most 14 are waited on as outstanding (the counter has 4 bits; the
+  // compiler's own waits stop at 14 as well).
+  bf16x8 fq[KC];  // Q rows of the unit (A operand of S), read one unit ahead
+  f32x4 l4[4];    // LSE log2(e) of the lane's 16 query rows (4 runs of 4), read with them
+  auto read_q_l4 = [&](auto ST, auto V) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value, v = decltype(V)::value;
+    constexpr unsigned o4 = ((unsigned)st * 2 * QT + 32u * v) * 4u;
+    static_for<0, 4>([&](auto J) { ds_rd128<o4 + 32u * decltype(J)::value>(l4[decltype(J)::value], lsd_lane); });
+    static_for<0, KC>([&](auto C) {
+      ds_rd128<(unsigned)st * TILE + (unsigned)v * 64 * D>(fq[decltype(C)::value], ta.rd[decltype(C)::value]);
+    });
+  };
+
   // One tile: stage ST (compile time, so every LDS offset is an immediate).
+  // Per 32-row unit, the products run S, dP, dV, dK, and each phase issues
+  // the reads of the next: the dO rows during S, dO^T during dP, Q^T during
+  // dV, the next unit's Q rows and LSE during dK.
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
     const int64_t qp0 = tile_ref(cc).qp0;
@@ -501,73 +551,60 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     const int64_t rel64 = my_k - qp0;
     const int rel = rel64 < -(1 << 30) ? -(1 << 30) : (int)rel64;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (tid < BN) {
+    if (tid < QT) {
       lsd[st][0][tid] = lsv;
       lsd[st][1][tid] = dlv;
     }
     __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
     if (it + 1 < total) issue(st ^ 1);
-    static_for<0, 2>([&](auto HF) {
-      constexpr int hf = decltype(HF)::value;
-      constexpr unsigned qo = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // Q unit; dO unit at + TILE
-      // Stage by stage, so that each operand set is live only as long as its
-      // products need it: S (Q rows), dP (dO rows) with P formed between its
-      // MFMAs, dV (dO^T) with dS formed between its MFMAs, dK (Q^T).
-      // S = Q K^T (queries x keys); query row of register r: 8 (r / 4) + 4 lg + (r % 4)
-      bf16x8 fq[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) ds_rd128<qo>(fq[c], ta.rd[c]);
-      // LSE log2(e) and D of the lane's 16 query rows (4 runs of 4)
-      f32x4 l4[4], d4[4];
+    read_q_l4(ST, std::integral_constant<int, 0>{});  // the tile's only exposed reads
+    static_for<0, NU>([&](auto V) {
+      constexpr int v = decltype(V)::value;
+      constexpr unsigned qo = (unsigned)st * TILE + (unsigned)v * 64 * D;  // unit v; dO at + DO_REGION
+      if constexpr (KC == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fq[4]),
+                     "+v"(fq[5]), "+v"(fq[6]), "+v"(fq[7]), "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]));
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(l4[0]),
+                     "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]));
+      // S = Q K^T (query row of register r: 8 (r / 4) + 4 lg + (r % 4)),
+      // with the dO rows read one per product, then D of the rows
+      f32x16 sacc;
+      bf16x8 fd[KC];
+      static_for<0, KC>([&](auto C) {
+        constexpr int c = decltype(C)::value;
+        if constexpr (c == 0) mfma_qk_first(sacc, fq[0], kf[0]);
+        else mfma_qk_next(sacc, fq[c], kf[c]);
+        ds_rd128<qo>(fd[c], ta.rd[c] + DO_REGION);
+      });
+      f32x4 d4[4];
       static_for<0, 4>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        constexpr unsigned o4 = ((unsigned)st * 2 * BN + 32u * hf + 8u * j) * 4u;
-        ds_rd128<o4>(l4[j], lsd_lane);
-        ds_rd128<o4 + BN * 4>(d4[j], lsd_lane);
+        ds_rd128<((unsigned)st * 2 * QT + QT + 32u * v + 8u * j) * 4u>(d4[j], lsd_lane);
       });
-      if constexpr (KC == 8)
-        asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fq[4]),
-                     "+v"(fq[5]), "+v"(fq[6]), "+v"(fq[7]));
-      else
-        asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]));
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sacc, 0, 0, 0);
-      // dP = dO V^T
-      bf16x8 fd[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) ds_rd128<qo + TILE>(fd[c], ta.rd[c]);
-      if constexpr (KC == 8)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(fd[4]),
-                     "+v"(fd[5]), "+v"(fd[6]), "+v"(fd[7]), "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]),
-                     "+v"(d4[0]), "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
-      else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fd[0]), "+v"(fd[1]), "+v"(fd[2]), "+v"(fd[3]), "+v"(l4[0]),
-                     "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]), "+v"(d4[0]), "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3]));
-      // dO^T for the dV product, in flight during the dP products
-      u32x2 olo[2][DB], ohi[2][DB];
-      static_for<0, 2 * DB>([&](auto X) {
-        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
-        constexpr unsigned off = qo + (unsigned)TILE + (unsigned)hh * 32 * D;
-        ds_rdtr<off>(olo[hh][d_], ta.tr[0][d_]);
-        ds_rdtr<off>(ohi[hh][d_], ta.tr[1][d_]);
-      });
-      // visible: under causal masking, the query at position qp0 + 32 hf +
+      // visible: under causal masking, the query at position qp0 + 32 v +
       // 4 lg + e (e = 8 (r / 4) + (r % 4)) is at or after this lane's key:
       // e >= lo.  Rows past their chunk need no test (their LSE is +inf:
       // P = 0, and D = 0), nor keys past the sequence (their P only reaches
       // their own dK, dV columns, which are not stored).
-      const int lo = !k_live ? (1 << 30) : (a.causal ? rel - 32 * hf - 4 * lg : -(1 << 30));
-      // dP = dO V^T, one MFMA at a time with 16 / KC elements of P formed
-      // after each (a single wave per SIMD: the vector work issues while the
-      // matrix core runs; the scheduling barriers keep this order)
+      const int lo = !k_live ? (1 << 30) : (a.causal ? rel - 32 * v - 4 * lg : -(1 << 30));
+      qk_drain(sacc);
+      // dP = dO V^T, one MFMA per slot; each slot also issues one pair of
+      // dO^T reads and forms 16 / KC elements of P
       constexpr int PE = 16 / KC;
-      f32x16 dpa = f32x16{};
+      f32x16 dpa;
       float pv[16];
       bf16x8 pf[2];
+      u32x2 olo[2][DB], ohi[2][DB], qlo[2][DB], qhi[2][DB];
       static_for<0, KC>([&](auto C) {
-        constexpr int c = decltype(C)::value;
-        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], vf[c], dpa, 0, 0, 0);
+        constexpr int c = decltype(C)::value, hh = c / DB, d_ = c % DB;
+        // fd[c] done: the reads after it are fd[c + 1 ..], D and c pairs
+        constexpr int n = KC + 3 + c < 14 ? KC + 3 + c : 14;
+        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fd[c]) : "n"(n));
+        if constexpr (c == 0) mfma_qk_first(dpa, fd[0], vf[0]);
+        else mfma_qk_next(dpa, fd[c], vf[c]);
+        ds_rdtr<qo + (unsigned)hh * 32 * D>(olo[hh][d_], ta.tr[0][d_] + DO_REGION);
+        ds_rdtr<qo + (unsigned)hh * 32 * D>(ohi[hh][d_], ta.tr[1][d_] + DO_REGION);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < PE; ++q) {
@@ -579,17 +616,25 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // dV^T += dO^T P, one MFMA at a time with 16 / (2 DB) elements of dS
-      // formed after each
+      qk_drain(dpa);
+      // dV^T += dO^T P, one MFMA per slot; each slot also issues one pair of
+      // Q^T reads and forms 16 / (2 DB) elements of dS = P (dP - D)
       constexpr int SE = 16 / (2 * DB);
       bf16x8 dsf[2];
       static_for<0, 2 * DB>([&](auto X) {
         constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
-        u32x2 l0 = olo[hh][d_], h0 = ohi[hh][d_];
-        asm volatile("" : "+v"(l0), "+v"(h0));
-        const u32x4 wd = {l0[0], l0[1], h0[0], h0[1]};
+        // dO^T pair x done (and D before it): the reads after it are the
+        // later dO^T pairs and x Q^T pairs
+        constexpr int n = 4 * DB - 2 < 14 ? 4 * DB - 2 : 14;
+        if constexpr (x == 0)
+          asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(olo[hh][d_]), "+v"(ohi[hh][d_]), "+v"(d4[0]), "+v"(d4[1]),
+                       "+v"(d4[2]), "+v"(d4[3]) : "n"(n));
+        else
+          asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(olo[hh][d_]), "+v"(ohi[hh][d_]) : "n"(n));
+        const u32x4 wd = {olo[hh][d_][0], olo[hh][d_][1], ohi[hh][d_][0], ohi[hh][d_][1]};
         mfma_acc1(dva[d_], wd, pf[hh]);
+        ds_rdtr<qo + (unsigned)hh * 32 * D>(qlo[hh][d_], ta.tr[0][d_]);
+        ds_rdtr<qo + (unsigned)hh * 32 * D>(qhi[hh][d_], ta.tr[1][d_]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < SE; ++q) {
@@ -598,32 +643,32 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      // Q^T for the dK product
-      u32x2 qlo[2][DB], qhi[2][DB];
-      static_for<0, 2 * DB>([&](auto X) {
-        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
-        constexpr unsigned off = qo + (unsigned)hh * 32 * D;
-        ds_rdtr<off>(qlo[hh][d_], ta.tr[0][d_]);
-        ds_rdtr<off>(qhi[hh][d_], ta.tr[1][d_]);
-      });
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      // dK^T += Q^T dS in two halves of 16 query rows; between them the next
+      // unit's LSE and Q rows are read (the S products of this unit, which
+      // read fq, are done)
+      static_for<0, 2>([&](auto HH) {
+        constexpr int hh = decltype(HH)::value;
+        // Q^T pairs of this half done: after them come the other half's
+        // pairs (first half) or the next unit's reads (second half)
+        constexpr int n = hh == 0 ? 2 * DB : (v + 1 < NU ? KC + 4 : 0);
+        if constexpr (DB == 4)
+          asm volatile("s_waitcnt lgkmcnt(%8)" : "+v"(qlo[hh][0]), "+v"(qhi[hh][0]), "+v"(qlo[hh][1]),
+                       "+v"(qhi[hh][1]), "+v"(qlo[hh][2]), "+v"(qhi[hh][2]), "+v"(qlo[hh][3]), "+v"(qhi[hh][3])
+                       : "n"(n));
+        else
+          asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(qlo[hh][0]), "+v"(qhi[hh][0]), "+v"(qlo[hh][1]),
+                       "+v"(qhi[hh][1]) : "n"(n));
         u32x4 wq[DB];
 #pragma unroll
-        for (int d_ = 0; d_ < DB; ++d_) {
-          u32x2 l1 = qlo[hh][d_], h1 = qhi[hh][d_];
-          asm volatile("" : "+v"(l1), "+v"(h1));
-          wq[d_] = u32x4{l1[0], l1[1], h1[0], h1[1]};
-        }
+        for (int d_ = 0; d_ < DB; ++d_) wq[d_] = u32x4{qlo[hh][d_][0], qlo[hh][d_][1], qhi[hh][d_][0], qhi[hh][d_][1]};
         if constexpr (DB == 4) {
           mfma_acc4(dka[0], dka[1], dka[2], dka[3], wq[0], wq[1], wq[2], wq[3], dsf[hh]);
         } else {
 #pragma unroll
-          for (int d_ = 0; d_ < DB; ++d_)
-            dka[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq[d_]), dsf[hh], dka[d_], 0, 0, 0);
+          for (int d_ = 0; d_ < DB; ++d_) mfma_acc1(dka[d_], wq[d_], dsf[hh]);
         }
-      }
+        if constexpr (hh == 0 && v + 1 < NU) read_q_l4(ST, std::integral_constant<int, v + 1>{});
+      });
     });
   };
   if (total > 0) issue(0);
@@ -631,6 +676,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     tile(it, std::integral_constant<int, 0>{});
     if (it + 1 < total) tile(it + 1, std::integral_constant<int, 1>{});
   }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int d_ = 0; d_ < DB; ++d_) {
     mfma_acc_drain(dka[d_]);

@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector (the fp32 path is VALU FMA)
 HBM_PEAK_GBS = 8000.0
+WARM_SECONDS = 0.3          # untimed back-to-back launches before the warm-up steps
 LLC_BYTES = 256 << 20       # last-level (Infinity) cache: working sets above it stream from HBM
 DEFAULT_WORKLOAD = "rank7_of_8_bf16_causal"
 METRIC = "rank-share ring-attention TFLOP/s (bf16, causal) and % of MFMA bf16 peak"
@@ -117,11 +118,13 @@ def warm(torch, fn, seconds: float = 0.3):
     """Back-to-back launches for about `seconds`, so that the clocks have
     left the idle state a CPU-side phase (input draws, the oracle) leaves
     them in before anything is timed."""
-    t0 = time.perf_counter()
+    t0, n = time.perf_counter(), 0
     while time.perf_counter() - t0 < seconds:
         for _ in range(5):
             fn()
+        n += 5
         torch.cuda.synchronize()
+    return n
 
 
 def summary(per):
@@ -586,7 +589,11 @@ def main() -> int:
     def step():
         ra.ra_rank_share(qd, kd, vd, w.P, r, w.causal, O, lse)
 
-    log(f"warmup {args.warmup}")
+    # The input draws leave the GPU idle at its lowest clock; untimed
+    # back-to-back steps for WARM_SECONDS bring it to the clock it holds
+    # under this load before the W warm-up steps and the K timed ones.
+    log(f"clock warm-up {WARM_SECONDS} s, then warmup {args.warmup}")
+    warm_launches = warm(torch, step, WARM_SECONDS)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -610,7 +617,11 @@ def main() -> int:
     log(f"{w.name}: {ms_per_step:.3f} ms/step, kernel mean {mean_ms:.3f} ms "
         f"(median {km['median']:.3f}, min {km['min']:.3f}) -> {achieved:.1f} TFLOP/s")
 
-    clock = ClockSampler(torch).sample_during(torch, step, 2.5)
+    if args.no_extras:
+        clock = {"recorded": False, "why": "not sampled with --no-extras (its launches would join a profiler's "
+                                           "per-kernel summary)"}
+    else:
+        clock = ClockSampler(torch).sample_during(torch, step, 2.5)
     if clock.get("recorded"):
         log(f"engine clock under load: median {clock['gfxclk_mhz']['median']} MHz "
             f"({clock['gfxclk_mhz']['min']}..{clock['gfxclk_mhz']['max']})")
@@ -620,7 +631,8 @@ def main() -> int:
     out = {
         "metric": METRIC,
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "clock_warmup": {"seconds": WARM_SECONDS, "launches": warm_launches},
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": w.N,
                    "P": w.P, "rank": r, "causal": w.causal, "q_block": w.nq, "input": w.dist,

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libringattn.so")
-SOURCES = ["ra_api.cpp", "ra_kernels.hip", "ra_bwd.hip", "ra_state.hip"]
+SOURCES = ["ra_api.cpp", "ra_kernels.hip", "ra_f32.hip", "ra_bwd.hip", "ra_state.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

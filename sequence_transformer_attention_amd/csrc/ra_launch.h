@@ -73,9 +73,11 @@ int64_t ra_state_workgroups(int64_t B, int64_t H, int64_t S, int64_t d);
 // Tile shape of the attention kernels (query rows per workgroup, keys per tile).
 constexpr int RA_BF16_BM = 256, RA_BF16_BN = 64;
 constexpr int RA_F32_BM = 64, RA_F32_BN = 64;
-// Threads per workgroup of the attention kernels (the fp32 one: 64 per 64
-// channels of the head dimension, at most 128).
-constexpr int RA_BF16_THREADS = 256, RA_F32_THREADS = 128;
+// Threads per workgroup of the attention kernels.  The fp32 one splits each
+// key tile over RA_F32_KGROUPS groups of 64 threads per 64 channels of the
+// head dimension: ra_f32_threads(d), at most RA_F32_THREADS.
+constexpr int RA_BF16_THREADS = 256, RA_F32_KGROUPS = 4, RA_F32_THREADS = 128 * RA_F32_KGROUPS;
+constexpr int ra_f32_threads(int d) { return 64 * (d / 64) * RA_F32_KGROUPS; }
 
 // Query tiles of a launch: per chunk ceil(rows / BM), times the chunk count.
 inline int64_t ra_query_tiles(const RaAttnArgs& a, int bm) {

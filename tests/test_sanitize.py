@@ -38,7 +38,7 @@ def test_oracle_under_asan_and_ubsan(tmp_path):
                     reason="CPU-only, needs hipcc")
 def test_library_host_code_under_asan_and_ubsan(tmp_path):
     lib = tmp_path / "libringattn_san.so"
-    srcs = [os.path.join(CSRC, f) for f in ("ra_api.cpp", "ra_kernels.hip", "ra_bwd.hip", "ra_state.hip")]
+    srcs = [os.path.join(CSRC, f) for f in ("ra_api.cpp", "ra_kernels.hip", "ra_f32.hip", "ra_bwd.hip", "ra_state.hip")]
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",

@@ -12,8 +12,8 @@
 //      test again;
 //   3. per masked unit and query row, the visible keys: a prefix of
 //      ra_plan_visible_prefix keys.
-// The dK/dV kernel starts its walk over query tiles of 64 rows at
-// ra_plan_first_query_tile.  Every decision must agree bit for bit with
+// The dK/dV kernel starts its walk over query tiles of 128 rows at
+// ra_plan_first_query_tile (checked for tiles of 64 rows too).  Every decision must agree bit for bit with
 // orc_classify / orc_visible_pairs: a tile is walked iff it holds a visible
 // pair; a tile or unit skips the mask only when every pair is visible; the
 // visible prefix counts exactly the visible keys; the query tiles before the
@@ -113,16 +113,16 @@ bool check_forward(int64_t q0, int nq, int64_t k0, int64_t nk, int causal, int w
 }
 
 // The dK/dV walk of a workgroup of keys [kfirst, kfirst + nk) over a query
-// chunk of nqc rows from position qpos, in tiles of BN rows.
-bool check_first_query_tile(int64_t kfirst, int64_t nk, int64_t qpos, int nqc, int causal) {
-  const int ntq = (nqc + BN - 1) / BN;
-  const int t0 = ra_plan_first_query_tile(kfirst, qpos, nqc, BN, causal);
+// chunk of nqc rows from position qpos, in tiles of qt rows.
+bool check_first_query_tile(int64_t kfirst, int64_t nk, int64_t qpos, int nqc, int causal, int qt) {
+  const int ntq = (nqc + qt - 1) / qt;
+  const int t0 = ra_plan_first_query_tile(kfirst, qpos, nqc, qt, causal);
   for (int t = 0; t < ntq; ++t) {
-    const int rows = nqc - t * BN < BN ? nqc - t * BN : BN;
-    const int64_t vis = orc_visible_pairs(qpos + (int64_t)t * BN, rows, kfirst, nk, causal);
+    const int rows = nqc - t * qt < qt ? nqc - t * qt : qt;
+    const int64_t vis = orc_visible_pairs(qpos + (int64_t)t * qt, rows, kfirst, nk, causal);
     ++g_checked;
     if ((t >= t0) != (vis > 0))
-      return fail("query tile walked iff it sees a key of the workgroup", qpos + (int64_t)t * BN, rows, kfirst, nk,
+      return fail("query tile walked iff it sees a key of the workgroup", qpos + (int64_t)t * qt, rows, kfirst, nk,
                   causal, t >= t0, vis);
   }
   return true;
@@ -161,13 +161,14 @@ int main() {
   }
   for (int causal = 0; causal < 2; ++causal)
     for (int64_t qpos : {0, 64, 100, 1000})
-      for (int nqc : {1, 63, 64, 65, 128, 200, 512})
+      for (int nqc : {1, 63, 64, 65, 127, 128, 129, 200, 256, 257, 512})
         for (int64_t dk = -300; dk <= 900; dk += 7)
-          for (int64_t nk : {1, 64, 127, 128}) {
-            const int64_t kfirst = qpos + dk;
-            if (kfirst < 0) continue;
-            if (!check_first_query_tile(kfirst, nk, qpos, nqc, causal)) return 1;
-          }
+          for (int64_t nk : {1, 64, 127, 128})
+            for (int qt : {64, 128}) {
+              const int64_t kfirst = qpos + dk;
+              if (kfirst < 0) continue;
+              if (!check_first_query_tile(kfirst, nk, qpos, nqc, causal, qt)) return 1;
+            }
   std::printf("ok %lld\n", g_checked);
   return 0;
 }

@@ -497,13 +497,13 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
         asm volatile("" : "+v"(sm_tot[rb]));
       }
     };
-    // After the step: redo a row block's unit if any lane asks for it, then add its
-    // row sum.  The redo moves m2 to the exact row max, rescales o and l by
-    // alpha = exp2(m2_old - m2_new) (0 when m2 was -inf) and recomputes p
-    // (0 for rows with no visible key yet).
-    auto sm_fix = [&](auto X, auto R) __attribute__((always_inline)) {
+    // After the step: redo a row block's unit if any lane asks for it (the
+    // row sum is added after, in sm_fix).  The redo moves m2 to the exact row
+    // max, rescales o and l by alpha = exp2(m2_old - m2_new) (0 when m2 was
+    // -inf) and recomputes p (0 for rows with no visible key yet).
+    auto sm_redo = [&](auto X, auto R) __attribute__((always_inline)) {
       constexpr int x = decltype(X)::value, rb = decltype(R)::value;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(sm_tot[rb] <= kRedoSum)) != 0, 0)) {
+      if (__builtin_amdgcn_ballot_w64(!(sm_tot[rb] <= kRedoSum)) != 0) {
         const f32x16& s = sacc[x][rb];
         float mx = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax3(s[6], s[7], s[8]));
         mx = vmax3(mx, vmax3(s[9], s[10], s[11]), vmax3(s[12], s[13], s[14]));
@@ -534,7 +534,17 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
             for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
         }
       }
-      lsum[rb] += sm_tot[rb];
+    };
+    // One test for both row blocks on the common path (a lane's sums in
+    // range); the redo of each row block behind it.
+    auto sm_fix = [&](auto X) __attribute__((always_inline)) {
+      const bool bad = !(sm_tot[0] <= kRedoSum) || !(sm_tot[1] <= kRedoSum);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
+        sm_redo(X, std::integral_constant<int, 0>{});
+        sm_redo(X, std::integral_constant<int, 1>{});
+      }
+      lsum[0] += sm_tot[0];
+      lsum[1] += sm_tot[1];
     };
 
     // MFMAs of a step.  S^T(u+1) of row block rb, k-step c, into sacc[XN][rb];
@@ -608,8 +618,7 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (sm) {
-        sm_fix(X, std::integral_constant<int, 0>{});
-        sm_fix(X, std::integral_constant<int, 1>{});
+        sm_fix(X);
       }
     };
     auto half_valid = [](int nv, int hf) { return ra_plan_half_valid(nv, hf, 32); };

@@ -417,10 +417,11 @@ __device__ __forceinline__ void qk_drain(f32x16& c) { asm volatile("s_nop 7\n\ts
 //   S = Q K^T, dP = dO V^T (8 + 8 MFMAs), P = exp2(S c - LSE log2 e)
 //   under the causal mask, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS
 // with dO^T and Q^T from transposing LDS reads.  The LDS reads are issued
-// ahead of their products: a unit's dO rows before its S products, its dO^T
-// and Q^T before its dP products, the next unit's Q rows and row statistics
-// during this unit's dK products (within a tile), so only the first unit of
-// a tile waits for its Q rows.
+// a phase ahead of their products: a unit's dO rows during its S products,
+// its dO^T during dP, its Q^T during dV, the next unit's Q rows and row
+// statistics during this unit's dK products (within a tile), so only the
+// first unit of a tile waits for its Q rows.  The next tile's direct loads
+// go out once the tile's first product runs (Q rows and statistics first).
 template <int D>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   constexpr int NW = 4, BK = NW * 32, QT = 128, NU = QT / 32, KC = D / 16, DB = D / 32;
@@ -502,25 +503,34 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   };
   WalkCur cl{0, 0}, cc{0, 0};  // load cursor, compute cursor
   float lsv = 0.f, dlv = 0.f;  // threads 0..QT-1: LSE log2(e) and D of row tid of the tile in flight
-  auto issue = [&](int st) __attribute__((always_inline)) {
-    const TileRef tr = tile_ref(cl);
-    walk_next(cl);
-    const int h = tr.h, r0 = tr.r0, nvalid = tr.nvalid;
-    const __bf16* qrow = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss;
-    const __bf16* drow = (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)r0 * a.do_ss;
-#pragma unroll
-    for (int half = 0; half < QT / 64; ++half) {
+  // The loads of tile nx into stage st in four parts: Q rows 0-63 with the
+  // rows' statistics (threads 0 .. QT-1), Q rows 64-127, dO rows 0-63, dO
+  // rows 64-127.
+  TileRef nx{0, 0, 0, 0};
+  auto issue_part = [&](int st, int part) __attribute__((always_inline)) {
+    const int h = nx.h, r0 = nx.r0, nvalid = nx.nvalid;
+    const int half = part & 1;
+    if (part < 2) {
+      const __bf16* qrow = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r0 * a.q_ss;
       load_tile<D, NW>(qrow + (int64_t)(64 * half) * a.q_ss, a.q_ss, nvalid - 64 * half,
                        &smem[st][0] + half * (TILE / 2), wave, lane);
+    } else {
+      const __bf16* drow = (const __bf16*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)r0 * a.do_ss;
       load_tile<D, NW>(drow + (int64_t)(64 * half) * a.do_ss, a.do_ss, nvalid - 64 * half,
                        &smem[2 + st][0] + half * (TILE / 2), wave, lane);
     }
-    if (tid < QT) {
+    if (part == 0 && tid < QT) {
       const int row = r0 + tid;
       const bool ok = tid < nvalid;
       lsv = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e : INFINITY;
       dlv = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
     }
+  };
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    nx = tile_ref(cl);
+    walk_next(cl);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(st, part);
   };
 
   // LDS reads are asm with immediate offsets, issued ahead of their
@@ -556,7 +566,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       lsd[st][1][tid] = dlv;
     }
     __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
-    if (it + 1 < total) issue(st ^ 1);
+    const bool more = it + 1 < total;
+    if (more) {
+      nx = tile_ref(cl);
+      walk_next(cl);
+    }
     read_q_l4(ST, std::integral_constant<int, 0>{});  // the tile's only exposed reads
     static_for<0, NU>([&](auto V) {
       constexpr int v = decltype(V)::value;
@@ -573,8 +587,17 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       bf16x8 fd[KC];
       static_for<0, KC>([&](auto C) {
         constexpr int c = decltype(C)::value;
-        if constexpr (c == 0) mfma_qk_first(sacc, fq[0], kf[0]);
-        else mfma_qk_next(sacc, fq[c], kf[c]);
+        if constexpr (c == 0) {
+          mfma_qk_first(sacc, fq[0], kf[0]);
+          // the next tile's loads, once the tile's first product runs
+          if constexpr (v == 0)
+            if (more) {
+#pragma unroll
+              for (int part = 0; part < 4; ++part) issue_part(st ^ 1, part);
+            }
+        } else {
+          mfma_qk_next(sacc, fq[c], kf[c]);
+        }
         ds_rd128<qo>(fd[c], ta.rd[c] + DO_REGION);
       });
       f32x4 d4[4];

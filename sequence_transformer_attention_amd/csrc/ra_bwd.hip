@@ -19,26 +19,25 @@
 //                     registers as B operands); per 32-key unit of a
 //                     64-key K/V tile staged in LDS:
 //                       S^T = K Q^T, then dP^T = V dO^T (A operands from
-//                       LDS, the V rows read into the registers the K rows
-//                       free), dS^T = P^T (dP^T - D) in fp32, then
+//                       LDS), dS^T = P^T (dP^T - D) in fp32, then
 //                       dQ^T += K^T dS^T with K^T from the transposing
-//                       ds_read_b64_tr_b16 and dS^T from registers.
-//                     252 VGPRs: two workgroups (two waves per SIMD) per CU.
-//   bwd_dkdv_kernel   4 waves x 32 keys (K and V fragments stay in
-//                     registers as B operands); per 32-query unit of a
-//                     64-row Q/dO tile staged in LDS, for every query head
-//                     of the kv head, stage by stage:
+//                       ds_read_b64_tr_b16 and dS^T from registers.  Each
+//                       product phase issues the LDS reads of the next into
+//                       the registers its own MFMAs free (V rows during S^T,
+//                       K^T during dP^T, the next unit's K rows during dQ^T).
+//                     256 VGPRs: two workgroups (two waves per SIMD) per CU.
+//   bwd_dkdv_kernel   4 waves x 32 keys (K and V fragments and the dK, dV
+//                     accumulators in AGPRs for the whole walk: inline-asm
+//                     MFMAs); per 32-query unit of a 128-row Q/dO tile
+//                     staged in LDS, for every query head of the kv head:
 //                       S = Q K^T, then dP = dO V^T (A operands from LDS)
 //                       with P formed between its MFMAs, dV^T += dO^T P
 //                       (dO^T from transposing reads) with dS formed
-//                       between its MFMAs, dK^T += Q^T dS.  One wave per
+//                       between its MFMAs, dK^T += Q^T dS, each phase
+//                       issuing the LDS reads of the next.  One wave per
 //                       SIMD issues both streams: scheduling barriers keep
 //                       the vector work between the MFMAs, where it issues
 //                       while the matrix core runs.
-//                     The dK, dV accumulators stay in AGPRs for the whole
-//                     walk (inline-asm MFMAs; the compiler otherwise copies
-//                     them between register files every iteration); one
-//                     wave per SIMD.
 // Both attention kernels use the forward's LDS layout (rows of 2d bytes,
 // 16-byte slots XOR-swizzled), two LDS stages with the next tile's loads in
 // flight, and inline-asm LDS reads whose waits carry their registers.
@@ -303,6 +302,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
     load_tile<D, NW>(vb + k0 * a.v_ss, a.v_ss, nvalid, &smem[st][1][0], wave, lane);
     cur_next(cl);
   };
+  // K rows of the unit (A operand of S^T), read a unit ahead within a tile
+  bf16x8 fk[KC];
+  auto read_k = [&](auto KO) __attribute__((always_inline)) {
+    static_for<0, KC>([&](auto C) { ds_rd128<decltype(KO)::value>(fk[decltype(C)::value], ta.rd[decltype(C)::value]); });
+  };
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
     const int64_t k0 = cc.k0 + (int64_t)cc.u * BN, left = blk_keys(cc.k0) - (int64_t)cc.u * BN;
@@ -310,40 +314,42 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
     cur_next(cc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
+    read_k(std::integral_constant<unsigned, (unsigned)st * 2 * TILE>{});  // the tile's only exposed reads
     if (it + 1 < total) issue(st ^ 1);
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
       constexpr unsigned ko = (unsigned)st * 2 * TILE + (unsigned)hf * 64 * D;  // K unit; V unit at + TILE
-      // S^T = K Q^T, then dP^T = V dO^T (keys x queries): the V rows are read
-      // while the S^T products run, into the registers the K rows free
-      bf16x8 fk[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) ds_rd128<ko>(fk[c], ta.rd[c]);
+      // Each phase issues the LDS reads of the next, into the registers its
+      // products free: the V rows during the S^T products, K^T during the
+      // dP^T products, the next unit's K rows during the dQ products.
       if constexpr (KC == 8)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]), "+v"(fk[4]),
                      "+v"(fk[5]), "+v"(fk[6]), "+v"(fk[7]));
       else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fk[0]), "+v"(fk[1]), "+v"(fk[2]), "+v"(fk[3]));
+      // S^T = K Q^T (keys x queries)
       f32x16 sacc = f32x16{}, dpa = f32x16{};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], qf[c], sacc, 0, 0, 0);
       bf16x8 fv[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) ds_rd128<ko + TILE>(fv[c], ta.rd[c]);
-      if constexpr (KC == 8)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fv[0]), "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]), "+v"(fv[4]),
-                     "+v"(fv[5]), "+v"(fv[6]), "+v"(fv[7]));
-      else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fv[0]), "+v"(fv[1]), "+v"(fv[2]), "+v"(fv[3]));
-#pragma unroll
-      for (int c = 0; c < KC; ++c) dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c], dof[c], dpa, 0, 0, 0);
-      // K^T for the dQ product, in flight while P^T and dS^T are formed
+      static_for<0, KC>([&](auto C) {
+        constexpr int c = decltype(C)::value;
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], qf[c], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        ds_rd128<ko + TILE>(fv[c], ta.rd[c]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // dP^T = V dO^T
       u32x2 tlo[2][DB], thi[2][DB];
-      static_for<0, 2 * DB>([&](auto X) {
-        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
+      static_for<0, KC>([&](auto C) {
+        constexpr int c = decltype(C)::value, hh = c / DB, d_ = c % DB;
+        // fv[c] done: the reads after it are fv[c + 1 ..] and c pairs of K^T
+        constexpr int n = KC - 1 + c < 14 ? KC - 1 + c : 14;
+        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fv[c]) : "n"(n));
+        dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c], dof[c], dpa, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         constexpr unsigned off = ko + (unsigned)hh * 32 * D;
         ds_rdtr<off>(tlo[hh][d_], ta.tr[0][d_]);
         ds_rdtr<off>(thi[hh][d_], ta.tr[1][d_]);
+        __builtin_amdgcn_sched_barrier(0);
       });
       // key index of register r: 8 (r / 4) + (r % 4) + 4 lg; keys below lim are visible
       const int nv = ra_plan_half_valid(nvalid, hf, 32);
@@ -366,16 +372,20 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(RaBwdArgs a) {
           dsf[r >> 3][r & 7] = (__bf16)(p * (dpa[r] - dlt));
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int d_ = 0; d_ < DB; ++d_) {
-          u32x2 l0 = tlo[hh][d_], h0 = thi[hh][d_];
-          asm volatile("" : "+v"(l0), "+v"(h0));
-          const u32x4 w = {l0[0], l0[1], h0[0], h0[1]};
-          dqa[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), dsf[hh], dqa[d_], 0, 0, 0);
-        }
+      // dQ^T += K^T dS^T
+      static_for<0, 2 * DB>([&](auto X) {
+        constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
+        // K^T pair x done: the reads after it are the later pairs and the x
+        // next K rows issued so far
+        constexpr int pend = 2 * (2 * DB - 1 - x) + (hf == 0 ? x : 0);
+        constexpr int n = pend < 14 ? pend : 14;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(tlo[hh][d_]), "+v"(thi[hh][d_]) : "n"(n));
+        const u32x4 w = {tlo[hh][d_][0], tlo[hh][d_][1], thi[hh][d_][0], thi[hh][d_][1]};
+        dqa[d_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), dsf[hh], dqa[d_], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (hf == 0 && x < KC) ds_rd128<ko + 64 * D>(fk[x], ta.rd[x]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     });
   };
   if (total > 0) issue(0);

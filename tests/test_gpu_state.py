@@ -55,8 +55,10 @@ def _flat(o, m, l):
 
 
 @pytest.mark.parametrize("B,S,H,d,bhsd", [
-    (1, 100, 3, 128, False),    # ragged row blocks (32 rows per workgroup at d = 128)
-    (2, 33, 2, 64, False),      # d = 64 (64 rows per workgroup), B = 2
+    (1, 100, 3, 128, False),    # ragged one-head blocks (64 rows per workgroup at d = 128)
+    (2, 33, 2, 64, False),      # d = 64 (128 rows per workgroup), B = 2
+    (2, 37, 16, 128, False),    # 8-head blocks (8 heads x 8 rows at d = 128), ragged, B = 2
+    (1, 45, 8, 64, False),      # 8-head blocks at d = 64 (8 heads x 16 rows)
     (1, 4096, 4, 128, True),    # strided views of both states
     (1, 1, 1, 64, False),       # a single row
 ])
@@ -80,8 +82,9 @@ def test_merge_matches_the_oracle(B, S, H, d, bhsd):
     assert np.array_equal(ob2, _flat(ob, mb, lb)[2])
 
 
-def test_merge_with_the_empty_state_is_the_identity():
-    B, S, H, d = 1, 257, 2, 128
+@pytest.mark.parametrize("S,H,d", [(257, 2, 128), (37, 16, 128), (45, 8, 64)])
+def test_merge_with_the_empty_state_is_the_identity(S, H, d):
+    B = 1
     (oa, ma, la), (oad, mad, lad) = _state(B, S, H, d, seed=5)
     e_o = torch.full((B, S, H, d), float("nan"), device=DEV)
     e_m = torch.full((B, H, S), float("nan"), device=DEV)
@@ -130,6 +133,9 @@ def test_two_ring_halves_merged_equal_the_share(dt):
     (100, 3, 128, torch.bfloat16, False),
     (33, 2, 64, torch.float32, False),
     (300, 2, 128, None, True),          # O written over o_acc
+    (37, 16, 128, torch.bfloat16, False),  # 8-head blocks, ragged
+    (45, 8, 64, torch.float32, False),
+    (21, 8, 128, None, True),
 ])
 def test_finalize_matches_the_oracle(S, H, d, o_dtype, in_place):
     say(f"ra_finalize S{S} H{H} d{d} out {o_dtype} in_place={in_place}")

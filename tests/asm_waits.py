@@ -16,6 +16,17 @@ kernels wait for every read before their barriers and loop heads, so no
 read is outstanding across a branch.  Scalar loads also count in lgkmcnt
 and can complete out of order; they only make a wait stricter and are not
 tracked.
+
+The kernels' matrix products are inline asm too, so the compiler does not
+space other instructions from them either; the kernels do it with s_nop.
+Two more walks check that spacing against what the compiler keeps for its
+own gfx950 MFMAs (read off its output): at least 12 wait states between an
+MFMA and any non-MFMA instruction that reads or writes its result, or an
+MFMA that takes it as a multiplicand (a product accumulating into it needs
+none), and at least 2 between a vector instruction and an MFMA that reads
+the register it wrote.  A wait state is one instruction, or n + 1 for
+s_nop n; an MFMA in between counts as one, which understates the time it
+takes, so the walks err on the strict side.
 """
 from __future__ import annotations
 
@@ -75,3 +86,52 @@ def check(lines: list) -> tuple:
                 bad.append((i, "uses a pending read", t))
                 break
     return nreads, nwaits, bad
+
+
+def _walk(lines):
+    """(line index, opcode, operand list, text) of every instruction."""
+    for i, line in enumerate(lines):
+        t = line.split(";")[0].strip()
+        if not t or t.startswith(".") or t.endswith(":"):
+            continue
+        op = t.split()[0]
+        rest = t[len(op):].strip()
+        yield i, op, ([x.strip() for x in rest.split(",")] if rest else []), t
+
+
+def _ws(op, ops):
+    return int(ops[0], 0) + 1 if op == "s_nop" else 1
+
+
+def check_mfma_results(lines: list, need: int = 12) -> list:
+    """Instructions that touch an MFMA's result fewer than `need` wait
+    states after it (an MFMA accumulating into it excepted)."""
+    pend, bad = [], []  # (result registers, wait states since, line)
+    for i, op, ops, t in _walk(lines):
+        if op.startswith("v_mfma"):
+            ab = _regs(ops[1]) | _regs(ops[2])
+            bad += [(i, w, t) for d, w, _ in pend if ab & d]
+        elif op != "s_nop":
+            used = set().union(*(_regs(x) for x in ops)) if ops else set()
+            bad += [(i, w, t) for d, w, _ in pend if used & d]
+        n = _ws(op, ops)
+        pend = [(d, w + n, l) for d, w, l in pend if w + n < need]
+        if op.startswith("v_mfma"):
+            pend.append((_regs(ops[0]), 0, i))
+    return bad
+
+
+def check_mfma_operands(lines: list, need: int = 2) -> list:
+    """MFMAs that read a register a vector instruction wrote fewer than
+    `need` wait states before."""
+    pend, bad = [], []
+    for i, op, ops, t in _walk(lines):
+        if op.startswith("v_mfma"):
+            src = set().union(*(_regs(x) for x in ops[1:4]))
+            bad += [(i, w, t) for d, w, _ in pend if src & d]
+        n = _ws(op, ops)
+        pend = [(d, w + n, l) for d, w, l in pend if w + n < need]
+        if (op.startswith("v_") and not op.startswith(("v_mfma", "v_cmp", "v_readlane", "v_readfirstlane"))
+                and ops):
+            pend.append((_regs(ops[0]), 0, i))
+    return bad

@@ -1,7 +1,9 @@
 """The inline-asm LDS reads of the bf16 forward and the backward kernels are
-waited for before their registers are used (tests/asm_waits.py), checked
-in the gfx950 assembly the build flags produce; a weakened wait in a copy
-of the backward source is caught."""
+waited for before their registers are used, and their inline-asm matrix
+products are spaced from the instructions around them (tests/asm_waits.py),
+checked in the gfx950 assembly the build flags produce; a weakened wait and
+a missing drain in copies of the sources are caught, and the spacing walks
+are checked on short sequences."""
 import os
 import shutil
 import subprocess
@@ -58,3 +60,53 @@ def test_a_weakened_wait_is_caught(tmp_path):
     asm = device_asm(str(mutant), str(tmp_path / "m.s"))
     _, _, bad = asm_waits.check(asm_waits.kernel_lines(asm, KERNELS["ra_bwd.hip"][0]))
     assert bad
+
+
+@pytest.mark.parametrize("source", sorted(KERNELS))
+def test_matrix_products_are_spaced(source, tmp_path):
+    asm = device_asm(os.path.join(CSRC, source), str(tmp_path / "k.s"))
+    for sym in KERNELS[source]:
+        lines = asm_waits.kernel_lines(asm, sym)
+        assert "v_mfma" in "\n".join(lines), sym
+        bad = asm_waits.check_mfma_results(lines)
+        assert not bad, (sym, bad[:5])
+        bad = asm_waits.check_mfma_operands(lines)
+        assert not bad, (sym, bad[:5])
+
+
+def mutant_asm(tmp_path, source: str, tag: str, repl: str) -> str:
+    with open(os.path.join(CSRC, source)) as f:
+        src = f.read()
+    assert src.count(tag) == 1
+    (tmp_path / source).write_text(src.replace(tag, repl))
+    for h in ("ra_bwd.h", "ra_plan.h", "ra_launch.h"):
+        if os.path.exists(os.path.join(CSRC, h)):
+            shutil.copy(os.path.join(CSRC, h), tmp_path / h)
+    return device_asm(str(tmp_path / source), str(tmp_path / "m.s"))
+
+
+def test_a_missing_drain_is_caught(tmp_path):
+    # the backward's drain between the S and dP chains and the vector code
+    # that reads their results, emptied in a copy of the source
+    asm = mutant_asm(tmp_path, "ra_bwd.hip",
+                     'void qk_drain(f32x16& c) { asm volatile("s_nop 7\\n\\ts_nop 7" : "+v"(c)); }',
+                     'void qk_drain(f32x16& c) { asm volatile("" : "+v"(c)); }')
+    assert any(asm_waits.check_mfma_results(asm_waits.kernel_lines(asm, sym)) for sym in KERNELS["ra_bwd.hip"])
+
+
+def test_the_spacing_walks_on_short_sequences():
+    # a vector write right before an MFMA that reads it, then spaced; an MFMA
+    # result read 5 and 12 wait states later; an accumulating MFMA right after
+    # (allowed).  (The compiler itself puts an s_nop 0 in front of an asm
+    # MFMA after a vector write, so no source change of the kernels shows
+    # the first case.)
+    close = ["v_cvt_pk_bf16_f32 v26, v26, v46", "s_waitcnt lgkmcnt(8)",
+             "v_mfma_f32_32x32x16_bf16 a[64:79], v[34:37], v[24:27], a[64:79]"]
+    assert asm_waits.check_mfma_operands(close)
+    assert not asm_waits.check_mfma_operands(close[:2] + ["s_nop 0"] + close[2:])
+    prod = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0"]
+    read = ["v_add_f32_e32 v30, v3, v31"]
+    assert asm_waits.check_mfma_results(prod + ["s_nop 3"] + read)
+    assert not asm_waits.check_mfma_results(prod + ["s_nop 7", "s_nop 3"] + read)
+    assert not asm_waits.check_mfma_results(prod + ["v_mfma_f32_32x32x16_bf16 v[0:15], v[24:27], v[20:23], v[0:15]"])
+    assert asm_waits.check_mfma_results(prod + ["v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], v[20:23], 0"])

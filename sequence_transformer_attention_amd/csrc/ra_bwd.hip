@@ -455,17 +455,21 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // no query and get zero gradients
   const bool k_live = my_k < a.kv_end;
 
-  bf16x8 kf[KC], vf[KC];  // lane: key my_k, elements 16c + 8lg .. +7 (AGPRs from here on)
+  // lane: key my_k, elements 16c + 8lg .. +7, in AGPRs once all loads are
+  // out (one wait, not one per load).  A key past the key end reads the
+  // first key: its P is masked to 0, so it reaches nothing.
+  bf16x8 kf[KC], vf[KC];
   {
     const int64_t row = k_live ? my_k : 0;
     const __bf16* kp = (const __bf16*)a.k + (int64_t)b * a.k_sb + row * a.k_ss + (int64_t)g * a.k_sh + 8 * lg;
     const __bf16* vp = (const __bf16*)a.v + (int64_t)b * a.v_sb + row * a.v_ss + (int64_t)g * a.v_sh + 8 * lg;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      kf[c] = k_live ? *(const bf16x8*)(kp + 16 * c) : bf16x8{};
-      vf[c] = k_live ? *(const bf16x8*)(vp + 16 * c) : bf16x8{};
-      asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
+      kf[c] = *(const bf16x8*)(kp + 16 * c);
+      vf[c] = *(const bf16x8*)(vp + 16 * c);
     }
+#pragma unroll
+    for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
   }
   f32x16 dka[DB], dva[DB];
 #pragma unroll

@@ -179,18 +179,16 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
   }
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[my_q[rb]][16c + 8lg .. +7].
+  // Rows past the block read the tensor's first row: finite, and never
+  // stored.  The loads all go out here, with no wait between them; the
+  // fragments are pinned to AGPRs once the prologue's tile loads are out too.
   bf16x8 qf[RB][KC];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)(q_ok[rb] ? my_q[rb] : 0) * a.q_ss +
                        (int64_t)h * a.q_sh + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (q_ok[rb]) w = *(const u32x4*)(qp + 16 * c);
-      qf[rb][c] = __builtin_bit_cast(bf16x8, w);
-      asm volatile("" : "+a"(qf[rb][c]));  // from here on the fragment lives in AGPRs
-    }
+    for (int c = 0; c < KC; ++c) qf[rb][c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * c));
   }
 
   // Running state per row block.  o[rb][db][r] = O^T[32db + 8(r/4) + 4lg +
@@ -204,8 +202,9 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     lsum[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[rb][db] = f32x16{};
-    if (a.state_in && q_ok[rb]) {
-      const float* op = a.oacc + (int64_t)b * a.oa_sb + (int64_t)my_q[rb] * a.oa_ss + (int64_t)h * a.oa_sh;
+    if (a.state_in) {  // rows past the block read the first row's state: never stored
+      const int64_t row = q_ok[rb] ? my_q[rb] : 0;
+      const float* op = a.oacc + (int64_t)b * a.oa_sb + row * a.oa_ss + (int64_t)h * a.oa_sh;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -214,12 +213,21 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[rb][db][4 * j + i] = x[i];
         }
-      const float mv = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + (int64_t)my_q[rb] * a.m_ss];
-      const float lv = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + (int64_t)my_q[rb] * a.l_ss];
-      m2[rb] = mv * kLog2e;  // -inf stays -inf
-      lsum[rb] = lg == 0 ? lv : 0.f;
+      // as stored (natural log units, the whole sum); state_units converts
+      // them once the tile loads are out, so that nothing waits for them here
+      m2[rb] = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + row * a.m_ss];
+      lsum[rb] = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + row * a.l_ss];
     }
   }
+  auto state_units = [&]() __attribute__((always_inline)) {
+    if (a.state_in) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        m2[rb] *= kLog2e;  // -inf stays -inf
+        lsum[rb] = lg == 0 ? lsum[rb] : 0.f;
+      }
+    }
+  };
   // The accumulators are read by vector code (a redo, the epilogue) only
   // after this: 16 wait states after the last MFMA that wrote them.
   auto ofrag_drain = [&o]() __attribute__((always_inline)) {
@@ -651,6 +659,11 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
 #pragma unroll
       for (int i = 0; i < per; ++i) *(u32x4*)(&smem[7][0] + (i * NW * 64 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(qf[rb][c]));  // from here on the fragments live in AGPRs
+    state_units();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     kread(uoff(integral_constant<int, 0>{}, H0));
@@ -710,6 +723,8 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     step(X0, F, T, F, F, uoff(integral_constant<int, 0>{}, H1), (unsigned)((n - 1) & 3) * TILE_BYTES,
          uoff(integral_constant<int, 0>{}, H0), [](auto) {});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    state_units();  // no tile: the state goes back as it came
   }
 
   // Epilogue, per row block: the two halves of each row sum live in lanes

@@ -213,21 +213,12 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[rb][db][4 * j + i] = x[i];
         }
-      // as stored (natural log units, the whole sum); state_units converts
-      // them once the tile loads are out, so that nothing waits for them here
-      m2[rb] = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + row * a.m_ss];
-      lsum[rb] = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + row * a.l_ss];
+      const float mv = a.m[(int64_t)b * a.m_sb + (int64_t)h * a.m_sh + row * a.m_ss];
+      const float lv = a.l[(int64_t)b * a.l_sb + (int64_t)h * a.l_sh + row * a.l_ss];
+      m2[rb] = mv * kLog2e;  // -inf stays -inf
+      lsum[rb] = lg == 0 ? lv : 0.f;
     }
   }
-  auto state_units = [&]() __attribute__((always_inline)) {
-    if (a.state_in) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        m2[rb] *= kLog2e;  // -inf stays -inf
-        lsum[rb] = lg == 0 ? lsum[rb] : 0.f;
-      }
-    }
-  };
   // The accumulators are read by vector code (a redo, the epilogue) only
   // after this: 16 wait states after the last MFMA that wrote them.
   auto ofrag_drain = [&o]() __attribute__((always_inline)) {
@@ -663,7 +654,6 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(qf[rb][c]));  // from here on the fragments live in AGPRs
-    state_units();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     kread(uoff(integral_constant<int, 0>{}, H0));
@@ -723,8 +713,6 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     step(X0, F, T, F, F, uoff(integral_constant<int, 0>{}, H1), (unsigned)((n - 1) & 3) * TILE_BYTES,
          uoff(integral_constant<int, 0>{}, H0), [](auto) {});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    state_units();  // no tile: the state goes back as it came
   }
 
   // Epilogue, per row block: the two halves of each row sum live in lanes

@@ -455,9 +455,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // no query and get zero gradients
   const bool k_live = my_k < a.kv_end;
 
-  // lane: key my_k, elements 16c + 8lg .. +7, in AGPRs once all loads are
-  // out (one wait, not one per load).  A key past the key end reads the
-  // first key: its P is masked to 0, so it reaches nothing.
+  // lane: key my_k, elements 16c + 8lg .. +7, in AGPRs once these loads and
+  // the first tile's are out (one wait, not one per load).  A key past the
+  // key end reads the first key: its P is masked to 0, so it reaches nothing.
   bf16x8 kf[KC], vf[KC];
   {
     const int64_t row = k_live ? my_k : 0;
@@ -468,8 +468,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       kf[c] = *(const bf16x8*)(kp + 16 * c);
       vf[c] = *(const bf16x8*)(vp + 16 * c);
     }
-#pragma unroll
-    for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
   }
   f32x16 dka[DB], dva[DB];
 #pragma unroll
@@ -516,7 +514,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     }
   };
   WalkCur cl{0, 0}, cc{0, 0};  // load cursor, compute cursor
-  float lsv = 0.f, dlv = 0.f;  // threads 0..QT-1: LSE log2(e) and D of row tid of the tile in flight
+  // threads 0..QT-1: LSE and D of row tid of the tile in flight as loaded,
+  // and whether the row exists; they are scaled and selected only when the
+  // tile's statistics go to LDS (after the wait for the tile's loads), so
+  // that issuing the loads waits for nothing
+  float lsv = 0.f, dlv = 0.f;
+  bool lok = false;
   // The loads of tile nx into stage st in four parts: Q rows 0-63 with the
   // rows' statistics (threads 0 .. QT-1), Q rows 64-127, dO rows 0-63, dO
   // rows 64-127.
@@ -534,10 +537,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
                        &smem[2 + st][0] + half * (TILE / 2), wave, lane);
     }
     if (part == 0 && tid < QT) {
-      const int row = r0 + tid;
-      const bool ok = tid < nvalid;
-      lsv = ok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] * kLog2e : INFINITY;
-      dlv = ok ? a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss] : 0.f;
+      lok = tid < nvalid;
+      const int row = r0 + (lok ? tid : 0);  // a tile has at least one row
+      lsv = a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss];
+      dlv = a.delta[(int64_t)b * a.de_sb + (int64_t)h * a.de_sh + (int64_t)row * a.de_ss];
     }
   };
   auto issue = [&](int st) __attribute__((always_inline)) {
@@ -576,8 +579,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     const int rel = rel64 < -(1 << 30) ? -(1 << 30) : (int)rel64;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (tid < QT) {
-      lsd[st][0][tid] = lsv;
-      lsd[st][1][tid] = dlv;
+      lsd[st][0][tid] = lok ? lsv * kLog2e : INFINITY;  // rows past the chunk: P = 0
+      lsd[st][1][tid] = lok ? dlv : 0.f;
     }
     __syncthreads();  // publishes stage st; every wave is done with stage st ^ 1
     const bool more = it + 1 < total;
@@ -709,6 +712,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     });
   };
   if (total > 0) issue(0);
+#pragma unroll
+  for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
   for (int it = 0; it < total; it += 2) {
     tile(it, std::integral_constant<int, 0>{});
     if (it + 1 < total) tile(it + 1, std::integral_constant<int, 1>{});

@@ -135,15 +135,14 @@ __device__ __forceinline__ bf16x8 read_tr(unsigned lo_addr, unsigned hi_addr, un
 }
 
 // acc[i] += A_i * B (v_mfma_f32_32x32x16_bf16, i = 0..3) with the
-// accumulators pinned to AGPRs.  Inline asm, so the compiler cannot insert
-// the wait states an MFMA needs after a vector write of its operands: the
-// leading s_nop gives them (A and B may have just been formed by VALU
-// instructions; gfx950 needs 2, as the compiler spaces its own MFMAs).  Only
-// other MFMAs of this form touch the accumulators until mfma_acc_drain.
+// accumulators pinned to AGPRs.  An MFMA needs 2 wait states after a vector
+// write of its operands (gfx950, as the compiler spaces its own MFMAs); the
+// compiler spaces an asm statement from the vector writes before it, which
+// the tests check in the assembly.  Only other MFMAs of this form touch the
+// accumulators until mfma_acc_drain.
 __device__ __forceinline__ void mfma_acc4(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3, const u32x4& a0,
                                           const u32x4& a1, const u32x4& a2, const u32x4& a3, const bf16x8& b) {
   asm volatile(
-      "s_nop 1\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
       "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
       "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
@@ -154,13 +153,13 @@ __device__ __forceinline__ void mfma_acc4(f32x16& c0, f32x16& c1, f32x16& c2, f3
 // acc += A * B, one v_mfma_f32_32x32x16_bf16 with the accumulator pinned to
 // AGPRs (as mfma_acc4, for interleaving with vector work).
 __device__ __forceinline__ void mfma_acc1(f32x16& c, const u32x4& A, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(A), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(A), "v"(b));
 }
 // Zero an accumulator with an MFMA (zero operands, inline-constant C), so
 // that it is born in AGPRs.
 __device__ __forceinline__ void mfma_acc_zero(f32x16& c) {
   const bf16x8 z = bf16x8{};
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(c) : "v"(z));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(c) : "v"(z));
 }
 // Wait until the MFMAs writing the accumulators are done before anything
 // else reads them (the compiler gives a vector read of an 8-pass MFMA's

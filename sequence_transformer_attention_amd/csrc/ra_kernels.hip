@@ -114,18 +114,20 @@ struct TileCursor {
 // The MFMAs of attn_bf16_w64_kernel, inline asm so that the operands sit in
 // the register file the kernel needs them in (the builtins leave that to the
 // compiler, which then runs out of VGPRs and copies between the files).
-// The compiler does not see the wait states around inline-asm MFMAs (gfx950,
-// as the compiler itself spaces its own MFMAs: 2 after a vector write of an
-// operand, none between dependent products, 12 before a vector read of a
-// result):
-//   - after a vector write of an operand: the P V product's leading s_nop 1
-//     (its A operand may have just been assembled by vector moves, its C may
-//     have just been rescaled); the S^T product's operands come from LDS
-//     reads (waited for) and from the Q fragments, written once before the
-//     first product, which has its own s_nop;
+// The wait states around them (gfx950, as the compiler spaces its own
+// MFMAs: 2 after a vector write of an operand, none between dependent
+// products, 12 before a vector read of a result):
+//   - after a vector write of an operand: none is needed where the products
+//     sit (P is written a step before its product, the V^T and K fragments
+//     come from LDS reads, the Q fragments are written once before the first
+//     product, which has its own s_nop, and a redo's rescale of O comes
+//     eight slots before the next P V product); the compiler also spaces an
+//     asm statement from vector writes before it.  A leading s_nop 1 on the
+//     P V product cost 3 % of the kernel's cycles;
 //   - before a vector read of a result: the kernel's drains (16 wait
 //     states), and otherwise whole pipeline slots between the write and the
 //     read.
+// Both are checked in the kernel's assembly by the tests.
 // S^T (keys x queries) = K Q^T, k-step 0 (C = 0) and later k-steps; the
 // accumulator in VGPRs, the Q fragment (B) in AGPRs.
 __device__ __forceinline__ void mfma_s_first(f32x16& c, const bf16x8& k, const bf16x8& q) {
@@ -136,7 +138,7 @@ __device__ __forceinline__ void mfma_s_next(f32x16& c, const bf16x8& k, const bf
 }
 // O^T += V^T P^T with the accumulator pinned to AGPRs.
 __device__ __forceinline__ void mfma_pv(f32x16& c, const bf16x8& A, const bf16x8& B) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(A), "v"(B));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(A), "v"(B));
 }
 
 template <int D>

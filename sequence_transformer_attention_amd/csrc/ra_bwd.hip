@@ -591,12 +591,16 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     static_for<0, NU>([&](auto V) {
       constexpr int v = decltype(V)::value;
       constexpr unsigned qo = (unsigned)st * TILE + (unsigned)v * 64 * D;  // unit v; dO at + DO_REGION
+      // Only the asm products read the Q and dO fragments, and volatile asm
+      // keeps its order, so the waits take them as inputs: as outputs the
+      // compiler counts the wait as a vector write and puts an s_nop before
+      // the next product.  l4 feeds compiled arithmetic and stays an output.
       if constexpr (KC == 8)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(fq[4]),
-                     "+v"(fq[5]), "+v"(fq[6]), "+v"(fq[7]), "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3])
+                     : "v"(fq[0]), "v"(fq[1]), "v"(fq[2]), "v"(fq[3]), "v"(fq[4]), "v"(fq[5]), "v"(fq[6]), "v"(fq[7]));
       else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fq[0]), "+v"(fq[1]), "+v"(fq[2]), "+v"(fq[3]), "+v"(l4[0]),
-                     "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3]));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3])
+                     : "v"(fq[0]), "v"(fq[1]), "v"(fq[2]), "v"(fq[3]));
       // S = Q K^T (query row of register r: 8 (r / 4) + 4 lg + (r % 4)),
       // with the dO rows read one per product, then D of the rows
       f32x16 sacc;
@@ -639,7 +643,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         constexpr int c = decltype(C)::value, hh = c / DB, d_ = c % DB;
         // fd[c] done: the reads after it are fd[c + 1 ..], D and c pairs
         constexpr int n = KC + 3 + c < 14 ? KC + 3 + c : 14;
-        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fd[c]) : "n"(n));
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(fd[c]));
         if constexpr (c == 0) mfma_qk_first(dpa, fd[0], vf[0]);
         else mfma_qk_next(dpa, fd[c], vf[c]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(olo[hh][d_], ta.tr[0][d_] + DO_REGION);

@@ -483,6 +483,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // rows that see any key of the workgroup (under causal masking those at
   // positions >= the first key's, per query chunk), as in the 64-row form.
   const int64_t kfirst = (int64_t)kt * BK;
+  const int64_t wave_klast = kfirst + wave * 32 + 31;  // the wave's last key
   const int nqc = a.nsplit == 2 ? (int)a.qc : a.nq;
   const int ntq = (nqc + QT - 1) / QT;  // tiles per chunk
   auto first_tile = [&](int64_t qpos) -> int { return ra_plan_first_query_tile(kfirst, qpos, nqc, QT, a.causal); };
@@ -651,14 +652,29 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < PE; ++q) {
-          const int r = PE * c + q, e = 8 * (r >> 2) + (r & 3);
-          float t = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);
-          asm volatile("" : "+v"(t));  // computed for every lane: no branch
-          pv[r] = e >= lo ? t : 0.f;
+          const int r = PE * c + q;
+          pv[r] = __builtin_amdgcn_exp2f(sacc[r] * a.c - l4[r >> 2][r & 3]);
           pf[r >> 3][r & 7] = (__bf16)pv[r];
+          // packed here, among the products (not sunk past the mask below)
+          if ((r & 7) == 7) asm volatile("" : "+v"(pf[r >> 3]));
         }
         __builtin_amdgcn_sched_barrier(0);
       });
+      // P above is formed without the mask (a term the mask drops may be
+      // inf: the select below discards it).  The mask is applied only where
+      // some element needs it: a query of the unit before a key of the wave,
+      // or a key of the wave past the key end (the units on the diagonal, or
+      // at the sequence's end).  Done for every unit, the test and select
+      // took about a tenth of the kernel's time; here the other units pass
+      // by on one branch on a wave-uniform value.
+      if (!(wave_klast < a.kv_end && (!a.causal || wave_klast <= qp0 + 32 * v))) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = 8 * (r >> 2) + (r & 3);
+          pv[r] = e >= lo ? pv[r] : 0.f;
+          pf[r >> 3][r & 7] = (__bf16)pv[r];
+        }
+      }
       qk_drain(dpa);
       // dV^T += dO^T P, one MFMA per slot; each slot also issues one pair of
       // Q^T reads and forms 16 / (2 DB) elements of dS = P (dP - D)

@@ -11,11 +11,14 @@ reports every instruction that reads or writes a register that an
 outstanding read has yet to write (a missing or too loose wait), or that
 uses a pending register as an LDS address.
 
-The walk is straight-line (labels and branches are not followed); the
-kernels wait for every read before their barriers and loop heads, so no
-read is outstanding across a branch.  Scalar loads also count in lgkmcnt
-and can complete out of order; they only make a wait stricter and are not
-tracked.
+The walks follow the branches: the state at a label merges the states of
+the fall-through and of every branch to it (a backward branch's on a
+further pass over the kernel, until the states stop changing).  A merge
+errs on the strict side: of the outstanding reads it keeps the longer
+queue, each position (counted from the newest read) with the registers of
+every path, and of the products every pending result with its shortest
+distance.  Scalar loads also count in lgkmcnt and can complete out of
+order; they only make a wait stricter and are not tracked.
 
 The kernels' matrix products are inline asm too, so the compiler does not
 space other instructions from them either; the kernels do it with s_nop.
@@ -51,24 +54,104 @@ def kernel_lines(asm: str, symbol: str) -> list:
     return asm[a:b].splitlines()
 
 
-def check(lines: list) -> tuple:
-    """Returns (LDS reads, lgkmcnt waits, list of violations)."""
-    queue, bad, nreads, nwaits = [], [], 0, 0
+_LABEL = re.compile(r"^(\.L\w+):")
+
+
+def _parse(lines):
+    """('label', name) or ('inst', line index, opcode, operands, text) items."""
+    out = []
     for i, line in enumerate(lines):
         t = line.split(";")[0].strip()
-        if not t or t.startswith(".") or t.endswith(":"):
+        if not t:
+            continue
+        m = _LABEL.match(t)
+        if m:
+            out.append(("label", m.group(1)))
+            continue
+        if t.startswith(".") or t.endswith(":"):
             continue
         op = t.split()[0]
         rest = t[len(op):].strip()
-        ops = [x.strip() for x in rest.split(",")] if rest else []
+        out.append(("inst", i, op, [x.strip() for x in rest.split(",")] if rest else [], t))
+    return out
+
+
+def _flow(lines, init, step, merge, passes=40):
+    """Runs step(state, i, op, ops, text, bad) over the instructions in
+    program order along the branches; returns the violations step reported
+    on the last pass.  States are immutable values."""
+    items = _parse(lines)
+    back = {}
+    for _ in range(passes):
+        bad, incoming, seen, new_back, state = [], {}, set(), {}, init
+        for it in items:
+            if it[0] == "label":
+                lab = it[1]
+                seen.add(lab)
+                ins = incoming.pop(lab, [])
+                if state is not None:
+                    ins.append(state)
+                if lab in back:
+                    ins.append(back[lab])
+                state = merge(ins) if ins else None
+                continue
+            _, i, op, ops, t = it
+            if state is None:  # reached only by a backward branch: known from the pass before
+                state = init
+            state = step(state, i, op, ops, t, bad)
+            if op == "s_branch" or op.startswith("s_cbranch"):
+                tgt = ops[0]
+                if tgt in seen:
+                    new_back[tgt] = merge([new_back[tgt], state]) if tgt in new_back else state
+                else:
+                    incoming.setdefault(tgt, []).append(state)
+                if op == "s_branch":
+                    state = None
+            elif op == "s_endpgm":
+                state = None
+        if new_back == back:
+            return bad
+        back = new_back
+    raise AssertionError("branch states did not settle")
+
+
+_QMAX = 16
+
+
+def _cap(q):
+    """At most _QMAX entries (a loop that never waits grows its queue every
+    pass): the oldest entry joins the next one, which retires later."""
+    while len(q) > _QMAX:
+        q = (q[0] | q[1],) + q[2:]
+    return q
+
+
+def _merge_queues(qs):
+    n = max(len(q) for q in qs)
+    return _cap(tuple(frozenset().union(*(q[len(q) - n + k] for q in qs if len(q) - n + k >= 0)) for k in range(n)))
+
+
+def _merge_pending(ps):
+    best = {}
+    for p in ps:
+        for d, w in p:
+            best[d] = min(w, best.get(d, w))
+    return tuple(sorted(best.items(), key=lambda x: (x[1], sorted(x[0]))))
+
+
+def check(lines: list) -> tuple:
+    """Returns (LDS reads, lgkmcnt waits, list of violations)."""
+    count = {"reads": set(), "waits": set()}
+
+    def step(queue, i, op, ops, t, bad):
         if op == "s_waitcnt":
             m = re.search(r"lgkmcnt\((\d+)\)", t)
             if m:
-                nwaits += 1
+                count["waits"].add(i)
                 n = int(m.group(1))
-                while len(queue) > n:
-                    queue.pop(0)
-            continue
+                if len(queue) > n:
+                    queue = queue[len(queue) - n:]
+            return queue
         used = set().union(*(_regs(x) for x in ops)) if ops else set()
         if op.startswith("ds_read"):
             dest = _regs(ops[0])
@@ -78,25 +161,23 @@ def check(lines: list) -> tuple:
                     bad.append((i, "address of a pending read", t))
                 if dest & pend:
                     bad.append((i, "overwrites a pending read", t))
-            queue.append(dest)
-            nreads += 1
-            continue
+            count["reads"].add(i)
+            return _cap(queue + (frozenset(dest),))
         for pend in queue:
             if used & pend:
                 bad.append((i, "uses a pending read", t))
                 break
-    return nreads, nwaits, bad
+        return queue
+
+    bad = _flow(lines, (), step, _merge_queues)
+    return len(count["reads"]), len(count["waits"]), bad
 
 
 def _walk(lines):
     """(line index, opcode, operand list, text) of every instruction."""
-    for i, line in enumerate(lines):
-        t = line.split(";")[0].strip()
-        if not t or t.startswith(".") or t.endswith(":"):
-            continue
-        op = t.split()[0]
-        rest = t[len(op):].strip()
-        yield i, op, ([x.strip() for x in rest.split(",")] if rest else []), t
+    for it in _parse(lines):
+        if it[0] == "inst":
+            yield it[1:]
 
 
 def _ws(op, ops):
@@ -106,32 +187,36 @@ def _ws(op, ops):
 def check_mfma_results(lines: list, need: int = 12) -> list:
     """Instructions that touch an MFMA's result fewer than `need` wait
     states after it (an MFMA accumulating into it excepted)."""
-    pend, bad = [], []  # (result registers, wait states since, line)
-    for i, op, ops, t in _walk(lines):
+
+    def step(pend, i, op, ops, t, bad):
         if op.startswith("v_mfma"):
             ab = _regs(ops[1]) | _regs(ops[2])
-            bad += [(i, w, t) for d, w, _ in pend if ab & d]
+            bad += [(i, w, t) for d, w in pend if ab & d]
         elif op != "s_nop":
             used = set().union(*(_regs(x) for x in ops)) if ops else set()
-            bad += [(i, w, t) for d, w, _ in pend if used & d]
+            bad += [(i, w, t) for d, w in pend if used & d]
         n = _ws(op, ops)
-        pend = [(d, w + n, l) for d, w, l in pend if w + n < need]
+        pend = tuple((d, w + n) for d, w in pend if w + n < need)
         if op.startswith("v_mfma"):
-            pend.append((_regs(ops[0]), 0, i))
-    return bad
+            pend = _merge_pending([pend, ((frozenset(_regs(ops[0])), 0),)])
+        return pend
+
+    return _flow(lines, (), step, _merge_pending)
 
 
 def check_mfma_operands(lines: list, need: int = 2) -> list:
     """MFMAs that read a register a vector instruction wrote fewer than
     `need` wait states before."""
-    pend, bad = [], []
-    for i, op, ops, t in _walk(lines):
+
+    def step(pend, i, op, ops, t, bad):
         if op.startswith("v_mfma"):
             src = set().union(*(_regs(x) for x in ops[1:4]))
-            bad += [(i, w, t) for d, w, _ in pend if src & d]
+            bad += [(i, w, t) for d, w in pend if src & d]
         n = _ws(op, ops)
-        pend = [(d, w + n, l) for d, w, l in pend if w + n < need]
+        pend = tuple((d, w + n) for d, w in pend if w + n < need)
         if (op.startswith("v_") and not op.startswith(("v_mfma", "v_cmp", "v_readlane", "v_readfirstlane"))
                 and ops):
-            pend.append((_regs(ops[0]), 0, i))
-    return bad
+            pend = _merge_pending([pend, ((frozenset(_regs(ops[0])), 0),)])
+        return pend
+
+    return _flow(lines, (), step, _merge_pending)

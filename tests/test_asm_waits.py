@@ -110,3 +110,28 @@ def test_the_spacing_walks_on_short_sequences():
     assert not asm_waits.check_mfma_results(prod + ["s_nop 7", "s_nop 3"] + read)
     assert not asm_waits.check_mfma_results(prod + ["v_mfma_f32_32x32x16_bf16 v[0:15], v[24:27], v[20:23], v[0:15]"])
     assert asm_waits.check_mfma_results(prod + ["v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], v[20:23], 0"])
+
+
+def test_the_walks_follow_branches():
+    # a read waited for on the fall-through path only, used where the paths
+    # join; waited for on both paths (clean)
+    rd = ["ds_read_b128 v[0:3], v10", "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)", ".LBB0_2:",
+          "v_mov_b32_e32 v20, v0"]
+    assert asm_waits.check(rd)[2]
+    assert not asm_waits.check(rd[:1] + ["s_waitcnt lgkmcnt(0)"] + rd[1:])[2]
+    # a read issued at the end of a loop body and used at its head before a
+    # wait: seen on the pass that takes the backward branch's state
+    loop = [".LBB0_1:", "v_add_f32_e32 v20, v0, v1", "ds_read_b128 v[0:3], v10", "s_cbranch_scc1 .LBB0_1",
+            "s_waitcnt lgkmcnt(0)"]
+    assert asm_waits.check(loop)[2]
+    assert not asm_waits.check(loop[:1] + ["s_waitcnt lgkmcnt(0)"] + loop[1:])[2]
+    # an MFMA result drained on the fall-through only; an unconditional
+    # branch over a block leaves that block's state out of the join
+    prod = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", "s_cbranch_scc1 .LBB0_2",
+            "s_nop 7", "s_nop 7", ".LBB0_2:", "v_mov_b32_e32 v30, v0"]
+    assert asm_waits.check_mfma_results(prod)
+    assert not asm_waits.check_mfma_results(prod[:1] + ["s_nop 7", "s_nop 7"] + prod[1:])
+    skip = ["s_branch .LBB0_3", "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", ".LBB0_3:",
+            "s_nop 7", "s_nop 3", "v_mov_b32_e32 v30, v0"]
+    assert not asm_waits.check_mfma_results(skip)
+    assert asm_waits.check_mfma_results(skip[:2] + skip[3:4] + ["v_mov_b32_e32 v30, v0"])

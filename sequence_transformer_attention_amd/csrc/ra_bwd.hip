@@ -414,9 +414,10 @@ __device__ __forceinline__ void mfma_qk_first(f32x16& c, const bf16x8& a, const 
 __device__ __forceinline__ void mfma_qk_next(f32x16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
 }
-// 16 wait states between the last MFMA writing c and a vector read of c
-// (gfx950 needs 12 after an 8-pass MFMA).
-__device__ __forceinline__ void qk_drain(f32x16& c) { asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c)); }
+// 12 wait states between the last MFMA writing c and a vector read of c,
+// what gfx950 needs after an 8-pass MFMA (the callers place an independent
+// product and its reads before it as well).
+__device__ __forceinline__ void qk_drain(f32x16& c) { asm volatile("s_nop 7\n\ts_nop 3" : "+v"(c)); }
 
 // dK and dV of one kv head for 128 keys per workgroup, 32 per wave (lane =
 // key lr, both lane halves): K and V of the lane's key stay in AGPRs, the
@@ -632,9 +633,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       // P = 0, and D = 0), nor keys past the sequence (their P only reaches
       // their own dK, dV columns, which are not stored).
       const int lo = !k_live ? (1 << 30) : (a.causal ? rel - 32 * v - 4 * lg : -(1 << 30));
-      qk_drain(sacc);
       // dP = dO V^T, one MFMA per slot; each slot also issues one pair of
-      // dO^T reads and forms 16 / KC elements of P
+      // dO^T reads and forms 16 / KC elements of P.  The first slot's
+      // product does not read S: it goes out before S's drain and runs
+      // through it.
       constexpr int PE = 16 / KC;
       f32x16 dpa;
       float pv[16];
@@ -649,6 +651,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         else mfma_qk_next(dpa, fd[c], vf[c]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(olo[hh][d_], ta.tr[0][d_] + DO_REGION);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(ohi[hh][d_], ta.tr[1][d_] + DO_REGION);
+        if constexpr (c == 0) qk_drain(sacc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < PE; ++q) {
@@ -675,9 +678,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
           pf[r >> 3][r & 7] = (__bf16)pv[r];
         }
       }
-      qk_drain(dpa);
       // dV^T += dO^T P, one MFMA per slot; each slot also issues one pair of
-      // Q^T reads and forms 16 / (2 DB) elements of dS = P (dP - D)
+      // Q^T reads and forms 16 / (2 DB) elements of dS = P (dP - D).  The
+      // first slot's product does not read dP: it runs through dP's drain.
       constexpr int SE = 16 / (2 * DB);
       bf16x8 dsf[2];
       static_for<0, 2 * DB>([&](auto X) {
@@ -694,6 +697,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         mfma_acc1(dva[d_], wd, pf[hh]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(qlo[hh][d_], ta.tr[0][d_]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(qhi[hh][d_], ta.tr[1][d_]);
+        if constexpr (x == 0) qk_drain(dpa);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < SE; ++q) {

@@ -89,7 +89,7 @@ def test_a_missing_drain_is_caught(tmp_path):
     # the backward's drain between the S and dP chains and the vector code
     # that reads their results, emptied in a copy of the source
     asm = mutant_asm(tmp_path, "ra_bwd.hip",
-                     'void qk_drain(f32x16& c) { asm volatile("s_nop 7\\n\\ts_nop 7" : "+v"(c)); }',
+                     'void qk_drain(f32x16& c) { asm volatile("s_nop 7\\n\\ts_nop 3" : "+v"(c)); }',
                      'void qk_drain(f32x16& c) { asm volatile("" : "+v"(c)); }')
     assert any(asm_waits.check_mfma_results(asm_waits.kernel_lines(asm, sym)) for sym in KERNELS["ra_bwd.hip"])
 

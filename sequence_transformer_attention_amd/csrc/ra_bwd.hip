@@ -689,10 +689,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         // later dO^T pairs and x Q^T pairs
         constexpr int n = 4 * DB - 2 < 14 ? 4 * DB - 2 : 14;
         if constexpr (x == 0)
-          asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(olo[hh][d_]), "+v"(ohi[hh][d_]), "+v"(d4[0]), "+v"(d4[1]),
-                       "+v"(d4[2]), "+v"(d4[3]) : "n"(n));
+          asm volatile("s_waitcnt lgkmcnt(%4)"
+                       : "+v"(d4[0]), "+v"(d4[1]), "+v"(d4[2]), "+v"(d4[3])
+                       : "n"(n), "v"(olo[hh][d_]), "v"(ohi[hh][d_]));
         else
-          asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(olo[hh][d_]), "+v"(ohi[hh][d_]) : "n"(n));
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(olo[hh][d_]), "v"(ohi[hh][d_]));
         const u32x4 wd = {olo[hh][d_][0], olo[hh][d_][1], ohi[hh][d_][0], ohi[hh][d_][1]};
         mfma_acc1(dva[d_], wd, pf[hh]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(qlo[hh][d_], ta.tr[0][d_]);
@@ -715,12 +716,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         // pairs (first half) or the next unit's reads (second half)
         constexpr int n = hh == 0 ? 2 * DB : (v + 1 < NU ? KC + 4 : 0);
         if constexpr (DB == 4)
-          asm volatile("s_waitcnt lgkmcnt(%8)" : "+v"(qlo[hh][0]), "+v"(qhi[hh][0]), "+v"(qlo[hh][1]),
-                       "+v"(qhi[hh][1]), "+v"(qlo[hh][2]), "+v"(qhi[hh][2]), "+v"(qlo[hh][3]), "+v"(qhi[hh][3])
-                       : "n"(n));
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(qlo[hh][0]), "v"(qhi[hh][0]), "v"(qlo[hh][1]),
+                       "v"(qhi[hh][1]), "v"(qlo[hh][2]), "v"(qhi[hh][2]), "v"(qlo[hh][3]), "v"(qhi[hh][3]));
         else
-          asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(qlo[hh][0]), "+v"(qhi[hh][0]), "+v"(qlo[hh][1]),
-                       "+v"(qhi[hh][1]) : "n"(n));
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(qlo[hh][0]), "v"(qhi[hh][0]), "v"(qlo[hh][1]),
+                       "v"(qhi[hh][1]));
         u32x4 wq[DB];
 #pragma unroll
         for (int d_ = 0; d_ < DB; ++d_) wq[d_] = u32x4{qlo[hh][d_][0], qlo[hh][d_][1], qhi[hh][d_][0], qhi[hh][d_][1]};

@@ -578,6 +578,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     // above by the tile walk; saturated below)
     const int64_t rel64 = my_k - qp0;
     const int rel = rel64 < -(1 << 30) ? -(1 << 30) : (int)rel64;
+    // units from vfull on need no causal test (every key of the wave is
+    // live and precedes their queries)
+    const int vfull = ra_plan_first_full_unit(wave_klast, a.kv_end, qp0, NU, a.causal);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (tid < QT) {
       lsd[st][0][tid] = lok ? lsv * kLog2e : INFINITY;  // rows past the chunk: P = 0
@@ -670,7 +673,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       // at the sequence's end).  Done for every unit, the test and select
       // took about a tenth of the kernel's time; here the other units pass
       // by on one branch on a wave-uniform value.
-      if (!(wave_klast < a.kv_end && (!a.causal || wave_klast <= qp0 + 32 * v))) {
+      if (v < vfull) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int e = 8 * (r >> 2) + (r & 3);

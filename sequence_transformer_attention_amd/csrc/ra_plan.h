@@ -121,6 +121,20 @@ RA_HD int ra_plan_half_valid(int nvalid, int hf, int half) {
   return x < 0 ? 0 : (x > half ? half : x);
 }
 
+// First of nu units of 32 queries (unit v from global position q0 + 32 v)
+// that the 32 keys klast - 31 .. klast (one wave of the dK/dV kernel) see
+// in full, or nu when none does: every key lies before the key end kv_end
+// and, under causal masking, at or before the unit's first query.  The
+// units before it take the per-element test.
+RA_HD int ra_plan_first_full_unit(int64_t klast, int64_t kv_end, int64_t q0, int nu, int causal) {
+  if (klast >= kv_end) return nu;
+  if (!causal) return 0;
+  const int64_t d = klast - q0;  // unit v is seen in full iff d <= 32 v
+  if (d <= 0) return 0;
+  const int64_t v = (d + 31) / 32;
+  return v < nu ? (int)v : nu;
+}
+
 // First query tile (bn rows, from local row 0 at global position qpos, nqc
 // rows) that sees the key at global position kfirst, or the tile count when
 // none does: under causal masking the rows before kfirst see no key at or

@@ -13,7 +13,11 @@
 //   3. per masked unit and query row, the visible keys: a prefix of
 //      ra_plan_visible_prefix keys.
 // The dK/dV kernel starts its walk over query tiles of 128 rows at
-// ra_plan_first_query_tile (checked for tiles of 64 rows too).  Every decision must agree bit for bit with
+// ra_plan_first_query_tile (checked for tiles of 64 rows too), and skips the
+// per-element test of the 32-query units of a tile from
+// ra_plan_first_full_unit on, which must be exactly the units whose every
+// pair with the wave's 32 keys is visible, all keys before the key end.
+// Every decision must agree bit for bit with
 // orc_classify / orc_visible_pairs: a tile is walked iff it holds a visible
 // pair; a tile or unit skips the mask only when every pair is visible; the
 // visible prefix counts exactly the visible keys; the query tiles before the
@@ -128,6 +132,21 @@ bool check_first_query_tile(int64_t kfirst, int64_t nk, int64_t qpos, int nqc, i
   return true;
 }
 
+// The dK/dV kernel's per-tile split: the wave's keys klast - 31 .. klast
+// (those before kv_end live), a tile of nu units of 32 queries from q0.
+bool check_first_full_unit(int64_t klast, int64_t kv_end, int64_t q0, int nu, int causal) {
+  const int first = ra_plan_first_full_unit(klast, kv_end, q0, nu, causal);
+  for (int v = 0; v < nu; ++v) {
+    const int64_t q0u = q0 + 32 * v;
+    const bool want = klast < kv_end && orc_visible_pairs(q0u, 32, klast - 31, 32, causal) == 32 * 32;
+    ++g_checked;
+    if ((v >= first) != want)
+      return fail("unit skips the test iff every key is live and sees every query", q0u, 32, klast - 31, 32, causal,
+                  v >= first, want);
+  }
+  return true;
+}
+
 }  // namespace
 
 int main() {
@@ -169,6 +188,16 @@ int main() {
               if (kfirst < 0) continue;
               if (!check_first_query_tile(kfirst, nk, qpos, nqc, causal, qt)) return 1;
             }
+  const int64_t q0us[] = {0, 31, 32, 100, 4096, (int64_t(3) << 30) + 7};
+  for (int causal = 0; causal < 2; ++causal)
+    for (int64_t q0u : q0us)
+      for (int64_t dk = -70; dk <= 170; ++dk)
+        for (int64_t de = -34; de <= 34; ++de) {
+          const int64_t klast = q0u + dk;
+          if (klast < 31) continue;
+          for (int nu : {1, 2, 4})
+            if (!check_first_full_unit(klast, klast + de, q0u, nu, causal)) return 1;
+        }
   std::printf("ok %lld\n", g_checked);
   return 0;
 }

@@ -671,8 +671,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       // some element needs it: a query of the unit before a key of the wave,
       // or a key of the wave past the key end (the units on the diagonal, or
       // at the sequence's end).  Done for every unit, the test and select
-      // took about a tenth of the kernel's time; here the other units pass
-      // by on one branch on a wave-uniform value.
+      // cost about 7 % of the kernel's cycles; here the other units pass by
+      // on one branch on a wave-uniform value.
       if (v < vfull) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -689,7 +689,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       static_for<0, 2 * DB>([&](auto X) {
         constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
         // dO^T pair x done (and D before it): the reads after it are the
-        // later dO^T pairs and x Q^T pairs
+        // later dO^T pairs and x Q^T pairs (the pair is an input, as the Q
+        // rows are above: only the asm product reads it)
         constexpr int n = 4 * DB - 2 < 14 ? 4 * DB - 2 : 14;
         if constexpr (x == 0)
           asm volatile("s_waitcnt lgkmcnt(%4)"

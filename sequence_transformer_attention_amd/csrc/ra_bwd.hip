@@ -557,13 +557,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // compiler's own waits stop at 14 as well).
   bf16x8 fq[KC];  // Q rows of the unit (A operand of S), read one unit ahead
   f32x4 l4[4];    // LSE log2(e) of the lane's 16 query rows (4 runs of 4), read with them
+  // The Q rows first: the S products wait for them one at a time, the LSE
+  // only the dP phase reads.
   auto read_q_l4 = [&](auto ST, auto V) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value, v = decltype(V)::value;
     constexpr unsigned o4 = ((unsigned)st * 2 * QT + 32u * v) * 4u;
-    static_for<0, 4>([&](auto J) { ds_rd128<o4 + 32u * decltype(J)::value>(l4[decltype(J)::value], lsd_lane); });
     static_for<0, KC>([&](auto C) {
       ds_rd128<(unsigned)st * TILE + (unsigned)v * 64 * D>(fq[decltype(C)::value], ta.rd[decltype(C)::value]);
     });
+    static_for<0, 4>([&](auto J) { ds_rd128<o4 + 32u * decltype(J)::value>(l4[decltype(J)::value], lsd_lane); });
   };
 
   // One tile: stage ST (compile time, so every LDS offset is an immediate).
@@ -596,22 +598,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
     static_for<0, NU>([&](auto V) {
       constexpr int v = decltype(V)::value;
       constexpr unsigned qo = (unsigned)st * TILE + (unsigned)v * 64 * D;  // unit v; dO at + DO_REGION
-      // Only the asm products read the Q and dO fragments, and volatile asm
-      // keeps its order, so the waits take them as inputs: as outputs the
-      // compiler counts the wait as a vector write and puts an s_nop before
-      // the next product.  l4 feeds compiled arithmetic and stays an output.
-      if constexpr (KC == 8)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3])
-                     : "v"(fq[0]), "v"(fq[1]), "v"(fq[2]), "v"(fq[3]), "v"(fq[4]), "v"(fq[5]), "v"(fq[6]), "v"(fq[7]));
-      else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3])
-                     : "v"(fq[0]), "v"(fq[1]), "v"(fq[2]), "v"(fq[3]));
       // S = Q K^T (query row of register r: 8 (r / 4) + 4 lg + (r % 4)),
-      // with the dO rows read one per product, then D of the rows
+      // with the dO rows read one per product, then D of the rows.  Each
+      // product waits for its own Q fragment: the reads after fq[c] are the
+      // later fragments, the unit's four LSE reads and the c dO rows read so
+      // far.  Only the asm products read the Q and dO fragments, and
+      // volatile asm keeps its order, so the waits take them as inputs: as
+      // outputs the compiler counts a wait as a vector write and puts an
+      // s_nop before the next product.
       f32x16 sacc;
       bf16x8 fd[KC];
       static_for<0, KC>([&](auto C) {
         constexpr int c = decltype(C)::value;
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(KC + 3), "v"(fq[c]));
         if constexpr (c == 0) {
           mfma_qk_first(sacc, fq[0], kf[0]);
           // the next tile's loads, once the tile's first product runs
@@ -648,8 +647,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
       static_for<0, KC>([&](auto C) {
         constexpr int c = decltype(C)::value, hh = c / DB, d_ = c % DB;
         // fd[c] done: the reads after it are fd[c + 1 ..], D and c pairs
+        // (the LSE, read before the dO rows, is done with fd[0]: it feeds
+        // compiled arithmetic and is an output there)
         constexpr int n = KC + 3 + c < 14 ? KC + 3 + c : 14;
-        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(fd[c]));
+        if constexpr (c == 0)
+          asm volatile("s_waitcnt lgkmcnt(%4)"
+                       : "+v"(l4[0]), "+v"(l4[1]), "+v"(l4[2]), "+v"(l4[3])
+                       : "n"(n), "v"(fd[c]));
+        else
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(fd[c]));
         if constexpr (c == 0) mfma_qk_first(dpa, fd[0], vf[0]);
         else mfma_qk_next(dpa, fd[c], vf[c]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(olo[hh][d_], ta.tr[0][d_] + DO_REGION);

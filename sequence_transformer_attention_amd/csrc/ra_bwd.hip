@@ -718,7 +718,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
       // dK^T += Q^T dS in two halves of 16 query rows; between them the next
-      // unit's LSE and Q rows are read (the S products of this unit, which
+      // unit's Q rows and LSE are read (the S products of this unit, which
       // read fq, are done)
       static_for<0, 2>([&](auto HH) {
         constexpr int hh = decltype(HH)::value;

@@ -557,15 +557,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
   // compiler's own waits stop at 14 as well).
   bf16x8 fq[KC];  // Q rows of the unit (A operand of S), read one unit ahead
   f32x4 l4[4];    // LSE log2(e) of the lane's 16 query rows (4 runs of 4), read with them
-  // The Q rows first: the S products wait for them one at a time, the LSE
-  // only the dP phase reads.
-  auto read_q_l4 = [&](auto ST, auto V) __attribute__((always_inline)) {
+  // Unit v's Q row fragment c and its LSE.  The Q rows go first: the S
+  // products wait for them one at a time, the LSE only the dP phase reads.
+  auto read_q = [&](auto ST, auto V, auto C) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value, v = decltype(V)::value, c = decltype(C)::value;
+    ds_rd128<(unsigned)st * TILE + (unsigned)v * 64 * D>(fq[c], ta.rd[c]);
+  };
+  auto read_l4 = [&](auto ST, auto V) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value, v = decltype(V)::value;
     constexpr unsigned o4 = ((unsigned)st * 2 * QT + 32u * v) * 4u;
-    static_for<0, KC>([&](auto C) {
-      ds_rd128<(unsigned)st * TILE + (unsigned)v * 64 * D>(fq[decltype(C)::value], ta.rd[decltype(C)::value]);
-    });
     static_for<0, 4>([&](auto J) { ds_rd128<o4 + 32u * decltype(J)::value>(l4[decltype(J)::value], lsd_lane); });
+  };
+  auto read_q_l4 = [&](auto ST, auto V) __attribute__((always_inline)) {
+    static_for<0, KC>([&](auto C) { read_q(ST, V, C); });
+    read_l4(ST, V);
   };
 
   // One tile: stage ST (compile time, so every LDS offset is an immediate).
@@ -688,15 +693,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         }
       }
       // dV^T += dO^T P, one MFMA per slot; each slot also issues one pair of
-      // Q^T reads and forms 16 / (2 DB) elements of dS = P (dP - D).  The
-      // first slot's product does not read dP: it runs through dP's drain.
+      // Q^T reads, then (within a tile) one Q row fragment of the next unit
+      // (2 DB = KC slots), and forms 16 / (2 DB) elements of dS = P (dP - D).
+      // The first slot's product does not read dP: it runs through dP's
+      // drain.  LDS reads complete in order, so the next unit's Q rows are
+      // done once the dK products' waits for the later Q^T pairs are.
       constexpr int SE = 16 / (2 * DB);
       bf16x8 dsf[2];
       static_for<0, 2 * DB>([&](auto X) {
         constexpr int x = decltype(X)::value, hh = x / DB, d_ = x % DB;
         // dO^T pair x done (and D before it): the reads after it are the
-        // later dO^T pairs and x Q^T pairs (the pair is an input, as the Q
-        // rows are above: only the asm product reads it)
+        // later dO^T pairs, x Q^T pairs and, within a tile, x Q row
+        // fragments; the wait counts the first two only, which is stricter
+        // (the pair is an input, as the Q rows are above: only the asm
+        // product reads it)
         constexpr int n = 4 * DB - 2 < 14 ? 4 * DB - 2 : 14;
         if constexpr (x == 0)
           asm volatile("s_waitcnt lgkmcnt(%4)"
@@ -708,6 +718,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         mfma_acc1(dva[d_], wd, pf[hh]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(qlo[hh][d_], ta.tr[0][d_]);
         ds_rdtr<qo + (unsigned)hh * 32 * D>(qhi[hh][d_], ta.tr[1][d_]);
+        if constexpr (v + 1 < NU) read_q(ST, std::integral_constant<int, v + 1>{}, X);
         if constexpr (x == 0) qk_drain(dpa);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -718,13 +729,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
       // dK^T += Q^T dS in two halves of 16 query rows; between them the next
-      // unit's Q rows and LSE are read (the S products of this unit, which
-      // read fq, are done)
+      // unit's LSE is read (its Q rows went out during the dV products)
       static_for<0, 2>([&](auto HH) {
         constexpr int hh = decltype(HH)::value;
-        // Q^T pairs of this half done: after them come the other half's
-        // pairs (first half) or the next unit's reads (second half)
-        constexpr int n = hh == 0 ? 2 * DB : (v + 1 < NU ? KC + 4 : 0);
+        // Q^T pairs of this half done: after them come (within a tile) the
+        // next unit's Q row fragment read with the half's last pair, then the
+        // other half's pairs and fragments (first half) or the next unit's
+        // LSE (second half)
+        constexpr int F = v + 1 < NU ? 1 : 0;
+        constexpr int n = hh == 0 ? F + DB * (2 + F) : 5 * F;
         if constexpr (DB == 4)
           asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(qlo[hh][0]), "v"(qhi[hh][0]), "v"(qlo[hh][1]),
                        "v"(qhi[hh][1]), "v"(qlo[hh][2]), "v"(qhi[hh][2]), "v"(qlo[hh][3]), "v"(qhi[hh][3]));
@@ -740,7 +753,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
 #pragma unroll
           for (int d_ = 0; d_ < DB; ++d_) mfma_acc1(dka[d_], wq[d_], dsf[hh]);
         }
-        if constexpr (hh == 0 && v + 1 < NU) read_q_l4(ST, std::integral_constant<int, v + 1>{});
+        if constexpr (hh == 0 && v + 1 < NU) read_l4(ST, std::integral_constant<int, v + 1>{});
       });
     });
   };

@@ -1,9 +1,10 @@
 """The inline-asm LDS reads of the bf16 forward and the backward kernels are
 waited for before their registers are used, and their inline-asm matrix
 products are spaced from the instructions around them (tests/asm_waits.py),
-checked in the gfx950 assembly the build flags produce; a weakened wait and
-a missing drain in copies of the sources are caught, and the spacing walks
-are checked on short sequences."""
+checked in the gfx950 assembly the build flags produce; a weakened wait, a
+wait that no longer holds back a builtin product and a missing drain in
+copies of the sources are caught, and the walks are checked on short
+sequences (branches and loops included)."""
 import os
 import shutil
 import subprocess
@@ -135,3 +136,14 @@ def test_the_walks_follow_branches():
             "s_nop 7", "s_nop 3", "v_mov_b32_e32 v30, v0"]
     assert not asm_waits.check_mfma_results(skip)
     assert asm_waits.check_mfma_results(skip[:2] + skip[3:4] + ["v_mov_b32_e32 v30, v0"])
+
+
+def test_a_wait_that_does_not_hold_back_a_builtin_product_is_caught(tmp_path):
+    # the dQ kernel's products are builtins: a wait that takes their V row
+    # fragment only as an input lets the compiler move the product above it,
+    # onto a register its LDS read has yet to write
+    asm = mutant_asm(tmp_path, "ra_bwd.hip",
+                     'asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fv[c]) : "n"(n));',
+                     'asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(n), "v"(fv[c]));')
+    _, _, bad = asm_waits.check(asm_waits.kernel_lines(asm, KERNELS["ra_bwd.hip"][0]))
+    assert any(why == "uses a pending read" and t.startswith("v_mfma") for _, why, t in bad)

@@ -428,9 +428,9 @@ __device__ __forceinline__ void qk_drain(f32x16& c) { asm volatile("s_nop 7\n\ts
 //   under the causal mask, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS
 // with dO^T and Q^T from transposing LDS reads.  The LDS reads are issued
 // a phase ahead of their products: a unit's dO rows during its S products,
-// its dO^T during dP, its Q^T during dV, the next unit's Q rows and row
-// statistics during this unit's dK products (within a tile), so only the
-// first unit of a tile waits for its Q rows.  The next tile's direct loads
+// its dO^T during dP, its Q^T and the next unit's Q rows during dV, the
+// next unit's row statistics during this unit's dK products (within a
+// tile), so only the first unit of a tile waits for its Q rows.  The next tile's direct loads
 // go out once the tile's first product runs (Q rows and statistics first).
 template <int D>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
@@ -575,8 +575,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(RaBwdArgs a) {
 
   // One tile: stage ST (compile time, so every LDS offset is an immediate).
   // Per 32-row unit, the products run S, dP, dV, dK, and each phase issues
-  // the reads of the next: the dO rows during S, dO^T during dP, Q^T during
-  // dV, the next unit's Q rows and LSE during dK.
+  // the reads of the next: the dO rows during S, dO^T during dP, Q^T and
+  // the next unit's Q rows during dV, the next unit's LSE during dK.
   auto tile = [&](int it, auto ST) __attribute__((always_inline)) {
     constexpr int st = decltype(ST)::value;
     const int64_t qp0 = tile_ref(cc).qp0;

@@ -325,6 +325,20 @@ def test_run_to_run_bitwise_determinism_and_nan_poison():
     assert not torch.isnan(O1.float()).any() and not torch.isnan(l1).any()   # outputs were NaN-filled
 
 
+def test_backward_run_to_run_bitwise_determinism():
+    """The backward has no atomics or order-dependent sums: two runs agree bit for bit."""
+    w = workloads.RANK7_BF16.shrunk(16)
+    d = _dev(inputs.workload_inputs(w))
+    g = torch.Generator().manual_seed(5)
+    dout = torch.randn(d["q"].shape, generator=g).to(torch.bfloat16).to(DEV)
+    say("backward determinism")
+    r1 = backward_gpu(d["q"], d["k"], d["v"], w.P, w.ranks[0], w.causal, dout)
+    r2 = backward_gpu(d["q"], d["k"], d["v"], w.P, w.ranks[0], w.causal, dout)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b) and not torch.isnan(a).any()
+
+
 def test_stepwise_resume_from_host_checkpoint():
     """Stop after k steps, copy the state to host memory and back, finish: bitwise equal."""
     w = workloads.GQA_BF16.shrunk(16)

@@ -97,22 +97,6 @@ struct TileAddr {
   }
 };
 
-// 128-bit A-operand reads of the 32-row unit at byte offset OFF, then a wait
-// that carries the registers (so no consumer is placed before it).
-template <int KC>
-__device__ __forceinline__ void read_rows(bf16x8 (&f)[KC], const unsigned (&rd)[KC], unsigned off) {
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    const unsigned ad = rd[c] + off;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(f[c]) : "v"(ad));
-  }
-  if constexpr (KC == 8)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
-                 "+v"(f[6]), "+v"(f[7]));
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
-}
-
 // LDS reads with an immediate byte offset.
 template <unsigned OFF, typename T>
 __device__ __forceinline__ void ds_rd128(T& r, unsigned addr) {
@@ -121,17 +105,6 @@ __device__ __forceinline__ void ds_rd128(T& r, unsigned addr) {
 template <unsigned OFF>
 __device__ __forceinline__ void ds_rdtr(u32x2& r, unsigned addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-}
-
-// Transposing A operand of channel block db, 16-row group at byte offset OFF.
-__device__ __forceinline__ bf16x8 read_tr(unsigned lo_addr, unsigned hi_addr, unsigned off) {
-  u32x2 lo, hi;
-  const unsigned a0 = lo_addr + off, a1 = hi_addr + off;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi));
-  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, w);
 }
 
 // acc[i] += A_i * B (v_mfma_f32_32x32x16_bf16, i = 0..3) with the

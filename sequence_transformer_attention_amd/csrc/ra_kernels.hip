@@ -468,8 +468,11 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
     // Softmax sub-step j of a step (row block j % 2, keys 2k, 2k+1 of the
     // lane's 16 with k = j / 2), software-pipelined over the slots: the
     // exponent arguments of sub-step j are formed in the slot before, so a
-    // slot runs the two exponentials (sm_a) under one MFMA and the sums, the
-    // bf16 P and the next sub-step's arguments (sm_b) under the other.
+    // slot runs the bf16 P of sub-step j - 1 and the two exponentials (sm_a)
+    // under one MFMA and the sums and the next sub-step's arguments (sm_b)
+    // under the other.  The conversion goes first: the compiler keeps a wait
+    // state between an MFMA and an exponential right behind it, which the
+    // conversion fills (the last sub-step's is converted after the slots).
     float sm_ps[RB][4], sm_tot[RB] = {0.f, 0.f}, sm_p[RB][2], sm_arg[2];
     auto sm_args = [&](auto X, auto J) __attribute__((always_inline)) {
       constexpr int x = decltype(X)::value, j = decltype(J)::value, rb = j % 2, k = j / 2;
@@ -478,8 +481,17 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
       sm_arg[1] = fmaf(s[2 * k + 1], a.c, -m2[rb]);
       asm volatile("" : "+v"(sm_arg[0]), "+v"(sm_arg[1]));
     };
+    // bf16 P of sub-step 2k + rb (its two exponentials, still in sm_p[rb])
+    auto sm_cvt = [&](auto X, auto R, auto K) __attribute__((always_inline)) {
+      constexpr int x = decltype(X)::value, rb = decltype(R)::value, k = decltype(K)::value;
+      pf[x][rb][k >> 2][2 * (k & 3)] = (__bf16)sm_p[rb][0];
+      pf[x][rb][k >> 2][2 * (k & 3) + 1] = (__bf16)sm_p[rb][1];
+      asm volatile("" : "+v"(pf[x][rb][k >> 2]));
+    };
     auto sm_a = [&](auto X, auto R, auto K) __attribute__((always_inline)) {
-      constexpr int rb = decltype(R)::value;
+      constexpr int rb = decltype(R)::value, j = 2 * decltype(K)::value + rb;
+      if constexpr (j > 0) sm_cvt(X, std::integral_constant<int, (j - 1) % 2>{}, std::integral_constant<int, (j - 1) / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
       sm_p[rb][0] = fast_exp2(sm_arg[0]);
       sm_p[rb][1] = fast_exp2(sm_arg[1]);
       asm volatile("" : "+v"(sm_p[rb][0]), "+v"(sm_p[rb][1]));
@@ -490,9 +502,7 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
       const float p0 = sm_p[rb][0], p1 = sm_p[rb][1];
       if constexpr (k < 4) sm_ps[rb][k] = p0 + p1;
       else sm_ps[rb][k - 4] += p0 + p1;
-      pf[x][rb][k >> 2][2 * (k & 3)] = (__bf16)p0;
-      pf[x][rb][k >> 2][2 * (k & 3) + 1] = (__bf16)p1;
-      asm volatile("" : "+v"(sm_ps[rb][k & 3]), "+v"(pf[x][rb][k >> 2]));
+      asm volatile("" : "+v"(sm_ps[rb][k & 3]));
       if constexpr (k == 7) {
         sm_tot[rb] = (sm_ps[rb][0] + sm_ps[rb][1]) + (sm_ps[rb][2] + sm_ps[rb][3]);
         asm volatile("" : "+v"(sm_tot[rb]));
@@ -619,6 +629,7 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_w64_kernel(RaAttnArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (sm) {
+        sm_cvt(X, std::integral_constant<int, 1>{}, std::integral_constant<int, 7>{});
         sm_fix(X);
       }
     };

@@ -253,6 +253,43 @@ def test_padded_backward_share(B, n_valid, P, Hq, Hkv, d, causal, ranks):
         assert float(dk[:, n_valid:].abs().max()) == 0.0 and float(dv[:, n_valid:].abs().max()) == 0.0
 
 
+# --------------------------------------------------------- seeded random shapes
+def _random_case(seed):
+    """Head dim, ring size, mask and rank cycle with the seed; sizes are drawn."""
+    rng = np.random.default_rng(1000 + seed)
+    d, P, causal = 128 if seed % 2 == 0 else 64, 2 + seed % 3, seed % 5 != 4
+    r = P - 1 - (seed // 3) % P
+    B, nb = int(rng.integers(1, 3)), int(rng.integers(20, 300))
+    Hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    return B, P, nb, G * Hkv, Hkv, d, causal, r
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_shapes_share_and_backward(seed):
+    """Seeded random shapes (block lengths off every tile size, GQA, d 64 or 128,
+    with and without the mask, any rank): the fused share and its backward
+    against the oracle on every row."""
+    B, P, nb, Hq, Hkv, d, causal, r = _random_case(seed)
+    N = P * nb
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=2000 + seed)
+    dv_ = _dev(x)
+    ql = x["q"][:, r * nb:(r + 1) * nb].contiguous()
+    say(f"random seed {seed}: B{B} N{N} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+    O, lse = rank_share_gpu(ql.to(DEV), dv_["k"], dv_["v"], P, r, causal, torch.float32)
+    torch.cuda.synchronize()
+    rows = oracle.all_rows(B, Hq, nb)
+    o_ref, l_ref = oracle.rank_share(ql, x["k"], x["v"], P, r, causal, rows=rows, nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, "bf16", f"random {seed} share")
+    dout = torch.randn(B, nb, Hq, d, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    dq, dk, dv = backward_gpu(ql.to(DEV), dv_["k"], dv_["v"], P, r, causal, dout.to(DEV))
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, P, r, causal, nthreads=oracle_threads())
+    grid = lambda a, H, S: a.reshape(B, H, S, d).transpose(0, 2, 1, 3)
+    assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nb), f"random {seed} dQ")
+    assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"random {seed} dK")
+    assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"random {seed} dV")
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,nq,nkv,Hq,Hkv,d,q_off,kv_off,causal", [

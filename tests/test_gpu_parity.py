@@ -290,6 +290,88 @@ def test_random_shapes_share_and_backward(seed):
     assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"random {seed} dV")
 
 
+def _random_variant_case(seed):
+    """Shapes for the load-balanced, padded and reordered stepwise shares."""
+    rng = np.random.default_rng(3000 + seed)
+    d, P, causal = 64 if seed % 2 == 0 else 128, 2 + seed % 3, seed % 4 != 3
+    B, Hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    c = int(rng.integers(9, 170))                   # zigzag chunk: N = 2 P c
+    n_valid = int(rng.integers(P + 1, 300 * P))      # padded: N = P ceil(n_valid / P)
+    r = int(rng.integers(0, P))
+    order = [int(j) for j in rng.permutation(P)]     # any fold order gives the same share
+    dt = "f32" if seed % 4 == 1 else "bf16"
+    return B, P, G * Hkv, Hkv, d, causal, r, c, n_valid, order, dt
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_zigzag_padded_and_reordered_steps(seed):
+    """Seeded random shapes for the other entry points, every row against the
+    oracle: the load-balanced share and its backward, the padded share (NaN
+    padding keys) and its backward, and the plain share as P ra_step calls in
+    a random block order (the merge is order-independent up to rounding)."""
+    B, P, Hq, Hkv, d, causal, r, c, n_valid, order, dt = _random_variant_case(seed)
+    grid = lambda a, H, S: a.reshape(B, H, S, d).transpose(0, 2, 1, 3)
+    g = torch.Generator().manual_seed(4000 + seed)
+
+    N = 2 * P * c
+    say(f"random zigzag seed {seed}: {dt} B{B} N{N} P{P} Hq{Hq} Hkv{Hkv} d{d} causal{int(causal)} rank {r}")
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=5000 + seed, dtype=dt)
+    xd = _dev(x)
+    ql = x["q"][:, zigzag_rows(N, P, r)].contiguous()
+    rows = oracle.all_rows(B, Hq, 2 * c)
+    O, lse = zigzag_gpu(ql.to(DEV), xd["k"], xd["v"], P, r, causal)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.rank_share_zigzag(ql, x["k"], x["v"], P, r, causal, rows=rows, nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"random {seed} zigzag")
+    if dt == "bf16":
+        dout = torch.randn(B, 2 * c, Hq, d, generator=g).to(torch.bfloat16)
+        dq, dk, dv = zigzag_backward_gpu(ql.to(DEV), xd["k"], xd["v"], P, r, causal, dout.to(DEV))
+        torch.cuda.synchronize()
+        dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, P, r, causal,
+                                                 nthreads=oracle_threads(), zigzag=True)
+        assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, 2 * c), f"random {seed} zigzag dQ")
+        assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"random {seed} zigzag dK")
+        assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"random {seed} zigzag dV")
+
+    nb = -(-n_valid // P)
+    N = P * nb
+    say(f"random padded seed {seed}: {dt} B{B} N{N} n_valid{n_valid} P{P} Hq{Hq} Hkv{Hkv} d{d} "
+        f"causal{int(causal)} rank {r}")
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=6000 + seed, dtype=dt)
+    x["k"][:, n_valid:] = float("nan")
+    x["v"][:, n_valid:] = float("nan")
+    xd = _dev(x)
+    ql = x["q"][:, r * nb:(r + 1) * nb].contiguous()
+    rows = oracle.all_rows(B, Hq, nb)
+    O, lse = padded_gpu(ql.to(DEV), xd["k"], xd["v"], P, r, causal, n_valid)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.rank_share_padded(ql, x["k"], x["v"], P, r, causal, n_valid, rows=rows,
+                                            nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"random {seed} padded")
+    if dt == "bf16":
+        dout = torch.randn(B, nb, Hq, d, generator=g).to(torch.bfloat16)
+        dq, dk, dv = padded_backward_gpu(ql.to(DEV), xd["k"], xd["v"], P, r, causal, n_valid, dout.to(DEV))
+        torch.cuda.synchronize()
+        dq_r, dk_r, dv_r = oracle.rank_share_bwd(ql, x["k"], x["v"], dout, P, r, causal,
+                                                 nthreads=oracle_threads(), n_valid=n_valid)
+        assert_grad_close(dq.double().cpu().numpy(), grid(dq_r, Hq, nb), f"random {seed} padded dQ")
+        assert_grad_close(dk.double().cpu().numpy(), grid(dk_r, Hkv, N), f"random {seed} padded dK")
+        assert_grad_close(dv.double().cpu().numpy(), grid(dv_r, Hkv, N), f"random {seed} padded dV")
+        if n_valid < N:
+            assert float(dk[:, n_valid:].abs().max()) == 0.0 and float(dv[:, n_valid:].abs().max()) == 0.0
+
+    # the contiguous share folded block by block in a random order (padding
+    # rows removed: every key real)
+    x = inputs.draw_qkv(B, N, N, Hq, Hkv, d, seed=7000 + seed, dtype=dt)
+    xd = _dev(x)
+    ql = x["q"][:, r * nb:(r + 1) * nb].contiguous()
+    say(f"random stepwise seed {seed}: {dt} B{B} N{N} P{P} order {order} rank {r}")
+    O, lse = stepwise_gpu(ql.to(DEV), xd["k"], xd["v"], P, r, causal, order=order)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.rank_share(ql, x["k"], x["v"], P, r, causal, rows=rows, nthreads=oracle_threads())
+    assert_close(*gather(O, lse, rows), o_ref, l_ref, dt, f"random {seed} stepwise")
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,nq,nkv,Hq,Hkv,d,q_off,kv_off,causal", [

@@ -293,6 +293,35 @@ def test_ra_merge_validation():
     assert merge(oa=e0, ob=e1, m=rows(1, 2, 0), l=rows(1, 2, 0), mb=rows(1, 2, 0), lb=rows(1, 2, 0)) == ra.RA_OK
 
 
+def test_empty_calls_return_ok_before_any_launch():
+    """A zero batch or a zero-length sequence is a no-op for every entry
+    point: each returns RA_OK after validation and before any HIP call (these
+    run with no GPU)."""
+    L = ra.lib()
+    F32 = ra.RA_F32
+    for B, N, Pn, rank in ((1, 0, 8, 7), (0, 4096, 8, 7), (0, 0, 1, 0)):
+        nq = N // Pn
+        q, k = T([B, nq, 4, 128]), T([B, N, 1, 128])
+        g, gk = T([B, nq, 4, 128], F32), T([B, N, 1, 128], F32)
+        st = rows(B, 4, nq)
+        opts = ra.RaOpts()
+        opts.o_out = ctypes.pointer(T([B, nq, 4, 128]))
+        o = ctypes.byref(opts)
+        case = f"B{B} N{N}"
+        assert L.ra_rank_share(P(q), P(k), P(k), Pn, rank, 1, o) == ra.RA_OK, case
+        assert L.ra_rank_share_zigzag(P(q), P(k), P(k), Pn, rank, 1, o) == ra.RA_OK, case
+        assert L.ra_rank_share_padded(P(q), P(k), P(k), Pn, rank, 1, N, o) == ra.RA_OK, case
+        bwd_args = (P(q), P(k), P(k), P(q), P(st), P(q), Pn, rank, 1)
+        assert L.ra_rank_share_bwd(*bwd_args, P(g), P(gk), P(gk), P(st), None) == ra.RA_OK, case
+        assert L.ra_rank_share_zigzag_bwd(*bwd_args, P(g), P(gk), P(gk), P(st), None) == ra.RA_OK, case
+        assert L.ra_rank_share_padded_bwd(*bwd_args[:-1], 1, N, P(g), P(gk), P(gk), P(st), None) == ra.RA_OK, case
+        assert L.ra_rank_share_bwd_noalloc(*bwd_args, P(g), P(gk), P(gk), None) == ra.RA_OK, case
+        assert L.ra_state_init(P(g), P(st), P(st), None) == ra.RA_OK, case
+        assert L.ra_merge(P(g), P(st), P(st), P(g), P(st), P(st), None) == ra.RA_OK, case
+        assert L.ra_finalize(P(g), P(st), None) == ra.RA_OK, case
+        assert step(q, k, k, g, st, st) == ra.RA_OK, case
+
+
 def test_launches_beyond_the_work_item_limit_are_rejected():
     """A grid is at most 2^32 - 1 work-items along x: the bf16 forward runs
     256 threads per 256 query rows, the backward 256 per 128 rows, the state

@@ -119,6 +119,7 @@ def test_ra_step_skip_and_empty_return_ok_without_launch():
     assert step(**good_step_args(), q_off=0, kv_off=1000, causal=1) == ra.RA_OK
     assert step(**good_step_args(nq=0)) == ra.RA_OK
     assert step(**good_step_args(B=0)) == ra.RA_OK
+    assert step(**good_step_args(nkv=0), causal=0) == ra.RA_OK   # an empty key block is SKIP
 
 
 def share(q, k, v, Pn, rank, causal=1, o_out=None, lse=None, scale=0.0):
